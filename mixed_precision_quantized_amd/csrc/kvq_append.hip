@@ -1,0 +1,522 @@
+// kvq_append.hip -- quantize-on-append kernels for gfx950.
+//
+//  * k_encode_q<FMT>: qN_0 / qN_1 / bf16 encoding of whole tokens (4 lanes per token and
+//    stream, one 32-dim block per lane).  Symmetric qN_0 takes its fp16 scale from the
+//    signed max-magnitude element and uses all 2^N levels; qN_1 stores an fp16 step
+//    (max-min)/(2^N-1) and an fp16 min.  Codes are a little-endian N-bit stream per token.
+//  * k_kvarn_page<N>: KVarN for one 128-token page of one stream per workgroup: unnormalized
+//    Walsh-Hadamard rotation of every token vector, 8 Sinkhorn iterations balancing
+//    per-token and per-channel mean squares, fp16 channel scales, then qN_0 of the
+//    normalized values ("Практическое руководство: запуск Bonsai-Ternary-27B на 120k
+//    токенах с менее чем 10 ГБ VRAM", sections "Решение: KVarN ..." and "Как
+//    преобразование Уолша-Адамара и Sinkhorn спасают качество при 4-битном сжатии").
+//  * k_ring_write: canonical bf16 rows of the newest tokens into the precision-tail ring.
+//
+// Every value is the canonical bf16 of the input (fp32 inputs rounded to nearest even),
+// so codes depend only on a token's (or its page's) values, never on when it is spilled.
+#pragma clang fp contract(off)
+
+#include <float.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+namespace {
+
+__device__ __forceinline__ char* stream_ptr(const CacheGeom& g, int seq, int layer, int head, int isv)
+{
+    int64_t unit = ((int64_t)seq * g.n_layers + layer) * g.n_kv_heads + head;
+    return g.base + unit * g.unit_bytes + (isv ? g.v_offset : 0);
+}
+
+// Address of the 128 input values of (layer - layer0, row, head) for K (isv=0) or V.
+__device__ __forceinline__ const char* input_row(const AppendArgs& a, int lrel, int64_t row, int head, int isv)
+{
+    const char* base = (const char*)(isv ? a.v_in : a.k_in);
+    int64_t elem = (((int64_t)lrel * a.rows + row) * a.g.n_kv_heads + head) * kD;
+    return base + elem * (a.in_dtype ? 4 : 2);
+}
+
+// Load NV consecutive canonical values (as floats) starting at element e0 of a row that is
+// either bf16 (ring rows, bf16 inputs) or fp32 (rounded to bf16 first).
+template <int NV>
+__device__ __forceinline__ void load_canon(const char* row, bool f32, int e0, float (&x)[NV])
+{
+    if (f32) {
+        const float4* p = (const float4*)(row + 4 * e0);
+#pragma unroll
+        for (int i = 0; i < NV / 4; ++i) {
+            float4 w = p[i];
+            x[4 * i + 0] = bf16_to_f32(bf16_rne(w.x));
+            x[4 * i + 1] = bf16_to_f32(bf16_rne(w.y));
+            x[4 * i + 2] = bf16_to_f32(bf16_rne(w.z));
+            x[4 * i + 3] = bf16_to_f32(bf16_rne(w.w));
+        }
+    } else {
+        const uint4* p = (const uint4*)(row + 2 * e0);
+#pragma unroll
+        for (int i = 0; i < NV / 8; ++i) {
+            uint4 w = p[i];
+            x[8 * i + 0] = bf16_to_f32(w.x & 0xFFFFu);
+            x[8 * i + 1] = bf16_to_f32(w.x >> 16);
+            x[8 * i + 2] = bf16_to_f32(w.y & 0xFFFFu);
+            x[8 * i + 3] = bf16_to_f32(w.y >> 16);
+            x[8 * i + 4] = bf16_to_f32(w.z & 0xFFFFu);
+            x[8 * i + 5] = bf16_to_f32(w.z >> 16);
+            x[8 * i + 6] = bf16_to_f32(w.w & 0xFFFFu);
+            x[8 * i + 7] = bf16_to_f32(w.w >> 16);
+        }
+    }
+}
+
+// clamp(rint(t) + off, 0, top) in binary32, rint = round half to even.
+__device__ __forceinline__ uint32_t code_of(float t, float off, float top)
+{
+    float v = __builtin_rintf(t) + off;
+    v = v < 0.0f ? 0.0f : v;
+    v = v > top ? top : v;
+    return (uint32_t)v;
+}
+
+// Pack 32 N-bit codes into N little-endian 32-bit words.
+template <int N>
+__device__ __forceinline__ void pack32(const uint32_t (&u)[32], uint32_t (&w)[N])
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k] = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int bit = i * N;
+        const int wi = bit >> 5, sh = bit & 31;
+        w[wi] |= u[i] << sh;
+        if (sh + N > 32) w[wi + 1] |= u[i] >> (32 - sh);
+    }
+}
+
+// Symmetric block encoder: returns the fp16 scale bits, fills 32 codes.
+template <int N>
+__device__ __forceinline__ uint32_t encode_block_q0(const float (&x)[32], uint32_t (&u)[32])
+{
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        mx = x[i] > mx ? x[i] : mx;
+        mn = x[i] < mn ? x[i] : mn;
+    }
+    const float m = (mx >= -mn) ? mx : mn;
+    const float qd = m / -(float)(1 << (N - 1));
+    const uint32_t d = fp16s_rne(qd);
+    if (d == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) u[i] = 1u << (N - 1);
+        return 0;
+    }
+    const float inv = 1.0f / fp16_to_f32(d);
+    const float off = (float)(1 << (N - 1)), top = (float)((1 << N) - 1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) u[i] = code_of(x[i] * inv, off, top);
+    return d;
+}
+
+// Affine block encoder: returns d | m << 16, fills 32 codes.
+template <int N>
+__device__ __forceinline__ uint32_t encode_block_q1(const float (&x)[32], uint32_t (&u)[32])
+{
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        mx = x[i] > mx ? x[i] : mx;
+        mn = x[i] < mn ? x[i] : mn;
+    }
+    const float top = (float)((1 << N) - 1);
+    const float dr = mx - mn;
+    const float dq = dr / top;
+    const uint32_t d = fp16s_rne(dq);
+    const uint32_t m = fp16s_rne(mn);
+    if (d == 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) u[i] = 0;
+        return m << 16;
+    }
+    const float mf = fp16_to_f32(m);
+    const float inv = 1.0f / fp16_to_f32(d);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        float diff = x[i] - mf;
+        u[i] = code_of(diff * inv, 0.0f, top);
+    }
+    return d | (m << 16);
+}
+
+template <int N>
+__device__ __forceinline__ void store_words(char* dst, const uint32_t (&w)[N])
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < N; k += 4) *(uint4*)(dst + 4 * k) = make_uint4(w[k], w[k + 1], w[k + 2], w[k + 3]);
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < N; k += 2) *(uint2*)(dst + 4 * k) = make_uint2(w[k], w[k + 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) *(uint32_t*)(dst + 4 * k) = w[k];
+    }
+}
+
+// Locate the sequence entry of a token index t in [0, total) where entry i owns
+// count_i consecutive indices; returns the entry and the offset inside it.
+template <typename CountFn>
+__device__ __forceinline__ int find_entry(const AppendArgs& a, int64_t t, int64_t* off, CountFn cnt)
+{
+    int64_t acc = 0;
+    for (int i = 0; i < a.n_seqs; ++i) {
+        int64_t c = cnt(a.seqs[i]);
+        if (t < acc + c) { *off = t - acc; return i; }
+        acc += c;
+    }
+    *off = 0;
+    return -1;
+}
+
+struct EncCount { __device__ int64_t operator()(const AppendSeq& s) const { return s.nq_new - s.nq_old; } };
+struct RingCount {
+    __device__ int64_t operator()(const AppendSeq& s) const
+    {
+        int64_t lo = s.nq_new > s.n_old ? s.nq_new : s.n_old;
+        return s.n_new > lo ? s.n_new - lo : 0;
+    }
+};
+struct PageCount { __device__ int64_t operator()(const AppendSeq& s) const { return (s.nq_new - s.nq_old) / kPage; } };
+
+// ------------------------------------------------------------------ qN / bf16 encoder
+// Lane work item: (layer, head, stream, token, block), token-fastest within a stream.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_encode_q(AppendArgs a, int64_t tokens)
+{
+    constexpr int N = fbits(FMT);
+    constexpr int KIND = fkind(FMT);
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = (int)(gid & 3);
+    int64_t w = gid >> 2;
+    const int64_t tg = w % tokens;
+    w /= tokens;
+    const int sv = (int)(w & 1);
+    w >>= 1;
+    const int head = (int)(w % a.g.n_kv_heads);
+    const int lrel = (int)(w / a.g.n_kv_heads);
+    if (lrel >= a.layers_in) return;
+    int64_t off;
+    const int e = find_entry(a, tg, &off, EncCount());
+    if (e < 0) return;
+    const AppendSeq& s = a.seqs[e];
+    const int64_t p = s.nq_old + off;
+    const int layer = a.layer0 + lrel;
+    char* st = stream_ptr(a.g, s.seq, layer, head, sv);
+    const StreamLayout& L = sv ? a.g.v : a.g.k;
+    const bool from_ring = p < s.n_old;
+    const char* src = from_ring ? st + L.ring + (p % a.g.ring_slots) * 256
+                                : input_row(a, lrel, s.in_row0 + (p - s.n_old), head, sv);
+    const bool f32 = !from_ring && a.in_dtype == 1;
+    char* codes = st + L.codes + p * fcode_bytes(FMT);
+
+    if constexpr (KIND == KIND_BF16) {
+        // identity: the canonical bf16 row
+        uint32_t o[16];
+        if (f32) {
+            const float4* q = (const float4*)(src + 4 * 32 * b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float4 v = q[i];
+                o[2 * i] = bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16);
+                o[2 * i + 1] = bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16);
+            }
+        } else {
+            const uint4* q = (const uint4*)(src + 2 * 32 * b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint4 v = q[i];
+                o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(uint4*)(codes + 64 * b + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    } else {
+        float x[32];
+        load_canon<32>(src, f32, 32 * b, x);
+        uint32_t u[32];
+        uint32_t packed[N];
+        char* scales = st + L.scales + p * (fscale_halves(FMT) * 2);
+        if constexpr (KIND == KIND_Q0) {
+            uint32_t d = encode_block_q0<N>(x, u);
+            *(uint16_t*)(scales + 2 * b) = (uint16_t)d;
+        } else {
+            uint32_t dm = encode_block_q1<N>(x, u);
+            *(uint32_t*)(scales + 4 * b) = dm;
+        }
+        pack32<N>(u, packed);
+        store_words<N>(codes + 4 * N * b, packed);
+    }
+}
+
+// ------------------------------------------------------------------ ring writer
+// 8 lanes per (token, stream), 16 values per lane.
+__global__ __launch_bounds__(256) void k_ring_write(AppendArgs a, int64_t tokens)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int part = (int)(gid & 7);
+    int64_t w = gid >> 3;
+    const int64_t tg = w % tokens;
+    w /= tokens;
+    const int sv = (int)(w & 1);
+    w >>= 1;
+    const int head = (int)(w % a.g.n_kv_heads);
+    const int lrel = (int)(w / a.g.n_kv_heads);
+    if (lrel >= a.layers_in) return;
+    int64_t off;
+    const int e = find_entry(a, tg, &off, RingCount());
+    if (e < 0) return;
+    const AppendSeq& s = a.seqs[e];
+    const int64_t lo = s.nq_new > s.n_old ? s.nq_new : s.n_old;
+    const int64_t p = lo + off;
+    const int layer = a.layer0 + lrel;
+    char* st = stream_ptr(a.g, s.seq, layer, head, sv);
+    const StreamLayout& L = sv ? a.g.v : a.g.k;
+    const char* src = input_row(a, lrel, s.in_row0 + (p - s.n_old), head, sv);
+    char* dst = st + L.ring + (p % a.g.ring_slots) * 256 + 32 * part;
+    if (a.in_dtype == 1) {
+        const float4* q = (const float4*)(src + 64 * part);
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 v = q[i];
+            o[2 * i] = bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16);
+            o[2 * i + 1] = bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16);
+        }
+        *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
+        *(uint4*)(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+        const uint4* q = (const uint4*)(src + 32 * part);
+        *(uint4*)dst = q[0];
+        *(uint4*)(dst + 16) = q[1];
+    }
+}
+
+// ------------------------------------------------------------------ KVarN page encoder
+constexpr int kLdsStride = 129;   // padded row of the 128x128 fp32 page (conflict-free rows and columns)
+
+// tree64 over a register array: for w = 32, 16, ..., 1: v[i] += v[i+w] for i < w.
+__device__ __forceinline__ float tree64(float (&v)[64])
+{
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
+    }
+    return v[0];
+}
+
+__device__ __forceinline__ float swap_pair(float x)
+{
+    // exchange with the neighbouring lane (lanes 2k <-> 2k+1): DPP quad_perm [1,0,3,2]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages, int streams_mask)
+{
+    __shared__ float As[kPage * kLdsStride];   // squares A[t][j]
+    __shared__ float part[2][kPage];           // tree halves (even / odd indices)
+    __shared__ float inv_s[kPage];             // reciprocals 1/c2 or 1/r2 of the current step
+    __shared__ float scale_s[kPage];           // r2 or c2 of the current step
+    __shared__ float ic16_s[kPage];            // 1 / fp16 channel scale
+
+    const int tid = threadIdx.x;
+    int64_t w = blockIdx.x;
+    const int64_t pg = w % pages;
+    w /= pages;
+    const int sv = (int)(w & 1);
+    w >>= 1;
+    const int head = (int)(w % a.g.n_kv_heads);
+    const int lrel = (int)(w / a.g.n_kv_heads);
+    if (!((streams_mask >> sv) & 1)) return;
+    int64_t off;
+    const int e = find_entry(a, pg, &off, PageCount());
+    if (e < 0) return;
+    const AppendSeq& s = a.seqs[e];
+    const int64_t page = s.nq_old / kPage + off;
+    const int layer = a.layer0 + lrel;
+    char* st = stream_ptr(a.g, s.seq, layer, head, sv);
+    const StreamLayout& L = sv ? a.g.v : a.g.k;
+
+    // ---- 1. load half a token row (64 values) and rotate it --------------------------
+    const int t = tid >> 1;            // token of the page
+    const int half = tid & 1;          // dims [64*half, 64*half+64)
+    const int64_t p = page * kPage + t;
+    const bool from_ring = p < s.n_old;
+    const char* src = from_ring ? st + L.ring + (p % a.g.ring_slots) * 256
+                                : input_row(a, lrel, s.in_row0 + (p - s.n_old), head, sv);
+    float y[64];
+    load_canon<64>(src, !from_ring && a.in_dtype == 1, 64 * half, y);
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            if (i & h) continue;
+            float u = y[i], v = y[i + h];
+            y[i] = u + v;
+            y[i + h] = u - v;
+        }
+    }
+    // stage h = 64 pairs dim i with i+64: the other half lives in the neighbouring lane
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        float o = swap_pair(y[i]);
+        y[i] = half ? (o - y[i]) : (y[i] + o);
+    }
+    // ---- 2. squares into LDS -----------------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < 64; ++i) As[t * kLdsStride + 64 * half + i] = y[i] * y[i];
+    if (tid < kPage) inv_s[tid] = 1.0f;    // 1 / c2 with c2 = 1
+    __syncthreads();
+
+    // ---- 3. Sinkhorn: 8 x (row step, column step) ---------------------------------------
+    const int idx = tid & 127;             // token (row step) or channel (column step)
+    const int par = tid >> 7;              // parity class of the summed index
+    const float inv128 = 1.0f / 128.0f;
+    for (int it = 0; it < 8; ++it) {
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            float v[64];
+            if (step == 0) {
+#pragma unroll
+                for (int k = 0; k < 64; ++k) v[k] = As[idx * kLdsStride + par + 2 * k] * inv_s[par + 2 * k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 64; ++k) v[k] = As[(par + 2 * k) * kLdsStride + idx] * inv_s[par + 2 * k];
+            }
+            part[par][idx] = tree64(v);
+            __syncthreads();
+            if (tid < kPage) {
+                float r = (part[0][tid] + part[1][tid]) * inv128;
+                if (!(r >= FLT_MIN)) r = 1.0f;
+                scale_s[tid] = r;
+                inv_s[tid] = 1.0f / r;
+            }
+            __syncthreads();
+        }
+    }
+    // ---- 4. channel scales ----------------------------------------------------------
+    if (tid < kPage) {
+        uint32_t c = fp16s_rne(__builtin_sqrtf(scale_s[tid]));
+        if (c == 0) c = 0x3C00u;
+        ic16_s[tid] = 1.0f / fp16_to_f32(c);
+        ((uint16_t*)(st + L.cscale + page * 256))[tid] = (uint16_t)c;
+    }
+    __syncthreads();
+    // ---- 5./6. normalize, symmetric block quantization, pack -----------------------------
+    char* codes = st + L.codes + p * (16 * N);
+    uint16_t* scl = (uint16_t*)(st + L.scales + p * 8);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = y[32 * bb + i] * ic16_s[64 * half + 32 * bb + i];
+        uint32_t u[32];
+        uint32_t d = encode_block_q0<N>(x, u);
+        uint32_t packed[N];
+        pack32<N>(u, packed);
+        const int blk = 2 * half + bb;
+        store_words<N>(codes + 4 * N * blk, packed);
+        scl[blk] = (uint16_t)d;
+    }
+}
+
+inline int64_t total_of(const AppendArgs& a, int which)
+{
+    int64_t tot = 0;
+    for (int i = 0; i < a.n_seqs; ++i) {
+        const AppendSeq& s = a.seqs[i];
+        if (which == 0) tot += s.nq_new - s.nq_old;
+        else if (which == 1) {
+            int64_t lo = s.nq_new > s.n_old ? s.nq_new : s.n_old;
+            tot += s.n_new > lo ? s.n_new - lo : 0;
+        } else {
+            tot += (s.nq_new - s.nq_old) / kPage;
+        }
+    }
+    return tot;
+}
+
+template <int FMT>
+int launch_enc(const AppendArgs& a, int64_t tokens, hipStream_t st)
+{
+    int64_t lanes = 4 * tokens * 2 * a.g.n_kv_heads * (int64_t)a.layers_in;
+    int64_t blocks = (lanes + 255) / 256;
+    hipLaunchKernelGGL(k_encode_q<FMT>, dim3((unsigned)blocks), dim3(256), 0, st, a, tokens);
+    return (int)hipGetLastError();
+}
+
+template <int N>
+int launch_kv(const AppendArgs& a, int64_t pages, int mask, hipStream_t st)
+{
+    int64_t blocks = pages * 2 * a.g.n_kv_heads * (int64_t)a.layers_in;
+    hipLaunchKernelGGL(k_kvarn_page<N>, dim3((unsigned)blocks), dim3(256), 0, st, a, pages, mask);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_append_encode(const AppendArgs& a, void* stream)
+{
+    int64_t tokens = total_of(a, 0);
+    if (tokens <= 0) return 0;
+    hipStream_t st = (hipStream_t)stream;
+    // K and V share one format (checked at init); a KVarN format never reaches here.
+    switch (a.g.fmt_k) {
+    case 0: return launch_enc<0>(a, tokens, st);
+    case 1: return launch_enc<1>(a, tokens, st);
+    case 2: return launch_enc<2>(a, tokens, st);
+    case 3: return launch_enc<3>(a, tokens, st);
+    case 4: return launch_enc<4>(a, tokens, st);
+    case 5: return launch_enc<5>(a, tokens, st);
+    case 6: return launch_enc<6>(a, tokens, st);
+    case 7: return launch_enc<7>(a, tokens, st);
+    case 8: return launch_enc<8>(a, tokens, st);
+    case 9: return launch_enc<9>(a, tokens, st);
+    case 10: return launch_enc<10>(a, tokens, st);
+    case 11: return launch_enc<11>(a, tokens, st);
+    case 12: return launch_enc<12>(a, tokens, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+int launch_append_kvarn(const AppendArgs& a, void* stream)
+{
+    int64_t pages = total_of(a, 2);
+    if (pages <= 0) return 0;
+    hipStream_t st = (hipStream_t)stream;
+    int mask = (fkind(a.g.fmt_k) == KIND_KVARN ? 1 : 0) | (fkind(a.g.fmt_v) == KIND_KVARN ? 2 : 0);
+    switch (fbits(a.g.fmt_k)) {
+    case 2: return launch_kv<2>(a, pages, mask, st);
+    case 3: return launch_kv<3>(a, pages, mask, st);
+    case 4: return launch_kv<4>(a, pages, mask, st);
+    case 5: return launch_kv<5>(a, pages, mask, st);
+    case 6: return launch_kv<6>(a, pages, mask, st);
+    case 8: return launch_kv<8>(a, pages, mask, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+int launch_append_ring(const AppendArgs& a, void* stream)
+{
+    int64_t tokens = total_of(a, 1);
+    if (tokens <= 0) return 0;
+    int64_t lanes = 8 * tokens * 2 * a.g.n_kv_heads * (int64_t)a.layers_in;
+    int64_t blocks = (lanes + 255) / 256;
+    hipLaunchKernelGGL(k_ring_write, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a, tokens);
+    return (int)hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,449 @@
+// kvq_decode.hip -- single-token GQA decode attention over the mixed-precision cache, gfx950.
+//
+// Long-context decode is a streaming read of the whole cache (memory bound: "Форк beellama
+// и KV-кванты kvarn на длинном контексте: что известно об ускорении в 2026 году", section
+// "Длинный контекст меняет профиль нагрузки с вычислений на работу с памятью"), so the
+// kernel reads every packed row once, coalesced, and dequantizes in registers.  It is not
+// a dense contraction at 4 query heads per KV head: no matrix cores.
+//
+// Work split (split-K flash decode): the tokens of each (sequence, KV head) are cut into
+// units (128-token quantized pages, 32-token ring chunks); every workgroup owns a run of
+// units of one kind, sized so the whole grid is resident at once.  Each wave keeps an
+// online softmax (running max m, sum l, accumulator acc) per token slot; slots and waves
+// merge through shuffles and LDS; the last workgroup of a (sequence, KV head) to finish
+// (device-scope counter) merges all partials and writes the output.
+//
+// KVarN: keys and values are stored rotated, x = H Yhat / 128 with H the unnormalized
+// Sylvester Hadamard matrix (symmetric).  So q.x = (H q / 128) . Yhat: the query is rotated
+// once, quantized values are accumulated in the rotated domain, and the merged quantized
+// accumulator is rotated back once at the end; ring tokens stay in the original domain.
+#include <float.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kG = 4;                 // query heads per KV head handled by this kernel
+constexpr float kNegBig = -1.0e30f;   // "no token yet" running max (finite: no inf - inf)
+
+__device__ __forceinline__ const char* stream_cptr(const CacheGeom& g, int seq, int layer, int head, int isv)
+{
+    int64_t unit = ((int64_t)seq * g.n_layers + layer) * g.n_kv_heads + head;
+    return g.base + unit * g.unit_bytes + (isv ? g.v_offset : 0);
+}
+
+__device__ __forceinline__ float dpp_xor1(float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)); }
+__device__ __forceinline__ float dpp_xor2(float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)); }
+// row_half_mirror: lane i <-> 7-i inside each group of 8 lanes
+__device__ __forceinline__ float dpp_hmirror(float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)); }
+
+// Sum over the 8 lanes of a token slot (lanes 8k .. 8k+7), result in every lane.
+__device__ __forceinline__ float sum8(float x)
+{
+    x += dpp_xor1(x);
+    x += dpp_xor2(x);
+    x += dpp_hmirror(x);
+    return x;
+}
+
+// Load the 2N bytes of 16 consecutive N-bit codes (dims 16*part ...) of one row into words.
+template <int N>
+__device__ __forceinline__ void load_codes16(const char* row, int part, uint32_t (&w)[(N + 1) / 2])
+{
+    const char* p = row + 2 * N * part;
+    if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) w[i] = ((const uint32_t*)p)[i];
+    } else {
+        uint32_t h[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) h[i] = ((const uint16_t*)p)[i];
+#pragma unroll
+        for (int i = 0; i < (N + 1) / 2; ++i) w[i] = h[2 * i] | ((2 * i + 1 < N ? h[2 * i + 1] : 0u) << 16);
+    }
+}
+
+// Dequantized values of dims [16*part, 16*part+16) of quantized token row t.
+template <int FMT>
+__device__ __forceinline__ void dequant16(const char* st, const StreamLayout& L, int64_t t, int part,
+                                          const float (&crow)[16], float (&x)[16])
+{
+    constexpr int N = fbits(FMT);
+    constexpr int KIND = fkind(FMT);
+    if constexpr (KIND == KIND_BF16) {
+        const uint4* p = (const uint4*)(st + L.codes + t * 256 + 32 * part);
+        uint4 a = p[0], b = p[1];
+        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    } else {
+        uint32_t w[(N + 1) / 2];
+        load_codes16<N>(st + L.codes + t * (16 * N), part, w);
+        const int b = part >> 1;
+        if constexpr (KIND == KIND_Q1) {
+            uint32_t dm = *(const uint32_t*)(st + L.scales + t * 16 + 4 * b);
+            float d = fp16_to_f32(dm & 0xFFFFu), m = fp16_to_f32(dm >> 16);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = m + d * (float)code_at<N>(w, j);
+        } else {
+            float d = fp16_to_f32(*(const uint16_t*)(st + L.scales + t * 8 + 2 * b));
+            const float off = (float)(1 << (N - 1));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                float c = ((float)code_at<N>(w, j) - off) * d;
+                if constexpr (KIND == KIND_KVARN) c *= crow[j];
+                x[j] = c;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void ring16(const char* st, const StreamLayout& L, int64_t slot, int part, float (&x)[16])
+{
+    const uint4* p = (const uint4*)(st + L.ring + slot * 256 + 32 * part);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+}
+
+struct Online {
+    float m[kG], l[kG], acc[kG][16];
+};
+
+__device__ __forceinline__ void online_step(Online& o, const float (&qr)[kG][16], const float (&k)[16],
+                                            const float (&v)[16], bool valid)
+{
+    float s[kG];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+        float ps = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) ps = fmaf(qr[h][j], k[j], ps);
+        s[h] = sum8(ps);
+    }
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+        float mn = valid ? fmaxf(o.m[h], s[h]) : o.m[h];
+        float alpha = __builtin_amdgcn_exp2f(o.m[h] - mn);
+        float p = valid ? __builtin_amdgcn_exp2f(s[h] - mn) : 0.0f;
+        o.m[h] = mn;
+        o.l[h] = o.l[h] * alpha + p;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o.acc[h][j] = fmaf(p, v[j], o.acc[h][j] * alpha);
+    }
+}
+
+// Combine two online states (m1,l1,a1) <- (m1,l1,a1) (+) (m2,l2,a2).
+__device__ __forceinline__ void combine(float& m1, float& l1, float* a1, float m2, float l2, const float* a2, int n)
+{
+    float M = fmaxf(m1, m2);
+    float e1 = __builtin_amdgcn_exp2f(m1 - M), e2 = __builtin_amdgcn_exp2f(m2 - M);
+    l1 = l1 * e1 + l2 * e2;
+    for (int j = 0; j < n; ++j) a1[j] = a1[j] * e1 + a2[j] * e2;
+    m1 = M;
+}
+
+// In-place unnormalized Walsh-Hadamard transform of rows [kG][128] held in LDS.
+__device__ __forceinline__ void lds_fwht(float (*buf)[kD])
+{
+    const int tid = threadIdx.x;
+    for (int h = 1; h < kD; h <<= 1) {
+        __syncthreads();
+        // 256 threads, kG*64 butterflies per stage
+        for (int pi = tid; pi < kG * 64; pi += blockDim.x) {
+            int r = pi >> 6, k = pi & 63;
+            int lo = k & (h - 1);
+            int i = ((k - lo) << 1) | lo;
+            float a = buf[r][i], b = buf[r][i + h];
+            buf[r][i] = a + b;
+            buf[r][i + h] = a - b;
+        }
+    }
+    __syncthreads();
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
+{
+    constexpr int KIND = fkind(FMT);
+    __shared__ float qs[kG][kD];
+    __shared__ float wm[4][kG], wl[4][kG];
+    __shared__ float wacc[4][kG][kD];
+    __shared__ int last_flag;
+
+    const int tid = threadIdx.x;
+    const int bid = blockIdx.x;
+    // ---- which (sequence, KV head, split) ------------------------------------------------
+    int e = 0;
+    for (int i = 1; i < a.n_seqs; ++i)
+        if (a.seqs[i].wg_base <= bid) e = i;
+    const DecodeSeq& sq = a.seqs[e];
+    const int S = sq.splits_q + sq.splits_t;
+    const int r = bid - sq.wg_base;
+    const int head = r / S;
+    const int sp = r % S;
+    const bool quant = sp < sq.splits_q;
+    const int u_lo = (quant ? sp : sp - sq.splits_q) * a.units_per_wg;
+    const int u_cnt = quant ? sq.units_q : sq.units_t;
+    const int u_hi = min(u_lo + a.units_per_wg, u_cnt);
+    const CacheGeom& g = a.g;
+    const char* kst = stream_cptr(g, sq.seq, a.layer, head, 0);
+    const char* vst = stream_cptr(g, sq.seq, a.layer, head, 1);
+
+    // ---- query of the kG heads of this KV head, scaled to the log2 domain ------------------
+    for (int i = tid; i < kG * kD; i += blockDim.x) {
+        int hh = i / kD, d = i % kD;
+        int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + hh) * kD + d;
+        float qv = a.q_dtype ? ((const float*)a.q)[qi] : bf16_to_f32(((const uint16_t*)a.q)[qi]);
+        qs[hh][d] = qv * a.scale_log2;
+    }
+    __syncthreads();
+    if (KIND == KIND_KVARN && quant) {
+        lds_fwht(qs);
+        for (int i = tid; i < kG * kD; i += blockDim.x) qs[i / kD][i % kD] *= (1.0f / 128.0f);
+        __syncthreads();
+    }
+    const int wave = tid >> 6, lane = tid & 63, slot = lane >> 3, part = lane & 7;
+    float qr[kG][16];
+#pragma unroll
+    for (int h = 0; h < kG; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) qr[h][j] = qs[h][16 * part + j];
+
+    Online o;
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+        o.m[h] = kNegBig;
+        o.l[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o.acc[h][j] = 0.0f;
+    }
+
+    // ---- main loop: units round-robin over the 4 waves --------------------------------------
+    for (int u = u_lo + wave; u < u_hi; u += 4) {
+        if (quant) {
+            const int64_t t0 = (int64_t)u * kPage;
+            const int64_t t1 = min<int64_t>(t0 + kPage, sq.n_q);
+            float ck[16], cv[16];
+            if constexpr (KIND == KIND_KVARN) {
+                const uint16_t* cks = (const uint16_t*)(kst + g.k.cscale + (int64_t)u * 256) + 16 * part;
+                const uint16_t* cvs = (const uint16_t*)(vst + g.v.cscale + (int64_t)u * 256) + 16 * part;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) { ck[j] = fp16_to_f32(cks[j]); cv[j] = fp16_to_f32(cvs[j]); }
+            }
+            for (int64_t tb = t0; tb < t1; tb += 8) {
+                const int64_t t = tb + slot;
+                const bool valid = t < t1;
+                const int64_t tc = valid ? t : t1 - 1;
+                float k[16], v[16];
+                dequant16<FMT>(kst, g.k, tc, part, ck, k);
+                dequant16<FMT>(vst, g.v, tc, part, cv, v);
+                online_step(o, qr, k, v, valid);
+            }
+        } else {
+            const int64_t t0 = sq.n_q + (int64_t)u * kTailUnit;
+            const int64_t t1 = min<int64_t>(t0 + kTailUnit, sq.n);
+            for (int64_t tb = t0; tb < t1; tb += 8) {
+                const int64_t t = tb + slot;
+                const bool valid = t < t1;
+                const int64_t tc = valid ? t : t1 - 1;
+                const int64_t rs = tc % g.ring_slots;
+                float k[16], v[16];
+                ring16(kst, g.k, rs, part, k);
+                ring16(vst, g.v, rs, part, v);
+                online_step(o, qr, k, v, valid);
+            }
+        }
+    }
+
+    // ---- merge the 8 token slots of the wave (lanes with equal part) --------------------------
+#pragma unroll 1
+    for (int x = 8; x < 64; x <<= 1) {
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            float m2 = __shfl_xor(o.m[h], x);
+            float l2 = __shfl_xor(o.l[h], x);
+            float a2[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) a2[j] = __shfl_xor(o.acc[h][j], x);
+            combine(o.m[h], o.l[h], o.acc[h], m2, l2, a2, 16);
+        }
+    }
+    if (slot == 0) {
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) wacc[wave][h][16 * part + j] = o.acc[h][j];
+            if (part == 0) { wm[wave][h] = o.m[h]; wl[wave][h] = o.l[h]; }
+        }
+    }
+    __syncthreads();
+    // ---- merge the 4 waves, write this workgroup's partial -----------------------------------
+    float* part_out = a.partials + (int64_t)bid * kPartialFloats;
+    for (int i = tid; i < kG * kD; i += blockDim.x) {
+        const int h = i / kD, d = i % kD;
+        float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float ew = __builtin_amdgcn_exp2f(wm[w][h] - M);
+            L += wl[w][h] * ew;
+            A += wacc[w][h][d] * ew;
+        }
+        part_out[2 * kMaxGroup + h * kD + d] = A;
+        if (d == 0) { part_out[h] = M; part_out[kMaxGroup + h] = L; }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* ctr = a.counters + sq.in_idx * g.n_kv_heads + head;
+        uint32_t old = atomicAdd(ctr, 1u);
+        int last = (old == (uint32_t)(S - 1));
+        if (last) *ctr = 0u;                 // leave the workspace reusable
+        last_flag = last;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+
+    // ---- last workgroup of this (sequence, KV head): merge all splits -------------------------
+    const int first = sq.wg_base + head * S;
+    float (*oq)[kD] = wacc[0];               // reuse LDS: quantized-domain sums
+    float (*ot)[kD] = wacc[1];               // ring-domain sums
+    float (*Ls)[kG] = wl;                    // reuse: total sum per head in wl[0]
+    for (int i = tid; i < kG * kD; i += blockDim.x) {
+        const int h = i / kD, d = i % kD;
+        float M = kNegBig;
+        for (int s = 0; s < S; ++s) {
+            const float* pp = a.partials + (int64_t)(first + s) * kPartialFloats;
+            M = fmaxf(M, __hip_atomic_load(pp + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        float L = 0.0f, Aq = 0.0f, At = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            const float* pp = a.partials + (int64_t)(first + s) * kPartialFloats;
+            float m = __hip_atomic_load(pp + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float l = __hip_atomic_load(pp + kMaxGroup + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float ac = __hip_atomic_load(pp + 2 * kMaxGroup + h * kD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float ew = __builtin_amdgcn_exp2f(m - M);
+            L += l * ew;
+            if (s < sq.splits_q) Aq += ac * ew; else At += ac * ew;
+        }
+        oq[h][d] = Aq;
+        ot[h][d] = At;
+        if (d == 0) Ls[0][h] = L;
+    }
+    __syncthreads();
+    if constexpr (KIND == KIND_KVARN) {
+        lds_fwht(oq);
+    }
+    for (int i = tid; i < kG * kD; i += blockDim.x) {
+        const int h = i / kD, d = i % kD;
+        float vq = oq[h][d];
+        if constexpr (KIND == KIND_KVARN) vq *= (1.0f / 128.0f);
+        float res = (vq + ot[h][d]) / Ls[0][h];
+        a.out[((int64_t)sq.in_idx * g.n_q_heads + head * kG + h) * kD + d] = res;
+    }
+}
+
+template <int FMT>
+int launch_fmt(const DecodeArgs& a, int n_wgs, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_decode<FMT>, dim3(n_wgs), dim3(256), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+template <int FMT>
+int occ_fmt()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT>, 256, 0) != hipSuccess) return 0;
+    return n;
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    switch (a.g.fmt_k) {
+    case 0: return launch_fmt<0>(a, n_wgs, st);
+    case 1: return launch_fmt<1>(a, n_wgs, st);
+    case 2: return launch_fmt<2>(a, n_wgs, st);
+    case 3: return launch_fmt<3>(a, n_wgs, st);
+    case 4: return launch_fmt<4>(a, n_wgs, st);
+    case 5: return launch_fmt<5>(a, n_wgs, st);
+    case 6: return launch_fmt<6>(a, n_wgs, st);
+    case 7: return launch_fmt<7>(a, n_wgs, st);
+    case 8: return launch_fmt<8>(a, n_wgs, st);
+    case 9: return launch_fmt<9>(a, n_wgs, st);
+    case 10: return launch_fmt<10>(a, n_wgs, st);
+    case 11: return launch_fmt<11>(a, n_wgs, st);
+    case 12: return launch_fmt<12>(a, n_wgs, st);
+    case 13: return launch_fmt<13>(a, n_wgs, st);
+    case 14: return launch_fmt<14>(a, n_wgs, st);
+    case 15: return launch_fmt<15>(a, n_wgs, st);
+    case 16: return launch_fmt<16>(a, n_wgs, st);
+    case 17: return launch_fmt<17>(a, n_wgs, st);
+    case 18: return launch_fmt<18>(a, n_wgs, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
+{
+    (void)fmt_v;
+    (void)group;
+    static int cache[19] = {0};
+    if (fmt_k < 0 || fmt_k >= 19) return 0;
+    if (cache[fmt_k]) return cache[fmt_k];
+    int n = 0;
+    switch (fmt_k) {
+    case 0: n = occ_fmt<0>(); break;
+    case 1: n = occ_fmt<1>(); break;
+    case 2: n = occ_fmt<2>(); break;
+    case 3: n = occ_fmt<3>(); break;
+    case 4: n = occ_fmt<4>(); break;
+    case 5: n = occ_fmt<5>(); break;
+    case 6: n = occ_fmt<6>(); break;
+    case 7: n = occ_fmt<7>(); break;
+    case 8: n = occ_fmt<8>(); break;
+    case 9: n = occ_fmt<9>(); break;
+    case 10: n = occ_fmt<10>(); break;
+    case 11: n = occ_fmt<11>(); break;
+    case 12: n = occ_fmt<12>(); break;
+    case 13: n = occ_fmt<13>(); break;
+    case 14: n = occ_fmt<14>(); break;
+    case 15: n = occ_fmt<15>(); break;
+    case 16: n = occ_fmt<16>(); break;
+    case 17: n = occ_fmt<17>(); break;
+    case 18: n = occ_fmt<18>(); break;
+    default: break;
+    }
+    cache[fmt_k] = n;
+    return n;
+}
+
+int device_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static int cache[64] = {0};
+    if (dev < 0 || dev >= 64) return 0;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+}  // namespace kvq

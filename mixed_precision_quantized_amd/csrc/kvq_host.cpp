@@ -1,0 +1,458 @@
+// kvq_host.cpp -- host side of the C ABI declared in include/kvq.h.
+//
+// Host-only translation unit: argument validation, buffer sizing and layout, the
+// precision-tail state machine and the decode split planner.  It contains no device
+// code and calls the HIP runtime only through the launchers of kvq_internal.h, so every
+// validation path runs (and is tested) on a machine without a GPU.
+//
+// Tail state machine ("Экспериментальные методы квантизации KV-кэша в BeeLLama.cpp
+// v0.4.0: KVarN и precision tail", section "Как это работает: гибридное хранение
+// кэша": the last T tokens stay BF16, positions before them use the low-bit type):
+//   granule G = 128 if a stream is KVarN (whole pages are encoded at once), else 1;
+//   after an append n += n_new and n_q = max(n_q, G*floor(max(0, n - T)/G));
+//   after a spill with keep tokens n_q = max(n_q, G*floor(max(0, n - keep)/G));
+//   token p with n_q <= p < n lives in ring slot p mod R, R = G*ceil((T+G-1)/G).
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+struct kv_cache {
+    kv_config cfg;
+    CacheGeom geom;
+    int64_t granule;
+    int64_t ring_slots;
+    int64_t max_tokens_pad;
+    int64_t bytes;
+    std::vector<int64_t> n;    // [seq * n_layers + layer]
+    std::vector<int64_t> nq;
+};
+
+namespace {
+
+bool format_desc(int32_t fmt, FormatDesc* d)
+{
+    static const int8_t bits[KV_NUM_FORMATS] = {16, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6, 8, 8, 2, 3, 4, 5, 6, 8};
+    if (fmt < 0 || fmt >= KV_NUM_FORMATS) return false;
+    FormatDesc r;
+    r.bits = bits[fmt];
+    if (fmt == KV_BF16) r.kind = KIND_BF16;
+    else if (fmt >= KV_KVARN2) r.kind = KIND_KVARN;
+    else r.kind = ((fmt - KV_Q2_0) % 2 == 0) ? KIND_Q0 : KIND_Q1;
+    r.code_bytes = (r.kind == KIND_BF16) ? 256 : 16 * r.bits;
+    r.scale_bytes = (r.kind == KIND_BF16) ? 0 : (r.kind == KIND_Q1 ? 16 : 8);
+    r.page_bytes = (r.kind == KIND_KVARN) ? 256 : 0;
+    *d = r;
+    return true;
+}
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+StreamLayout stream_layout(const FormatDesc& f, int64_t tokens_pad, int64_t ring_slots)
+{
+    StreamLayout s;
+    int64_t off = 0;
+    s.codes = off;
+    off = align256(off + tokens_pad * f.code_bytes);
+    s.scales = off;
+    off = align256(off + tokens_pad * f.scale_bytes);
+    if (f.kind == KIND_KVARN) {
+        s.cscale = off;
+        off = align256(off + (tokens_pad / kPage) * 256);
+    } else {
+        s.cscale = -1;
+    }
+    s.ring = off;
+    off = align256(off + ring_slots * 256);
+    s.bytes = off;
+    return s;
+}
+
+int64_t granule_of(int32_t fk, int32_t fv)
+{
+    FormatDesc a, b;
+    format_desc(fk, &a);
+    format_desc(fv, &b);
+    return (a.kind == KIND_KVARN || b.kind == KIND_KVARN) ? kPage : 1;
+}
+
+int64_t ring_capacity(int64_t T, int64_t G) { return G * ((T + G - 1 + G - 1) / G); }
+
+int64_t nq_after(int64_t nq, int64_t n, int64_t keep, int64_t G)
+{
+    int64_t over = std::max<int64_t>(0, n - keep);
+    return std::max(nq, G * (over / G));
+}
+
+// Validates a configuration; fills the geometry (without base pointer) and total bytes.
+int plan_config(const kv_config* cfg, CacheGeom* geom, int64_t* total, int64_t* G,
+                int64_t* R, int64_t* tok_pad)
+{
+    if (!cfg) return KV_EINVAL;
+    if (cfg->n_layers < 1 || cfg->n_kv_heads < 1 || cfg->n_q_heads < 1 || cfg->n_seqs < 1 ||
+        cfg->max_tokens < 1 || cfg->tail_tokens < 0)
+        return KV_EINVAL;
+    if (cfg->n_q_heads % cfg->n_kv_heads) return KV_EINVAL;
+    FormatDesc fk, fv;
+    if (!format_desc(cfg->fmt_k, &fk) || !format_desc(cfg->fmt_v, &fv)) return KV_EINVAL;
+    if (cfg->head_dim != kD) return KV_EUNSUPPORTED;
+    int group = cfg->n_q_heads / cfg->n_kv_heads;
+    if (group > kMaxGroup) return KV_EUNSUPPORTED;
+    // decode kernels are built for one format shared by K and V, and GQA groups of 4
+    if (cfg->fmt_k != cfg->fmt_v) return KV_EUNSUPPORTED;
+    if (group != 4) return KV_EUNSUPPORTED;
+    if (cfg->max_tokens > (int64_t(1) << 31) - kPage) return KV_EINVAL;
+    int64_t g = granule_of(cfg->fmt_k, cfg->fmt_v);
+    // The ring never holds more than min(T + G - 1, n) tokens, so a ring larger than the
+    // capacity rounded up to G is never needed.
+    int64_t r = std::min(ring_capacity(cfg->tail_tokens, g), ((cfg->max_tokens + g - 1) / g) * g);
+    int64_t tp = ((cfg->max_tokens + kPage - 1) / kPage) * kPage;
+    CacheGeom gm;
+    std::memset(&gm, 0, sizeof(gm));
+    gm.k = stream_layout(fk, tp, r);
+    gm.v = stream_layout(fv, tp, r);
+    gm.v_offset = gm.k.bytes;
+    gm.unit_bytes = gm.k.bytes + gm.v.bytes;
+    gm.fmt_k = cfg->fmt_k;
+    gm.fmt_v = cfg->fmt_v;
+    gm.n_layers = cfg->n_layers;
+    gm.n_kv_heads = cfg->n_kv_heads;
+    gm.n_q_heads = cfg->n_q_heads;
+    gm.group = group;
+    gm.ring_slots = (int32_t)r;
+    double units = (double)cfg->n_seqs * cfg->n_layers * cfg->n_kv_heads;
+    if (units * (double)gm.unit_bytes > 9.0e18) return KV_EINVAL;
+    if (geom) *geom = gm;
+    if (total) *total = (int64_t)units * gm.unit_bytes;
+    if (G) *G = g;
+    if (R) *R = r;
+    if (tok_pad) *tok_pad = tp;
+    return KV_OK;
+}
+
+inline int64_t& n_at(kv_cache* c, int s, int l) { return c->n[(size_t)s * c->cfg.n_layers + l]; }
+inline int64_t& nq_at(kv_cache* c, int s, int l) { return c->nq[(size_t)s * c->cfg.n_layers + l]; }
+
+bool distinct_valid_ids(const kv_cache* c, int32_t n_seqs, const int32_t* ids)
+{
+    if (!ids || n_seqs < 1 || n_seqs > c->cfg.n_seqs) return false;
+    std::vector<char> seen(c->cfg.n_seqs, 0);
+    for (int i = 0; i < n_seqs; ++i) {
+        if (ids[i] < 0 || ids[i] >= c->cfg.n_seqs || seen[ids[i]]) return false;
+        seen[ids[i]] = 1;
+    }
+    return true;
+}
+
+// Enqueue the encode launches for one group of at most kMaxSeqsPerLaunch sequences.
+int launch_group(kv_cache* c, AppendArgs& a, void* stream)
+{
+    FormatDesc fk, fv;
+    format_desc(c->cfg.fmt_k, &fk);
+    format_desc(c->cfg.fmt_v, &fv);
+    bool any_enc = false, any_ring = false;
+    for (int i = 0; i < a.n_seqs; ++i) {
+        const AppendSeq& s = a.seqs[i];
+        if (s.nq_new > s.nq_old) any_enc = true;
+        if (s.n_new > std::max(s.nq_new, s.n_old)) any_ring = true;
+    }
+    int rc = 0;
+    if (any_enc) {
+        if (fk.kind != KIND_KVARN || fv.kind != KIND_KVARN) {
+            rc = launch_append_encode(a, stream);
+            if (rc) return rc;
+        }
+        if (fk.kind == KIND_KVARN || fv.kind == KIND_KVARN) {
+            rc = launch_append_kvarn(a, stream);
+            if (rc) return rc;
+        }
+    }
+    // ring writes strictly after the encoders, which may read the slots being reused
+    if (any_ring) rc = launch_append_ring(a, stream);
+    return rc;
+}
+
+// Shared body of kv_append and kv_spill_tail once every argument is validated.
+// entries: per sequence (seq, rows before it, n_new tokens); keep: T or keep_tokens.
+int do_append(kv_cache* c, int32_t layer, int n_seqs, const int32_t* seqs, const int32_t* n_add,
+              const void* k, const void* v, int32_t in_dtype, int64_t keep, void* stream)
+{
+    const int L = c->cfg.n_layers;
+    const int l0 = layer < 0 ? 0 : layer;
+    const int l1 = layer < 0 ? L : layer + 1;
+    int64_t rows = 0;
+    for (int i = 0; i < n_seqs; ++i) rows += n_add[i];
+    std::vector<int64_t> new_n((size_t)n_seqs), new_nq((size_t)n_seqs);
+    for (int i = 0; i < n_seqs; ++i) {
+        int64_t n0 = n_at(c, seqs[i], l0);
+        new_n[i] = n0 + n_add[i];
+        new_nq[i] = nq_after(nq_at(c, seqs[i], l0), new_n[i], keep, c->granule);
+    }
+    // One launch set per layer range: when layer == -1 every layer of a sequence has the
+    // same (n, n_q), so the per-sequence entries hold for all layers.
+    for (int base = 0; base < n_seqs; base += kMaxSeqsPerLaunch) {
+        AppendArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.g = c->geom;
+        a.k_in = k;
+        a.v_in = v;
+        a.in_dtype = in_dtype;
+        a.layer0 = l0;
+        a.layers_in = l1 - l0;
+        a.rows = (int32_t)rows;
+        int cnt = std::min(kMaxSeqsPerLaunch, n_seqs - base);
+        a.n_seqs = cnt;
+        int64_t row0 = 0;
+        for (int i = 0; i < base; ++i) row0 += n_add[i];
+        for (int i = 0; i < cnt; ++i) {
+            int j = base + i;
+            AppendSeq& s = a.seqs[i];
+            s.seq = seqs[j];
+            s.in_row0 = (int32_t)row0;
+            s.n_old = n_at(c, seqs[j], l0);
+            s.n_new = new_n[j];
+            s.nq_old = nq_at(c, seqs[j], l0);
+            s.nq_new = new_nq[j];
+            row0 += n_add[j];
+        }
+        int rc = launch_group(c, a, stream);
+        if (rc) {
+            // metadata advances anyway: the launches before the failure may have run
+            for (int i = 0; i < n_seqs; ++i)
+                for (int l = l0; l < l1; ++l) { n_at(c, seqs[i], l) = new_n[i]; nq_at(c, seqs[i], l) = new_nq[i]; }
+            return KV_EDEVICE;
+        }
+    }
+    for (int i = 0; i < n_seqs; ++i)
+        for (int l = l0; l < l1; ++l) {
+            n_at(c, seqs[i], l) = new_n[i];
+            nq_at(c, seqs[i], l) = new_nq[i];
+        }
+    return KV_OK;
+}
+
+bool layers_agree(kv_cache* c, int32_t seq)
+{
+    for (int l = 1; l < c->cfg.n_layers; ++l)
+        if (n_at(c, seq, l) != n_at(c, seq, 0) || nq_at(c, seq, l) != nq_at(c, seq, 0)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_format_info(int32_t fmt, int32_t* bits, int32_t* code_bytes, int32_t* scale_bytes,
+                   int32_t* page_bytes)
+{
+    FormatDesc d;
+    if (!format_desc(fmt, &d)) return KV_EINVAL;
+    if (bits) *bits = d.bits;
+    if (code_bytes) *code_bytes = d.code_bytes;
+    if (scale_bytes) *scale_bytes = d.scale_bytes;
+    if (page_bytes) *page_bytes = d.page_bytes;
+    return KV_OK;
+}
+
+int64_t kv_cache_bytes(const kv_config* cfg)
+{
+    int64_t total = 0;
+    int rc = plan_config(cfg, nullptr, &total, nullptr, nullptr, nullptr);
+    return rc ? rc : total;
+}
+
+int kv_cache_init(const kv_config* cfg, void* dev_mem, int64_t bytes, kv_cache** out)
+{
+    if (!out) return KV_EINVAL;
+    *out = nullptr;
+    CacheGeom g;
+    int64_t total, G, R, tp;
+    int rc = plan_config(cfg, &g, &total, &G, &R, &tp);
+    if (rc) return rc;
+    if (!dev_mem || ((uintptr_t)dev_mem & 255)) return KV_EINVAL;
+    if (bytes < total) return KV_ESIZE;
+    kv_cache* c = new (std::nothrow) kv_cache;
+    if (!c) return KV_EINVAL;
+    c->cfg = *cfg;
+    g.base = (char*)dev_mem;
+    c->geom = g;
+    c->granule = G;
+    c->ring_slots = R;
+    c->max_tokens_pad = tp;
+    c->bytes = total;
+    size_t cells = (size_t)cfg->n_seqs * cfg->n_layers;
+    c->n.assign(cells, 0);
+    c->nq.assign(cells, 0);
+    *out = c;
+    return KV_OK;
+}
+
+int kv_cache_destroy(kv_cache* c)
+{
+    delete c;
+    return KV_OK;
+}
+
+int kv_append(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+              const int32_t* n_new, const void* k, const void* v, int32_t in_dtype, void* stream)
+{
+    if (!c || !n_new) return KV_EINVAL;
+    if (layer < -1 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (in_dtype != KV_IN_BF16 && in_dtype != KV_IN_F32) return KV_EINVAL;
+    if (!distinct_valid_ids(c, n_seqs, seq_ids)) return KV_EINVAL;
+    int64_t rows = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        if (n_new[i] < 0) return KV_EINVAL;
+        rows += n_new[i];
+    }
+    if (rows > (int64_t(1) << 30)) return KV_EINVAL;
+    if (rows > 0 && (!k || !v)) return KV_EINVAL;
+    const int l0 = layer < 0 ? 0 : layer;
+    for (int i = 0; i < n_seqs; ++i) {
+        if (layer < 0 && !layers_agree(c, seq_ids[i])) return KV_EINVAL;
+        if (n_at(c, seq_ids[i], l0) + n_new[i] > c->cfg.max_tokens) return KV_ENOSPC;
+    }
+    if (rows == 0) return KV_OK;
+    return do_append(c, layer, n_seqs, seq_ids, n_new, k, v, in_dtype, c->cfg.tail_tokens, stream);
+}
+
+int kv_spill_tail(kv_cache* c, int32_t layer, int32_t seq_id, int32_t keep_tokens, void* stream)
+{
+    if (!c) return KV_EINVAL;
+    if (layer < -1 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (seq_id < 0 || seq_id >= c->cfg.n_seqs) return KV_EINVAL;
+    if (keep_tokens < 0 || keep_tokens > c->cfg.tail_tokens) return KV_EINVAL;
+    if (layer < 0) {
+        // layers may differ here: spill each layer on its own
+        if (!layers_agree(c, seq_id)) {
+            for (int l = 0; l < c->cfg.n_layers; ++l) {
+                int rc = kv_spill_tail(c, l, seq_id, keep_tokens, stream);
+                if (rc) return rc;
+            }
+            return KV_OK;
+        }
+    }
+    int32_t zero = 0;
+    return do_append(c, layer, 1, &seq_id, &zero, nullptr, nullptr, KV_IN_BF16, keep_tokens, stream);
+}
+
+int64_t kv_decode_workspace_bytes(const kv_cache* c, int32_t n_seqs)
+{
+    if (!c || n_seqs < 1 || n_seqs > c->cfg.n_seqs) return KV_EINVAL;
+    int64_t part = (int64_t)kMaxDecodeWGs * kPartialFloats * 4;
+    int64_t cnt = (int64_t)kMaxSeqsPerLaunch * c->cfg.n_kv_heads * 4;
+    return align256(part) + align256(cnt);
+}
+
+int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                   const void* q, int32_t q_dtype, float softmax_scale, float* out,
+                   void* workspace, int64_t ws_bytes, void* stream)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (!distinct_valid_ids(c, n_seqs, seq_ids)) return KV_EINVAL;
+    if (n_seqs > kMaxSeqsPerLaunch) return KV_EUNSUPPORTED;
+    if (!q || !out || !workspace) return KV_EINVAL;
+    if (q_dtype != KV_IN_BF16 && q_dtype != KV_IN_F32) return KV_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+        return KV_EINVAL;
+    if (ws_bytes < kv_decode_workspace_bytes(c, n_seqs)) return KV_ESIZE;
+    for (int i = 0; i < n_seqs; ++i)
+        if (n_at(c, seq_ids[i], layer) == 0) return KV_EEMPTY;
+
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.g = c->geom;
+    a.layer = layer;
+    a.n_seqs = n_seqs;
+    a.q_dtype = q_dtype;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.q = q;
+    a.out = out;
+    a.partials = (float*)workspace;
+    a.counters = (uint32_t*)((char*)workspace + align256((int64_t)kMaxDecodeWGs * kPartialFloats * 4));
+
+    const int H = c->cfg.n_kv_heads;
+    int64_t total_units = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        DecodeSeq& s = a.seqs[i];
+        s.seq = seq_ids[i];
+        s.in_idx = i;
+        s.n = n_at(c, seq_ids[i], layer);
+        s.n_q = nq_at(c, seq_ids[i], layer);
+        s.units_q = (int32_t)((s.n_q + kPage - 1) / kPage);
+        s.units_t = (int32_t)((s.n - s.n_q + kTailUnit - 1) / kTailUnit);
+        total_units += (int64_t)H * (s.units_q + s.units_t);
+    }
+    // Balanced split: every workgroup gets about the same number of units, sized so the
+    // whole grid is resident at once.
+    int cus = device_cu_count();
+    int per_cu = decode_wgs_per_cu(c->cfg.fmt_k, c->cfg.fmt_v, c->geom.group);
+    if (cus <= 0 || per_cu <= 0) return KV_EDEVICE;
+    int64_t target = (int64_t)cus * per_cu;
+    int64_t upw = std::max<int64_t>(1, (total_units + target - 1) / target);
+    int64_t wgs;
+    for (;;) {
+        wgs = 0;
+        for (int i = 0; i < n_seqs; ++i) {
+            DecodeSeq& s = a.seqs[i];
+            // quantized and ring units never share a workgroup: KVarN accumulates the
+            // quantized values in the rotated domain, the ring values in the original one
+            s.splits_q = (int32_t)((s.units_q + upw - 1) / upw);
+            s.splits_t = (int32_t)((s.units_t + upw - 1) / upw);
+            s.wg_base = (int32_t)wgs;
+            wgs += (int64_t)H * (s.splits_q + s.splits_t);
+        }
+        if (wgs <= kMaxDecodeWGs) break;
+        upw *= 2;
+    }
+    a.units_per_wg = (int32_t)upw;
+    int rc = launch_decode(a, (int)wgs, stream);
+    return rc ? KV_EDEVICE : KV_OK;
+}
+
+int kv_seq_get(const kv_cache* c, int32_t seq, int32_t layer, int64_t* n, int64_t* n_q)
+{
+    if (!c || seq < 0 || seq >= c->cfg.n_seqs || layer < 0 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    size_t i = (size_t)seq * c->cfg.n_layers + layer;
+    if (n) *n = c->n[i];
+    if (n_q) *n_q = c->nq[i];
+    return KV_OK;
+}
+
+int kv_seq_set(kv_cache* c, int32_t seq, int32_t layer, int64_t n, int64_t n_q)
+{
+    if (!c || seq < 0 || seq >= c->cfg.n_seqs || layer < -1 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (n_q < 0 || n_q > n || n > c->cfg.max_tokens) return KV_EINVAL;
+    if (n_q % c->granule) return KV_EINVAL;
+    if (n - n_q > c->ring_slots) return KV_EINVAL;
+    int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->cfg.n_layers : layer + 1;
+    for (int l = l0; l < l1; ++l) {
+        n_at(c, seq, l) = n;
+        nq_at(c, seq, l) = n_q;
+    }
+    return KV_OK;
+}
+
+int kv_stream_layout(const kv_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t is_v,
+                     int64_t offsets[4], int64_t* ring_slots)
+{
+    if (!c || !offsets || seq < 0 || seq >= c->cfg.n_seqs || layer < 0 || layer >= c->cfg.n_layers ||
+        kv_head < 0 || kv_head >= c->cfg.n_kv_heads || (is_v != 0 && is_v != 1))
+        return KV_EINVAL;
+    int64_t unit = ((int64_t)seq * c->cfg.n_layers + layer) * c->cfg.n_kv_heads + kv_head;
+    int64_t base = unit * c->geom.unit_bytes + (is_v ? c->geom.v_offset : 0);
+    const StreamLayout& s = is_v ? c->geom.v : c->geom.k;
+    offsets[0] = base + s.codes;
+    offsets[1] = base + s.scales;
+    offsets[2] = s.cscale < 0 ? -1 : base + s.cscale;
+    offsets[3] = base + s.ring;
+    if (ring_slots) *ring_slots = c->ring_slots;
+    return KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// kvq_internal.h -- layout of the cache buffer and the argument blocks passed from the
+// host library to the HIP kernels.  Plain C++ (no HIP types): included by the host-only
+// translation unit and by the kernel translation units.
+#pragma once
+
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kD = 128;          // head_dim
+constexpr int kBlock = 32;       // dims per block scale
+constexpr int kPage = 128;       // tokens per KVarN page (channel-scale row)
+constexpr int kTailUnit = 32;    // tokens of the BF16 ring per decode work unit
+constexpr int kMaxSeqsPerLaunch = 32;
+constexpr int kMaxGroup = 8;     // query heads per KV head
+
+enum Kind : int32_t { KIND_BF16 = 0, KIND_Q0 = 1, KIND_Q1 = 2, KIND_KVARN = 3 };
+
+struct FormatDesc {
+    int32_t bits;         // N (16 for bf16)
+    int32_t kind;         // Kind
+    int32_t code_bytes;   // per token: 16N, or 256 for bf16
+    int32_t scale_bytes;  // per token: 8 (qN_0, kvarn), 16 (qN_1), 0 (bf16)
+    int32_t page_bytes;   // per 128-token page: 256 (kvarn), else 0
+};
+
+// Byte layout of one stream (the K or V history of one (seq, layer, kv_head)).
+// All offsets are relative to the start of the stream and 256-byte aligned.
+struct StreamLayout {
+    int64_t codes;        // [max_tokens_pad][code_bytes]
+    int64_t scales;       // [max_tokens_pad][scale_bytes]
+    int64_t cscale;       // [max_tokens_pad/128][128] fp16, or -1
+    int64_t ring;         // [ring_slots][128] bf16
+    int64_t bytes;        // total bytes of the stream
+};
+
+// Everything a kernel needs to address a stream.
+struct CacheGeom {
+    char* base;           // device buffer
+    int64_t unit_bytes;   // bytes of one (seq, layer, kv_head): K stream then V stream
+    int64_t v_offset;     // offset of the V stream inside a unit (= K stream bytes)
+    StreamLayout k, v;
+    int32_t fmt_k, fmt_v;
+    int32_t n_layers, n_kv_heads, n_q_heads, group;
+    int32_t ring_slots;   // R
+    int32_t pad_;
+};
+
+// Per-sequence entry of an append launch.
+struct AppendSeq {
+    int32_t seq;          // cache sequence slot
+    int32_t in_row0;      // first input row of this sequence
+    int64_t n_old;        // tokens before the call
+    int64_t n_new;        // tokens after the call
+    int64_t nq_old;       // quantized boundary before
+    int64_t nq_new;       // quantized boundary after
+};
+
+struct AppendArgs {
+    CacheGeom g;
+    const void* k_in;     // [layers_in][rows][H][128]
+    const void* v_in;
+    int32_t in_dtype;     // 0 bf16, 1 fp32
+    int32_t layer0;       // first cache layer addressed
+    int32_t layers_in;    // layers present in the input (1 or n_layers)
+    int32_t rows;         // sum of n_new over the call (input rows per layer)
+    int32_t n_seqs;
+    int32_t pad_;
+    AppendSeq seqs[kMaxSeqsPerLaunch];
+};
+
+// Per-sequence entry of a decode launch.
+struct DecodeSeq {
+    int32_t seq;          // cache sequence slot
+    int32_t in_idx;       // index into q / out
+    int64_t n;
+    int64_t n_q;
+    int32_t units_q;      // quantized work units (128-token pages)
+    int32_t units_t;      // tail work units (32 tokens)
+    int32_t splits_q;     // workgroups per kv head over the quantized region
+    int32_t splits_t;     // workgroups per kv head over the BF16 ring
+    int32_t wg_base;      // first workgroup of this sequence
+    int32_t pad_;
+};
+
+struct DecodeArgs {
+    CacheGeom g;
+    int32_t layer;
+    int32_t n_seqs;
+    int32_t units_per_wg;
+    int32_t q_dtype;      // 0 bf16, 1 fp32
+    float scale_log2;     // softmax_scale * log2(e)
+    int32_t pad_;
+    const void* q;        // [n_seqs][n_q_heads][128]
+    float* out;           // [n_seqs][n_q_heads][128]
+    float* partials;      // [max_wgs][kPartialFloats]
+    uint32_t* counters;   // [n_seqs * n_kv_heads]
+    DecodeSeq seqs[kMaxSeqsPerLaunch];
+};
+
+constexpr int kPartialFloats = kMaxGroup * (kD + 2);   // m, l, acc[128] per query head
+constexpr int kMaxDecodeWGs = 8192;
+
+// Kernel launchers (implemented in the .hip translation units).  Return 0 on a
+// successful launch, or the HIP error code.
+int launch_append_encode(const AppendArgs& a, void* stream);   // qN / bf16 streams
+int launch_append_kvarn(const AppendArgs& a, void* stream);    // KVarN pages
+int launch_append_ring(const AppendArgs& a, void* stream);     // BF16 ring writes
+int launch_decode(const DecodeArgs& a, int n_wgs, void* stream);
+int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of the decode kernel
+int device_cu_count();
+
+}  // namespace kvq
