@@ -1,0 +1,267 @@
+"""Benchmark of the quantized KV cache hot path on one MI355X.
+
+Workload (default): 64 layers x 8 KV heads (32 query heads, GQA 4) x head_dim 128, one
+sequence at 240,000 tokens of context, kvarn4 cache with a 2,048-token BF16 tail, seeded
+synthetic bf16 K/V (Gaussian, 4 of 128 key channels x15).  A step is one pass of the whole
+hot path: append one token to all 64 layers (canonicalize, ring write, spill the oldest
+tail token, KVarN page encode every 128 steps) and decode attention on all 64 layers.
+
+Reported (one JSON line):
+  value      decode-attention KV read rate, GB/s: algorithmic bytes of the 64 decodes
+             (every quantized row K+V plus every BF16 ring row, read once) / their time
+  roofline   the decode kernel against HBM peak (8 TB/s), per launch from HIP events
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  append_tokens_per_s  64-layer appends of 512-token chunks (whole-model tokens per second)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--fmt", default="kvarn4")
+    p.add_argument("--ctx", type=int, default=240000)
+    p.add_argument("--layers", type=int, default=64)
+    p.add_argument("--tail", type=int, default=2048)
+    p.add_argument("--append-chunk", type=int, default=512)
+    p.add_argument("--append-reps", type=int, default=4)
+    p.add_argument("--cpu-units", type=int, default=16, help="(layer, kv head) units of the CPU sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0,
+                   help="only run a plain device copy of this many bytes (counter calibration)")
+    return p.parse_args()
+
+
+def stream_bytes(fmt):
+    from mixed_precision_quantized_amd import kvq
+    bits, cb, sb, pb = kvq.format_info(fmt)
+    return cb + sb + pb / 128.0
+
+
+def decode_bytes_layer(fmt, n, n_q, heads):
+    """Algorithmic bytes of one decode launch: every quantized row of K and V (codes,
+    block scales, amortized channel scales) plus every BF16 ring row, read once."""
+    return heads * (n_q * 2 * stream_bytes(fmt) + (n - n_q) * 2 * 256)
+
+
+def copy_probe(nbytes):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "dispatches": 5}))
+
+
+def fill_cache(cache, wl, layers, heads, ctx, chunk=16384):
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from mixed_precision_quantized_amd import synth
+    for layer in range(layers):
+        t = 0
+        while t < ctx:
+            c = min(chunk, ctx - t)
+            k = torch.stack([synth.kv_rows(wl, 0, layer, h, 0, t, t + c, "cuda") for h in range(heads)], 1)
+            v = torch.stack([synth.kv_rows(wl, 0, layer, h, 1, t, t + c, "cuda") for h in range(heads)], 1)
+            cache.append(layer, [0], [c], synth.to_bf16_bits(k).contiguous(), synth.to_bf16_bits(v).contiguous())
+            t += c
+        if layer % 16 == 15:
+            torch.cuda.synchronize()
+            print("  filled layer %d" % layer, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(fmt, wl, ctx, tail, units):
+    """The oracle, untuned, on `units` full-context (layer, KV head) units in parallel:
+    encode (append) then binary64 decode attention.  One thread per unit."""
+    import numpy as np
+    import oracle as O
+    from mixed_precision_quantized_amd import synth
+    f = O.FORMAT_NAMES.index(fmt)
+    G = O.granule(f, f)
+    n_q = O.nq_after(0, ctx, tail, G)
+    cores = min(units, os.cpu_count() or 1, 16)
+    units = cores
+    work = [(u // 8, u % 8) for u in range(units)]
+    data = {}
+
+    def gen(i):
+        layer, h = work[i]
+        k = synth.bf16_as_u16(synth.to_bf16_bits(synth.kv_rows(wl, 0, layer, h, 0, 0, ctx)))
+        v = synth.bf16_as_u16(synth.to_bf16_bits(synth.kv_rows(wl, 0, layer, h, 1, 0, ctx)))
+        data[i] = [k, v, None, None]
+
+    def enc(i):
+        k, v = data[i][0], data[i][1]
+        data[i][2] = O.encode_stream(f, n_q, k)
+        data[i][3] = O.encode_stream(f, n_q, v)
+
+    def att(i):
+        layer, h = work[i]
+        k, v, kq, vq = data[i]
+        q = synth.q_rows(wl, 0, layer, 0, 32)[4 * h: 4 * h + 4].double().numpy()
+        O.attention(ctx, n_q, f, f, kq, vq, k[n_q:], v[n_q:], q, 1.0 / math.sqrt(128))
+
+    def run(fn):
+        ths = [threading.Thread(target=fn, args=(i,)) for i in range(units)]
+        t0 = time.perf_counter()
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        return time.perf_counter() - t0
+
+    run(gen)
+    t_enc = run(enc)
+    t_att = run(att)
+    byts = units * decode_bytes_layer(fmt, ctx, n_q, 1)
+    return {
+        "value": round(byts / t_att / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": "%d full-context (layer, KV head) units of the same workload (%d tokens, %s, tail %d), "
+                  "one thread each: binary64 decode attention over the oracle's own encoding"
+                  % (units, ctx, fmt, tail),
+        "seconds": round(t_att, 2),
+        "append_tokens_per_s": round(units * ctx / (64 * 8) / t_enc, 1),
+        "append_seconds": round(t_enc, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    import torch
+    from mixed_precision_quantized_amd import kvq, synth
+
+    wl = "c4_ctx240000_64l"
+    L, H, QH = args.layers, 8, 32
+    steps, warm = args.steps, args.warmup
+    extra = warm + steps + args.append_chunk * args.append_reps + 256
+    print("bench: %s, %d layers, ctx %d, tail %d, %s" % (args.fmt, L, args.ctx, args.tail,
+          torch.cuda.get_device_name(0)), file=sys.stderr, flush=True)
+    cache = kvq.Cache(L, H, QH, args.fmt, tail_tokens=args.tail, n_seqs=1, max_tokens=args.ctx + extra)
+    t0 = time.time()
+    fill_cache(cache, wl, L, H, args.ctx)
+    torch.cuda.synchronize()
+    print("  fill %.1f s, cache %.2f GiB" % (time.time() - t0, cache.nbytes / 2**30), file=sys.stderr, flush=True)
+
+    qs = [synth.to_bf16_bits(synth.q_rows(wl, 0, l, 0, QH, "cuda")).unsqueeze(0).contiguous() for l in range(L)]
+    out = torch.empty((1, QH, 128), dtype=torch.float32, device="cuda")
+    tok_k = [synth.to_bf16_bits(torch.stack([synth.kv_rows(wl, 0, l, h, 0, args.ctx, args.ctx + extra, "cuda")
+                                             for h in range(H)], 1)) for l in range(L)]
+    tok_v = [synth.to_bf16_bits(torch.stack([synth.kv_rows(wl, 0, l, h, 1, args.ctx, args.ctx + extra, "cuda")
+                                             for h in range(H)], 1)) for l in range(L)]
+    K_all = torch.stack(tok_k, 0).contiguous()     # [L][extra][H][128]
+    V_all = torch.stack(tok_v, 0).contiguous()
+    del tok_k, tok_v
+    stream = torch.cuda.current_stream()
+    pos = [0]
+
+    def step(ev_dec=None):
+        # append one token to every layer (layer = -1: input [L][1][H][128])
+        i = pos[0]
+        cache.append(-1, [0], [1], K_all[:, i:i + 1].contiguous(), V_all[:, i:i + 1].contiguous())
+        pos[0] += 1
+        if ev_dec is not None:
+            ev_dec[0].record(stream)
+        for l in range(L):
+            cache.decode(l, [0], qs[l], out=out)
+        if ev_dec is not None:
+            ev_dec[1].record(stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    dec_bytes = 0.0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(steps):
+        step(evs[s])
+        n, n_q = cache.seq_get(0, 0)
+        dec_bytes += L * decode_bytes_layer(args.fmt, n, n_q, H)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    value = dec_bytes / steps / (dec_ms * 1e-3) / 1e9
+
+    # per-launch duration of the decode kernel (events around each launch)
+    n, n_q = cache.seq_get(0, 0)
+    per = []
+    for l in range(L):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cache.decode(l, [0], qs[l], out=out)
+        b.record(stream)
+        per.append((a, b))
+    torch.cuda.synchronize()
+    launch_ms = sum(a.elapsed_time(b) for a, b in per) / L
+    launch_bytes = decode_bytes_layer(args.fmt, n, n_q, H)
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+
+    # append throughput: 512-token chunks into all 64 layers (layer = -1)
+    ch = args.append_chunk
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start = pos[0]
+    a0.record(stream)
+    for r in range(args.append_reps):
+        i = start + r * ch
+        cache.append(-1, [0], [ch], K_all[:, i:i + ch].contiguous(), V_all[:, i:i + ch].contiguous())
+    a1.record(stream)
+    torch.cuda.synchronize()
+    app_tps = ch * args.append_reps / (a0.elapsed_time(a1) * 1e-3)
+
+    cpu = None
+    if not args.no_cpu:
+        print("  cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.fmt, wl, args.ctx, args.tail, args.cpu_units)
+
+    line = {
+        "metric": "decode-attn KV read GB/s (% of HBM peak) @240k ctx; append tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode step, 64 layers x 8 KV heads x 32 q heads x d128, ctx %d, %s, "
+                               "BF16 tail %d, batch 1" % (args.ctx, args.fmt, args.tail),
+                   "layers": L, "kv_heads": H, "q_heads": QH, "ctx": args.ctx, "fmt": args.fmt,
+                   "tail": args.tail, "batch": 1},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_ms_per_step": round(dec_ms, 4),
+        "append_tokens_per_s": round(app_tps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_decode<%s>" % args.fmt, "bytes_per_launch": int(launch_bytes),
+                     "launch_us": round(launch_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
