@@ -18,10 +18,23 @@
 // once, quantized values are accumulated in the rotated domain, and the merged quantized
 // accumulator is rotated back once at the end; ring tokens stay in the original domain.
 #include <float.h>
+#include <stdlib.h>
 
 #include "kvq_device.h"
 
 namespace kvq {
+
+// KVQ_DECODE_GENERIC=1 selects the generic kernel for every format (the fast 4-bit
+// kernel is otherwise used where it applies); read once per process.
+bool decode_generic_forced()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("KVQ_DECODE_GENERIC");
+        v = (e && e[0] == '1') ? 1 : 0;
+    }
+    return v == 1;
+}
 
 namespace {
 
@@ -373,6 +386,8 @@ int occ_fmt()
 
 int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
 {
+    if (decode_fast_supported(a.g.fmt_k, a.g.fmt_v) && !decode_generic_forced())
+        return launch_decode_fast(a, n_wgs, stream);
     hipStream_t st = (hipStream_t)stream;
     switch (a.g.fmt_k) {
     case 0: return launch_fmt<0>(a, n_wgs, st);
@@ -400,8 +415,8 @@ int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
 
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
 {
-    (void)fmt_v;
     (void)group;
+    if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k);
     static int cache[19] = {0};
     if (fmt_k < 0 || fmt_k >= 19) return 0;
     if (cache[fmt_k]) return cache[fmt_k];

@@ -108,6 +108,11 @@ int launch_append_kvarn(const AppendArgs& a, void* stream);    // KVarN pages
 int launch_append_ring(const AppendArgs& a, void* stream);     // BF16 ring writes
 int launch_decode(const DecodeArgs& a, int n_wgs, void* stream);
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of the decode kernel
+// 4-bit fast path (kvq_decode_fast.hip), used by launch_decode when it applies.
+bool decode_fast_supported(int fmt_k, int fmt_v);
+int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream);
+int decode_fast_wgs_per_cu(int fmt);
+bool decode_generic_forced();
 int device_cu_count();
 
 }  // namespace kvq
