@@ -119,8 +119,9 @@ int kv_append(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq
               void* stream);
 
 /* Bytes of decode workspace needed by kv_decode_attn for up to n_seqs sequences at any
- * length up to max_tokens.  The workspace must be zero-filled once before its first use;
- * every completed kv_decode_attn call leaves it in that reusable state. */
+ * length up to max_tokens.  The workspace holds the per-workgroup partial results of one
+ * call; it needs no initialization, and calls that share one workspace must be ordered on
+ * one stream (or synchronized). */
 int64_t kv_decode_workspace_bytes(const kv_cache* cache, int32_t n_seqs);
 
 /* Single-token decode attention for `layer` over sequences seq_ids[0..n_seqs).

@@ -24,7 +24,8 @@ UNITS = [
     ("kvq_host.cpp", ["-ffp-contract=off"]),
     ("kvq_append.hip", ["-ffp-contract=off"]),
     ("kvq_decode.hip", []),
-    ("kvq_decode_fast.hip", []),
+    ("kvq_decode_ws.hip", []),
+    ("kvq_merge.hip", []),
     ("kvq_debug.hip", ["-ffp-contract=off"]),
 ]
 

@@ -10,8 +10,8 @@
 // units (128-token quantized pages, 32-token ring chunks); every workgroup owns a run of
 // units of one kind, sized so the whole grid is resident at once.  Each wave keeps an
 // online softmax (running max m, sum l, accumulator acc) per token slot; slots and waves
-// merge through shuffles and LDS; the last workgroup of a (sequence, KV head) to finish
-// (device-scope counter) merges all partials and writes the output.
+// merge through shuffles and LDS into one partial result per workgroup, and a second
+// launch (kvq_merge.hip) merges the partials of each (sequence, KV head).
 //
 // KVarN: keys and values are stored rotated, x = H Yhat / 128 with H the unnormalized
 // Sylvester Hadamard matrix (symmetric).  So q.x = (H q / 128) . Yhat: the query is rotated
@@ -191,7 +191,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
     __shared__ float qs[kG][kD];
     __shared__ float wm[4][kG], wl[4][kG];
     __shared__ float wacc[4][kG][kD];
-    __shared__ int last_flag;
 
     const int tid = threadIdx.x;
     const int bid = blockIdx.x;
@@ -315,56 +314,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
         part_out[2 * kMaxGroup + h * kD + d] = A;
         if (d == 0) { part_out[h] = M; part_out[kMaxGroup + h] = L; }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t* ctr = a.counters + sq.in_idx * g.n_kv_heads + head;
-        uint32_t old = atomicAdd(ctr, 1u);
-        int last = (old == (uint32_t)(S - 1));
-        if (last) *ctr = 0u;                 // leave the workspace reusable
-        last_flag = last;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-
-    // ---- last workgroup of this (sequence, KV head): merge all splits -------------------------
-    const int first = sq.wg_base + head * S;
-    float (*oq)[kD] = wacc[0];               // reuse LDS: quantized-domain sums
-    float (*ot)[kD] = wacc[1];               // ring-domain sums
-    float (*Ls)[kG] = wl;                    // reuse: total sum per head in wl[0]
-    for (int i = tid; i < kG * kD; i += blockDim.x) {
-        const int h = i / kD, d = i % kD;
-        float M = kNegBig;
-        for (int s = 0; s < S; ++s) {
-            const float* pp = a.partials + (int64_t)(first + s) * kPartialFloats;
-            M = fmaxf(M, __hip_atomic_load(pp + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        }
-        float L = 0.0f, Aq = 0.0f, At = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            const float* pp = a.partials + (int64_t)(first + s) * kPartialFloats;
-            float m = __hip_atomic_load(pp + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float l = __hip_atomic_load(pp + kMaxGroup + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float ac = __hip_atomic_load(pp + 2 * kMaxGroup + h * kD + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            float ew = __builtin_amdgcn_exp2f(m - M);
-            L += l * ew;
-            if (s < sq.splits_q) Aq += ac * ew; else At += ac * ew;
-        }
-        oq[h][d] = Aq;
-        ot[h][d] = At;
-        if (d == 0) Ls[0][h] = L;
-    }
-    __syncthreads();
-    if constexpr (KIND == KIND_KVARN) {
-        lds_fwht(oq);
-    }
-    for (int i = tid; i < kG * kD; i += blockDim.x) {
-        const int h = i / kD, d = i % kD;
-        float vq = oq[h][d];
-        if constexpr (KIND == KIND_KVARN) vq *= (1.0f / 128.0f);
-        float res = (vq + ot[h][d]) / Ls[0][h];
-        a.out[((int64_t)sq.in_idx * g.n_q_heads + head * kG + h) * kD + d] = res;
-    }
 }
 
 template <int FMT>
@@ -385,6 +334,12 @@ int occ_fmt()
 }  // namespace
 
 int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
+{
+    int rc = launch_decode_split(a, n_wgs, stream);
+    return rc ? rc : launch_merge(a, stream);
+}
+
+int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)
 {
     if (decode_fast_supported(a.g.fmt_k, a.g.fmt_v) && !decode_generic_forced())
         return launch_decode_fast(a, n_wgs, stream);

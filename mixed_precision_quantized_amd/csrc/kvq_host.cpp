@@ -344,9 +344,7 @@ int kv_spill_tail(kv_cache* c, int32_t layer, int32_t seq_id, int32_t keep_token
 int64_t kv_decode_workspace_bytes(const kv_cache* c, int32_t n_seqs)
 {
     if (!c || n_seqs < 1 || n_seqs > c->cfg.n_seqs) return KV_EINVAL;
-    int64_t part = (int64_t)kMaxDecodeWGs * kPartialFloats * 4;
-    int64_t cnt = (int64_t)kMaxSeqsPerLaunch * c->cfg.n_kv_heads * 4;
-    return align256(part) + align256(cnt);
+    return align256((int64_t)kMaxDecodeWGs * kPartialFloats * 4);
 }
 
 int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
@@ -374,7 +372,6 @@ int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* se
     a.q = q;
     a.out = out;
     a.partials = (float*)workspace;
-    a.counters = (uint32_t*)((char*)workspace + align256((int64_t)kMaxDecodeWGs * kPartialFloats * 4));
 
     const int H = c->cfg.n_kv_heads;
     int64_t total_units = 0;

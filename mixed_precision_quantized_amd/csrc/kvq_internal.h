@@ -94,7 +94,6 @@ struct DecodeArgs {
     const void* q;        // [n_seqs][n_q_heads][128]
     float* out;           // [n_seqs][n_q_heads][128]
     float* partials;      // [max_wgs][kPartialFloats]
-    uint32_t* counters;   // [n_seqs * n_kv_heads]
     DecodeSeq seqs[kMaxSeqsPerLaunch];
 };
 
@@ -106,9 +105,11 @@ constexpr int kMaxDecodeWGs = 8192;
 int launch_append_encode(const AppendArgs& a, void* stream);   // qN / bf16 streams
 int launch_append_kvarn(const AppendArgs& a, void* stream);    // KVarN pages
 int launch_append_ring(const AppendArgs& a, void* stream);     // BF16 ring writes
-int launch_decode(const DecodeArgs& a, int n_wgs, void* stream);
+int launch_decode(const DecodeArgs& a, int n_wgs, void* stream);        // split kernel + merge
+int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream);  // partials only
+int launch_merge(const DecodeArgs& a, void* stream);                    // kvq_merge.hip
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of the decode kernel
-// 4-bit fast path (kvq_decode_fast.hip), used by launch_decode when it applies.
+// 4-bit fast path (kvq_decode_ws.hip), used by launch_decode when it applies.
 bool decode_fast_supported(int fmt_k, int fmt_v);
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream);
 int decode_fast_wgs_per_cu(int fmt);

@@ -145,7 +145,7 @@ class Cache:
                                    nbytes, ctypes.byref(h)), "kv_cache_init")
         self.h = h
         ws = int(lib().kv_decode_workspace_bytes(self.h, n_seqs))
-        self.ws = torch.zeros(ws, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=device)
 
     def __del__(self):
         try:
