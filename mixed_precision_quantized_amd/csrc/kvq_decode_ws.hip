@@ -46,6 +46,7 @@ constexpr int kStages = 3;               // LDS ring depth per wave
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ const char* sptr(const CacheGeom& g, int seq, int layer, int head, int isv)
 {
@@ -60,6 +61,8 @@ __device__ __forceinline__ float dpp(float x)
 }
 constexpr int QP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int QP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int ROW_ROR1 = 0x121;     // row_ror:1
+constexpr int ROW_ROR2 = 0x122;     // row_ror:2
 constexpr int ROW_ROR4 = 0x124;     // row_ror:4
 constexpr int ROW_ROR8 = 0x128;     // row_ror:8
 constexpr int ROW_HMIRROR = 0x141;  // row_half_mirror
@@ -150,38 +153,42 @@ struct alignas(16) Stage {
 };
 
 struct alignas(16) PBuf {
-    float p[16][4][2];       // [pair slot][head][token] probabilities of the step
+    float p[16][2][4];       // [pair slot][token of the pair][head] probabilities of the step
     float alpha[4];          // accumulator rescale of the step (running max grew)
     float pad[4];
 };
 
-struct alignas(16) QDig {
-    uint32_t d[4][4][4][4];  // [block kb][slot r][digit k][dword i] of head kb^r
-    float S[4][4];           // [kb][r] fixed-point scale
-    float qsum[4][4];        // [kb][r] block sum of the query (affine format)
+// Query operand of the score MFMA for one pair: 16-bit fixed-point query per (head, 32-dim
+// block) split into a low and a high signed byte, q_int = 256 hi + lo, the dims of every
+// 8-dim group stored even dims first (the order in which the code nibbles unpack).
+struct alignas(16) QMat {
+    int8_t qa[2][kG][kD];    // [byte: lo, hi][head][permuted dim]
+    float S[kG][4];          // [head][block] scale of q_int
+    int off[kG][4];          // [head][block] 8 * sum of q_int (symmetric formats)
+    float qsum[kG][4];       // [head][block] sum of the query (affine formats)
 };
 
 struct alignas(16) WsLds {
     float qs[kG][kD];
-    Stage st[4][kStages];
+    Stage st[2][kStages];    // LDS rings of the two value waves
     PBuf pb[2][2];
-    QDig qd[2];
+    QMat qm[2];
     float wm[2][kG], wl[2][kG];
+    float wacc[2][kG][kD];   // slot-summed value accumulators of the pairs
 };
 
-// Fixed-point digits of the query (one page or the whole split).  Lane = head h
-// (lane >> 4) x 8-dim group g8 (lane & 15).  c: the page's key channel scales or null.
+// Fixed-point query operand (one page or the whole split).  Lane = head h (lane >> 4) x
+// 8-dim group g8 (lane & 15).  cw: the 8 key channel scales of the group (KVarN) or null.
 template <bool AFFINE>
-__device__ __forceinline__ void build_qdigits(QDig& Q, const float (*src)[kD], const uint16_t* c, int lane)
+__device__ __forceinline__ void build_qmat(QMat& Q, const float (*src)[kD], const uint4* cw, int lane)
 {
-    const int h = lane >> 4, g8 = lane & 15, kb = g8 >> 2, i = g8 & 3;
+    const int h = lane >> 4, g8 = lane & 15, kb = g8 >> 2;
     float v[8];
-    uint4 cw = c ? *(const uint4*)(c + 8 * g8) : make_uint4(0, 0, 0, 0);
-    uint32_t cc[4] = {cw.x, cw.y, cw.z, cw.w};
+    const uint32_t cc[4] = {cw ? cw->x : 0u, cw ? cw->y : 0u, cw ? cw->z : 0u, cw ? cw->w : 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float q = src[h][8 * g8 + e];
-        if (c) q *= fp16_to_f32((cc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        if (cw) q *= fp16_to_f32((cc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
         v[e] = q;
     }
     float amax = 0.0f, sum = 0.0f;
@@ -194,24 +201,26 @@ __device__ __forceinline__ void build_qdigits(QDig& Q, const float (*src)[kD], c
         sum += dpp<QP_XOR2>(sum);
     }
     const float inv = amax > 0.0f ? kQLim * __builtin_amdgcn_rcpf(amax) : 0.0f;
-    uint32_t d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+    int isum = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        int qi = (int)__builtin_rintf(fminf(fmaxf(v[e] * inv, -kQLim), kQLim)) + kQBias;
-        d0 |= (((uint32_t)qi & 15u) ^ 8u) << (4 * e);
-        d1 |= ((((uint32_t)qi >> 4) & 15u) ^ 8u) << (4 * e);
-        d2 |= ((((uint32_t)qi >> 8) & 15u) ^ 8u) << (4 * e);
-        d3 |= ((((uint32_t)qi >> 12) & 15u) ^ 8u) << (4 * e);
+        const int qi = (int)__builtin_rintf(fminf(fmaxf(v[e] * inv, -kQLim), kQLim));
+        const int l8 = ((qi + 128) & 255) - 128;       // signed low byte
+        const int h8 = (qi - l8) >> 8;                 // signed high byte
+        const int pos = (e & 1) * 4 + (e >> 1);        // even dims first
+        lo[pos >> 2] |= ((uint32_t)l8 & 255u) << (8 * (pos & 3));
+        hi[pos >> 2] |= ((uint32_t)h8 & 255u) << (8 * (pos & 3));
+        isum += qi;
     }
-    const int r = h ^ kb;
-    Q.d[kb][r][0][i] = d0;
-    Q.d[kb][r][1][i] = d1;
-    Q.d[kb][r][2][i] = d2;
-    Q.d[kb][r][3][i] = d3;
-    if (i == 0) {
-        // dequantization scale of the digits: q ~ q_int * S
-        Q.S[kb][r] = inv > 0.0f ? 1.0f / inv : 0.0f;
-        Q.qsum[kb][r] = sum;
+    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR1, 0xF, 0xF, false);
+    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR2, 0xF, 0xF, false);
+    *(uint2*)&Q.qa[0][h][8 * g8] = make_uint2(lo[0], lo[1]);
+    *(uint2*)&Q.qa[1][h][8 * g8] = make_uint2(hi[0], hi[1]);
+    if ((g8 & 3) == 0) {
+        Q.S[h][kb] = inv > 0.0f ? 1.0f / inv : 0.0f;
+        Q.off[h][kb] = 8 * isum;
+        Q.qsum[h][kb] = sum;
     }
 }
 
@@ -242,15 +251,16 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     constexpr int SB = AFF ? 16 : 8;                  // scale bytes per token row
     constexpr int kLoads = 3 + (KVARN ? 1 : 0);      // load instructions per stage
     static_assert(fbits(FMT) == 4, "4-bit formats only");
-    static_assert(sizeof(Stage) * kStages >= 2 * 2 * kG * kD * sizeof(float), "merge scratch fits one wave ring");
 
     __shared__ WsLds S;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pr = wave & 1;                          // pair
-    const bool kwave = wave < 2;
     const int bid = blockIdx.x;
+    const int pr = wave & 1;                          // pair
+    // score waves are 0,1 in even workgroups and 2,3 in odd ones, so that every SIMD runs both
+    // roles (wave w of a workgroup runs on SIMD w)
+    const bool kwave = ((wave >> 1) ^ (bid & 1)) == 0;
     int e = 0;
     for (int i = 1; i < a.n_seqs; ++i)
         if (a.seqs[i].wg_base <= bid) e = i;
@@ -293,33 +303,214 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     const int Jmax = max(steps_of(0), steps_of(1));
     const int u_first = u_lo + pr;
 
-    const int kg = lane >> 2, kb = lane & 3;          // K layout: pair slot, block
     const int vg = lane >> 3, vp = lane & 7;          // V layout: pair slot (of 8), 16-dim part
     const int vb = vp >> 1;
 
     // end of a role: the K wave leaves (m, l) per head, the V wave its slot-summed accumulator
-    auto finish_k = [&](float mv, float lsum, bool quant_layout) {
-        const float t = quant_layout ? wave_sum16(lsum) : wave_sum8(vp < kG ? lsum : 0.0f);
-        if (lane < kG) {                 // lane h holds head h in both layouts
+    // end of a ring role: the K wave leaves (m, l) per head, the V wave its slot-summed
+    // accumulator (lane h < 4 of the K wave holds head h)
+    auto finish_k = [&](float mv, float lsum) {
+        const float t = wave_sum8(vp < kG ? lsum : 0.0f);
+        if (lane < kG) {
             S.wl[pr][lane] = t;
             S.wm[pr][lane] = mv;
         }
     };
     auto finish_v = [&](float (&acc)[kG][16]) {
-        float (*wacc)[kD] = reinterpret_cast<float (*)[kD]>(&S.st[wave][0]);
 #pragma unroll
         for (int h = 0; h < kG; ++h)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const float y = wave_sum8(acc[h][jj]);
-                if (vg == 0) wacc[h][16 * vp + jj] = y;
+                if (vg == 0) S.wacc[pr][h][16 * vp + jj] = y;
             }
     };
-    if (quant) {
-        const char* cbase = kwave ? kst + g.k.codes : vst + g.v.codes;
-        const char* sbase = kwave ? kst + g.k.scales : vst + g.v.scales;
-        const char* chbase = kwave ? kst + g.k.cscale : vst + g.v.cscale;
-        Stage* ring = S.st[wave];
+    if (quant && kwave) {
+        // ============================ K wave (MFMA scores) ============================
+        // One v_mfma_i32_16x16x64_i8 per (16-token tile, block pair): rows = (block of the
+        // pair, head, byte of q_int), columns = tokens, K = the 64 dims of the two blocks (a
+        // row is zero over the other block's dims).  Lane (n = lane & 15, q = lane >> 4)
+        // supplies the codes of token n, dims 16q..16q+15 of the pair, and receives the four
+        // rows 4q..4q+3: block 2bp + (q >> 1), heads 2(q & 1) and 2(q & 1) + 1, both bytes.
+        const int n16 = lane & 15, q4 = lane >> 4;
+        const int hp = q4 & 1, bsel = q4 >> 1;
+        const char* kcodes = kst + g.k.codes;
+        const char* kscales = kst + g.k.scales;
+        const char* kchan = kst + g.k.cscale;
+        QMat& Q = S.qm[pr];
+        i32x4 A[2];
+        float Sc[2][2], Qs[2][2];
+        int Of[2][2];
+        auto load_a = [&]() {
+            const int m = n16, dig = m & 1, h = (m >> 1) & 3, sel = m >> 3;
+#pragma unroll
+            for (int bp = 0; bp < 2; ++bp) {
+                const int b = 2 * bp + sel;
+                const i32x4 z = {0, 0, 0, 0};
+                A[bp] = sel == bsel ? *(const i32x4*)&Q.qa[dig][h][32 * b + 16 * (q4 & 1)] : z;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int hq = 2 * hp + hh, bq = 2 * bp + bsel;
+                    Sc[bp][hh] = Q.S[hq][bq];
+                    Of[bp][hh] = AFF ? 0 : Q.off[hq][bq];
+                    Qs[bp][hh] = AFF ? Q.qsum[hq][bq] : 0.0f;
+                }
+            }
+        };
+        // codes and scales of one step, straight to registers (tokens clamped to the page)
+        struct KLoad { uint2 c[2][2]; uint4 s[2]; };
+        auto kload = [&](int j, KLoad& L) {
+            const int jj = j < J ? j : J - 1;
+            const int u = u_first + 2 * (jj >> 2);
+            const int64_t tp = (int64_t)u * kPage;
+            const int64_t te = min<int64_t>(tp + kPage, sq.n_q);
+            const int64_t tb = tp + 32 * (jj & 3);
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                const int64_t t = min<int64_t>(tb + 16 * T + n16, te - 1);
+#pragma unroll
+                for (int bp = 0; bp < 2; ++bp) L.c[T][bp] = *(const uint2*)(kcodes + t * 64 + 32 * bp + 8 * q4);
+                if (AFF) {
+                    L.s[T] = *(const uint4*)(kscales + t * 16);
+                } else {
+                    const uint2 w = *(const uint2*)(kscales + t * 8);
+                    L.s[T] = make_uint4(w.x, w.y, 0u, 0u);
+                }
+            }
+        };
+        auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
+            const int nu = (u_hi - u_first + 1) / 2;
+            const int u = u_first + 2 * min(i, nu - 1);
+            return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
+        };
+        float mh0 = kNeg, mh1 = kNeg;              // running max of heads 2hp, 2hp + 1
+        float ls0 = 0.0f, ls1 = 0.0f;              // sums of p over the lane's tokens
+        uint4 cnext = make_uint4(0u, 0u, 0u, 0u);
+        if (!KVARN) {
+            build_qmat<AFF>(Q, S.qs, nullptr, lane);
+            wave_sync_lds();
+            load_a();
+        } else if (J > 0) {
+            cnext = chan_load(0);
+        }
+        auto kstep = [&](int j, const KLoad& L) __attribute__((always_inline)) {
+            const int u = u_first + 2 * (j >> 2);
+            const int64_t t_page = (int64_t)u * kPage;
+            const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
+            if (KVARN && (j & 3) == 0) {
+                const uint4 cw = cnext;
+                cnext = chan_load((j >> 2) + 1);
+                wave_sync_lds();
+                build_qmat<false>(Q, S.qs, &cw, lane);
+                wave_sync_lds();
+                load_a();
+            }
+            float sc[2][2];
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                for (int bp = 0; bp < 2; ++bp) {
+                    const uint2 x = L.c[T][bp];
+                    const i32x4 Bm = {(int)(x.x & 0x0F0F0F0Fu), (int)((x.x >> 4) & 0x0F0F0F0Fu),
+                                      (int)(x.y & 0x0F0F0F0Fu), (int)((x.y >> 4) & 0x0F0F0F0Fu)};
+                    const i32x4 z = {0, 0, 0, 0};
+                    const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, z, 0, 0, 0);
+                    const int b = 2 * bp + bsel;
+                    float d, mm = 0.0f;
+                    if (AFF) {
+                        const uint32_t w = (b & 2) ? (bsel ? L.s[T].w : L.s[T].z) : (bsel ? L.s[T].y : L.s[T].x);
+                        d = fp16_to_f32(w & 0xFFFFu);
+                        mm = fp16_to_f32(w >> 16);
+                    } else {
+                        const uint32_t w = bp ? L.s[T].y : L.s[T].x;
+                        d = fp16_to_f32((w >> (16 * bsel)) & 0xFFFFu);
+                    }
+                    const int t0 = (C.y << 8) + C.x - Of[bp][0];
+                    const int t1 = (C.w << 8) + C.z - Of[bp][1];
+                    a0 = fmaf((float)t0, Sc[bp][0] * d, a0);
+                    a1 = fmaf((float)t1, Sc[bp][1] * d, a1);
+                    if (AFF) {
+                        a0 = fmaf(mm, Qs[bp][0], a0);
+                        a1 = fmaf(mm, Qs[bp][1], a1);
+                    }
+                }
+                // the other two blocks are in lane ^ 32
+                const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a0), false, false);
+                const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a1), false, false);
+                const bool valid = t_page + 32 * (j & 3) + 16 * T + n16 < t_end;
+                sc[T][0] = valid ? __uint_as_float(r0[0]) + __uint_as_float(r0[1]) : kNeg;
+                sc[T][1] = valid ? __uint_as_float(r1[0]) + __uint_as_float(r1[1]) : kNeg;
+            }
+            // running max per head over the 16 lanes of the row
+            float x0 = fmaxf(sc[0][0], sc[1][0]), x1 = fmaxf(sc[0][1], sc[1][1]);
+            x0 = fmaxf(x0, dpp<ROW_ROR8>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR8>(x1));
+            x0 = fmaxf(x0, dpp<ROW_ROR4>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR4>(x1));
+            x0 = fmaxf(x0, dpp<ROW_ROR2>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR2>(x1));
+            x0 = fmaxf(x0, dpp<ROW_ROR1>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR1>(x1));
+            const float n0 = fmaxf(mh0, x0), n1 = fmaxf(mh1, x1);
+            const float al0 = __builtin_amdgcn_exp2f(mh0 - n0);     // exactly 1 if unchanged
+            const float al1 = __builtin_amdgcn_exp2f(mh1 - n1);
+            mh0 = n0;
+            mh1 = n1;
+            float p[2][2];
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+                p[T][0] = __builtin_amdgcn_exp2f(sc[T][0] - n0);
+                p[T][1] = __builtin_amdgcn_exp2f(sc[T][1] - n1);
+            }
+            ls0 = fmaf(ls0, al0, p[0][0] + p[1][0]);
+            ls1 = fmaf(ls1, al1, p[0][1] + p[1][1]);
+            PBuf& P = S.pb[pr][j & 1];
+            if (q4 < 2) {
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    const int t = 16 * T + n16;
+                    *(float2*)&P.p[t >> 1][t & 1][2 * hp] = make_float2(p[T][0], p[T][1]);
+                }
+            }
+            if (n16 == 0 && q4 < 2) *(float2*)&P.alpha[2 * hp] = make_float2(al0, al1);
+            __syncthreads();
+        };
+        // three register stages, loads issued two steps ahead of their use
+        KLoad X, Y, Z;
+        if (J > 0) {
+            kload(0, X);
+            kload(1, Y);
+            kload(2, Z);
+        }
+        int j = 0;
+#pragma unroll 1
+        for (; j + 2 < J; j += 3) {
+            kstep(j, X);
+            kload(j + 3, X);
+            kstep(j + 1, Y);
+            kload(j + 4, Y);
+            kstep(j + 2, Z);
+            kload(j + 5, Z);
+        }
+        if (j < J) { kstep(j, X); ++j; }
+        if (j < J) { kstep(j, Y); ++j; }
+#pragma unroll 1
+        for (; j <= Jmax; ++j) __syncthreads();
+        // normalizers over the row; lanes 0 and 16 hold heads (0, 1) and (2, 3)
+        float l0 = ls0, l1 = ls1;
+        l0 += dpp<ROW_ROR8>(l0); l1 += dpp<ROW_ROR8>(l1);
+        l0 += dpp<ROW_ROR4>(l0); l1 += dpp<ROW_ROR4>(l1);
+        l0 += dpp<ROW_ROR2>(l0); l1 += dpp<ROW_ROR2>(l1);
+        l0 += dpp<ROW_ROR1>(l0); l1 += dpp<ROW_ROR1>(l1);
+        if (n16 == 0 && q4 < 2) {
+            S.wl[pr][2 * hp] = l0;
+            S.wl[pr][2 * hp + 1] = l1;
+            S.wm[pr][2 * hp] = mh0;
+            S.wm[pr][2 * hp + 1] = mh1;
+        }
+    } else if (quant) {
+        // ================================ V wave ================================
+        const char* cbase = vst + g.v.codes;
+        const char* sbase = vst + g.v.scales;
+        const char* chbase = vst + g.v.cscale;
+        Stage* ring = S.st[pr];
         // stage j -> ring slot j % kStages; the number of load instructions per stage is
         // fixed (stages past the end repeat the last), so one vmcnt value covers a stage.
         auto issue = [&](int j) {
@@ -348,241 +539,125 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             issue(0);
             issue(1);
         }
-        if (kwave) {
-            // ================================ K wave ================================
-            float mh = kNeg;                           // running max of the lane's head kb
-            float lsum = 0.0f;                         // sum of p of the lane's head
-            QDig& Q = S.qd[pr];
-            uint32_t qd[4][4][4];
-            float qS[4], qsm[4];
-            auto load_digits = [&]() {
+        float acc[kG][16], wsum[kG], msum[kG], cv[16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+        for (int h = 0; h < kG; ++h) {
+            wsum[h] = 0.0f;
+            msum[h] = 0.0f;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        uint4 w4 = *(const uint4*)&Q.d[kb][r][k][0];
-                        qd[r][k][0] = w4.x; qd[r][k][1] = w4.y; qd[r][k][2] = w4.z; qd[r][k][3] = w4.w;
-                    }
-                    qS[r] = Q.S[kb][r];
-                    qsm[r] = Q.qsum[kb][r];
+            for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) cv[jj] = 1.0f;
+        auto vstep = [&](int j, bool page_start) __attribute__((always_inline)) {
+            issue(j + 2);
+            wait_vmcnt<2 * kLoads>();
+            asm volatile("" ::: "memory");
+            const Stage& B = ring[j % kStages];
+            const PBuf& P = S.pb[pr][j & 1];
+            const float4 al = *(const float4*)P.alpha;
+            if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
+                const float alv[kG] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+                for (int h = 0; h < kG; ++h) {
+                    wsum[h] *= alv[h];
+                    msum[h] *= alv[h];
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
                 }
-            };
-            if (!KVARN) {
-                build_qdigits<AFF>(Q, S.qs, nullptr, lane);
-                wave_sync_lds();
-                load_digits();
             }
-            // one 32-token step of the scores; `page_start`: the step opens a page
-            auto kstep = [&](int j, int64_t t_page, int64_t t_end, bool page_start) __attribute__((always_inline)) {
-                issue(j + 2);
-                wait_vmcnt<2 * kLoads>();
-                asm volatile("" ::: "memory");
-                const Stage& B = ring[j % kStages];
-                if (KVARN && page_start) {
-                    wave_sync_lds();
-                    build_qdigits<false>(Q, S.qs, B.chan, lane);
-                    wave_sync_lds();
-                    load_digits();
-                }
-                const int64_t t0 = t_page + 32 * (j & 3) + 2 * kg;
-                const bool v0 = t0 < t_end, v1 = t0 + 1 < t_end;
-                const uint4 kc0 = *(const uint4*)(B.codes + 16 * lane);
-                const uint4 kc1 = *(const uint4*)(B.codes + 1024 + 16 * lane);
-                float kd0, kd1, km0 = 0.0f, km1 = 0.0f;
-                if (AFF) {
-                    uint32_t s0 = ((const uint32_t*)B.scales)[8 * kg + kb];
-                    uint32_t s1 = ((const uint32_t*)B.scales)[8 * kg + 4 + kb];
-                    kd0 = fp16_to_f32(s0 & 0xFFFFu); kd1 = fp16_to_f32(s1 & 0xFFFFu);
-                    km0 = fp16_to_f32(s0 >> 16); km1 = fp16_to_f32(s1 >> 16);
-                } else {
-                    kd0 = fp16_to_f32(((const uint16_t*)B.scales)[8 * kg + kb]);
-                    kd1 = fp16_to_f32(((const uint16_t*)B.scales)[8 * kg + 4 + kb]);
-                }
-                const uint32_t c0[4] = {kc0.x ^ 0x88888888u, kc0.y ^ 0x88888888u, kc0.z ^ 0x88888888u, kc0.w ^ 0x88888888u};
-                const uint32_t c1[4] = {kc1.x ^ 0x88888888u, kc1.y ^ 0x88888888u, kc1.z ^ 0x88888888u, kc1.w ^ 0x88888888u};
-                float ps0[4], ps1[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int a0[4], a1[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        int x = 0, y = 0;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            x = __builtin_amdgcn_sdot8((int)c0[i], (int)qd[r][k][i], x, false);
-                            y = __builtin_amdgcn_sdot8((int)c1[i], (int)qd[r][k][i], y, false);
-                        }
-                        a0[k] = x;
-                        a1[k] = y;
-                    }
-                    const int t0i = a0[0] + (a0[1] << 4) + (a0[2] << 8) + (a0[3] << 12);
-                    const int t1i = a1[0] + (a1[1] << 4) + (a1[2] << 8) + (a1[3] << 12);
-                    ps0[r] = (float)t0i * (qS[r] * kd0);
-                    ps1[r] = (float)t1i * (qS[r] * kd1);
-                    if (AFF) {
-                        ps0[r] = fmaf(km0 + 8.0f * kd0, qsm[r], ps0[r]);
-                        ps1[r] = fmaf(km1 + 8.0f * kd1, qsm[r], ps1[r]);
-                    }
-                }
-                // reduce-scatter over the quad: lane kb ends with head kb
-                const float k00 = ps0[0] + dpp<QP_XOR2>(ps0[2]);
-                const float k01 = ps0[1] + dpp<QP_XOR2>(ps0[3]);
-                const float k10 = ps1[0] + dpp<QP_XOR2>(ps1[2]);
-                const float k11 = ps1[1] + dpp<QP_XOR2>(ps1[3]);
-                float s0 = k00 + dpp<QP_XOR1>(k01);
-                float s1 = k10 + dpp<QP_XOR1>(k11);
-                s0 = v0 ? s0 : kNeg;
-                s1 = v1 ? s1 : kNeg;
-                // lanes with equal kb hold the same head: the new max needs no exchange
-                const float nm = fmaxf(mh, wave_max16(fmaxf(s0, s1)));
-                const float al = __builtin_amdgcn_exp2f(mh - nm);    // exactly 1 if unchanged
-                mh = nm;
-                lsum *= al;
-                const float p0 = v0 ? __builtin_amdgcn_exp2f(s0 - mh) : 0.0f;
-                const float p1 = v1 ? __builtin_amdgcn_exp2f(s1 - mh) : 0.0f;
-                lsum += p0 + p1;
-                PBuf& P = S.pb[pr][j & 1];
-                *(float2*)&P.p[kg][kb][0] = make_float2(p0, p1);
-                if (lane < kG) P.alpha[lane] = al;
-                __syncthreads();
-            };
-            // J work steps, page by page, then idle barriers up to the workgroup's Jmax + 1
-            int j = 0;
-#pragma unroll 1
-            for (int u = u_first; u < u_hi; u += 2) {
-                const int64_t t_page = (int64_t)u * kPage;
-                const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
-                const int ns = (int)((t_end - t_page + 31) / 32);
-                kstep(j, t_page, t_end, true);
-                ++j;
-#pragma unroll 1
-                for (int js = 1; js < ns; ++js, ++j) kstep(j, t_page, t_end, false);
-            }
-#pragma unroll 1
-            for (; j <= Jmax; ++j) __syncthreads();
-            finish_k(mh, lsum, true);
-        } else {
-            // ================================ V wave ================================
-            float acc[kG][16], wsum[kG], msum[kG], cv[16];
-#pragma unroll
-            for (int h = 0; h < kG; ++h) {
-                wsum[h] = 0.0f;
-                msum[h] = 0.0f;
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
-            }
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) cv[jj] = 1.0f;
-            auto vstep = [&](int j, bool page_start) __attribute__((always_inline)) {
-                issue(j + 2);
-                wait_vmcnt<2 * kLoads>();
-                asm volatile("" ::: "memory");
-                const Stage& B = ring[j % kStages];
-                const PBuf& P = S.pb[pr][j & 1];
-                const float4 al = *(const float4*)P.alpha;
-                if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
-                    const float alv[kG] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) {
-                        wsum[h] *= alv[h];
-                        msum[h] *= alv[h];
-#pragma unroll
-                        for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
-                    }
-                }
-                if (KVARN && page_start) {
-                    // this page's value channel scales: rescale the accumulator to them (the
-                    // accumulator is zero before the first page, so the first rescale is inert)
-                    const uint4 c0 = *(const uint4*)(B.chan + 16 * vp);
-                    const uint4 c1 = *(const uint4*)(B.chan + 16 * vp + 8);
-                    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-                    for (int jj = 0; jj < 16; ++jj) {
-                        const float cn = fp16_to_f32((cw[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu);
-                        const float r = cv[jj] * __builtin_amdgcn_rcpf(cn);
-#pragma unroll
-                        for (int h = 0; h < kG; ++h) acc[h][jj] = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * r;
-                        cv[jj] = cn;
-                    }
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) wsum[h] = 0.0f;
-                }
-#pragma unroll 1
-                for (int half = 0; half < 2; ++half) {
-                    const int slot = vg + 8 * half;
-                    const uint2 a0 = *(const uint2*)(B.codes + 64 * slot + 8 * vp);
-                    const uint2 a1 = *(const uint2*)(B.codes + 1024 + 64 * slot + 8 * vp);
-                    uint32_t sv0, sv1;
-                    if (AFF) {
-                        sv0 = ((const uint32_t*)B.scales)[8 * slot + vb];
-                        sv1 = ((const uint32_t*)B.scales)[8 * slot + 4 + vb];
-                    } else {
-                        sv0 = ((const uint16_t*)B.scales)[8 * slot + vb];
-                        sv1 = ((const uint16_t*)B.scales)[8 * slot + 4 + vb];
-                    }
-                    const float vd0 = fp16_to_f32(sv0 & 0xFFFFu), vd1 = fp16_to_f32(sv1 & 0xFFFFu);
-                    const float4 pa = *(const float4*)&P.p[slot][0][0];
-                    const float4 pb = *(const float4*)&P.p[slot][2][0];
-                    const float pp[4][2] = {{pa.x, pa.y}, {pa.z, pa.w}, {pb.x, pb.y}, {pb.z, pb.w}};
-                    uint32_t wp[kG];
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) {
-                        wp[h] = pack_h2(pp[h][0] * vd0, pp[h][1] * vd1);
-                        wsum[h] = fdot2(wp[h], 0x3C003C00u, wsum[h]);
-                        if (AFF) {
-                            const float mv0 = fp16_to_f32(sv0 >> 16), mv1 = fp16_to_f32(sv1 >> 16);
-                            msum[h] = fmaf(pp[h][0], mv0 + 8.0f * vd0, fmaf(pp[h][1], mv1 + 8.0f * vd1, msum[h]));
-                        }
-                    }
-                    const uint32_t xw[2] = {a0.x, a0.y}, yw[2] = {a1.x, a1.y};
-#pragma unroll
-                    for (int wdx = 0; wdx < 2; ++wdx) {
-                        // (t0 dims 0-3 | t1 dims 0-3) and (t0 dims 4-7 | t1 dims 4-7)
-                        const uint32_t lo = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x05040100u);
-                        const uint32_t hi = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x07060302u);
-#pragma unroll
-                        for (int n = 0; n < 4; ++n) {
-                            const uint32_t pl = (lo >> (4 * n)) & 0x000F000Fu;
-                            const uint32_t ph = (hi >> (4 * n)) & 0x000F000Fu;
-#pragma unroll
-                            for (int h = 0; h < kG; ++h) {
-                                acc[h][8 * wdx + n] = fdot2(wp[h], pl, acc[h][8 * wdx + n]);
-                                acc[h][8 * wdx + 4 + n] = fdot2(wp[h], ph, acc[h][8 * wdx + 4 + n]);
-                            }
-                        }
-                    }
-                }
-                __syncthreads();
-            };
-            // one idle barrier (the K wave scores the first step), J work steps, idle barriers
-            __syncthreads();
-            int j = 0;
-#pragma unroll 1
-            for (int u = u_first; u < u_hi; u += 2) {
-                const int64_t t_page = (int64_t)u * kPage;
-                const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
-                const int ns = (int)((t_end - t_page + 31) / 32);
-                vstep(j, true);
-                ++j;
-#pragma unroll 1
-                for (int js = 1; js < ns; ++js, ++j) vstep(j, false);
-            }
-#pragma unroll 1
-            for (++j; j <= Jmax; ++j) __syncthreads();
-            // raw units -> values: remove the code offset, apply 2^24 and the page's c_V
-#pragma unroll
-            for (int h = 0; h < kG; ++h)
+            if (KVARN && page_start) {
+                // this page's value channel scales: rescale the accumulator to them (the
+                // accumulator is zero before the first page, so the first rescale is inert)
+                const uint4 c0 = *(const uint4*)(B.chan + 16 * vp);
+                const uint4 c1 = *(const uint4*)(B.chan + 16 * vp + 8);
+                const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) {
-                    float v = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * 16777216.0f;
-                    if (KVARN) v *= cv[jj];
-                    if (AFF) v += msum[h];
-                    acc[h][jj] = v;
+                    const float cn = fp16_to_f32((cw[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu);
+                    const float r = cv[jj] * __builtin_amdgcn_rcpf(cn);
+#pragma unroll
+                    for (int h = 0; h < kG; ++h) acc[h][jj] = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * r;
+                    cv[jj] = cn;
                 }
-            wait_vmcnt<0>();                          // stages past the end, before reusing the ring
-            asm volatile("" ::: "memory");
-            finish_v(acc);
+#pragma unroll
+                for (int h = 0; h < kG; ++h) wsum[h] = 0.0f;
+            }
+#pragma unroll 1
+            for (int half = 0; half < 2; ++half) {
+                const int slot = vg + 8 * half;
+                const uint2 a0 = *(const uint2*)(B.codes + 64 * slot + 8 * vp);
+                const uint2 a1 = *(const uint2*)(B.codes + 1024 + 64 * slot + 8 * vp);
+                uint32_t sv0, sv1;
+                if (AFF) {
+                    sv0 = ((const uint32_t*)B.scales)[8 * slot + vb];
+                    sv1 = ((const uint32_t*)B.scales)[8 * slot + 4 + vb];
+                } else {
+                    sv0 = ((const uint16_t*)B.scales)[8 * slot + vb];
+                    sv1 = ((const uint16_t*)B.scales)[8 * slot + 4 + vb];
+                }
+                const float vd0 = fp16_to_f32(sv0 & 0xFFFFu), vd1 = fp16_to_f32(sv1 & 0xFFFFu);
+                const float4 pa = *(const float4*)&P.p[slot][0][0];
+                const float4 pb = *(const float4*)&P.p[slot][1][0];
+                const float pp[4][2] = {{pa.x, pb.x}, {pa.y, pb.y}, {pa.z, pb.z}, {pa.w, pb.w}};
+                uint32_t wp[kG];
+#pragma unroll
+                for (int h = 0; h < kG; ++h) {
+                    wp[h] = pack_h2(pp[h][0] * vd0, pp[h][1] * vd1);
+                    wsum[h] = fdot2(wp[h], 0x3C003C00u, wsum[h]);
+                    if (AFF) {
+                        const float mv0 = fp16_to_f32(sv0 >> 16), mv1 = fp16_to_f32(sv1 >> 16);
+                        msum[h] = fmaf(pp[h][0], mv0 + 8.0f * vd0, fmaf(pp[h][1], mv1 + 8.0f * vd1, msum[h]));
+                    }
+                }
+                const uint32_t xw[2] = {a0.x, a0.y}, yw[2] = {a1.x, a1.y};
+#pragma unroll
+                for (int wdx = 0; wdx < 2; ++wdx) {
+                    // (t0 dims 0-3 | t1 dims 0-3) and (t0 dims 4-7 | t1 dims 4-7)
+                    const uint32_t lo = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x07060302u);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n) {
+                        const uint32_t pl = (lo >> (4 * n)) & 0x000F000Fu;
+                        const uint32_t ph = (hi >> (4 * n)) & 0x000F000Fu;
+#pragma unroll
+                        for (int h = 0; h < kG; ++h) {
+                            acc[h][8 * wdx + n] = fdot2(wp[h], pl, acc[h][8 * wdx + n]);
+                            acc[h][8 * wdx + 4 + n] = fdot2(wp[h], ph, acc[h][8 * wdx + 4 + n]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        };
+        // one idle barrier (the K wave scores the first step), J work steps, idle barriers
+        __syncthreads();
+        int j = 0;
+#pragma unroll 1
+        for (int u = u_first; u < u_hi; u += 2) {
+            const int64_t t_page = (int64_t)u * kPage;
+            const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
+            const int ns = (int)((t_end - t_page + 31) / 32);
+            vstep(j, true);
+            ++j;
+#pragma unroll 1
+            for (int js = 1; js < ns; ++js, ++j) vstep(j, false);
         }
+#pragma unroll 1
+        for (++j; j <= Jmax; ++j) __syncthreads();
+        // raw units -> values: remove the code offset, apply 2^24 and the page's c_V
+#pragma unroll
+        for (int h = 0; h < kG; ++h)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                float v = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * 16777216.0f;
+                if (KVARN) v *= cv[jj];
+                if (AFF) v += msum[h];
+                acc[h][jj] = v;
+            }
+        wait_vmcnt<0>();                          // stages past the end, before reusing the ring
+        asm volatile("" ::: "memory");
+        finish_v(acc);
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
     } else {
@@ -659,7 +734,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                     const float p0 = (tb + off < te) ? __builtin_amdgcn_exp2f(x[half][0] - mh) : 0.0f;
                     const float p1 = (tb + off + 1 < te) ? __builtin_amdgcn_exp2f(x[half][1] - mh) : 0.0f;
                     if (vp < kG) {
-                        *(float2*)&P.p[8 * half + vg][vp][0] = make_float2(p0, p1);
+                        P.p[8 * half + vg][0][vp] = p0;
+                        P.p[8 * half + vg][1][vp] = p1;
                         lsum += p0 + p1;
                     }
                 }
@@ -668,7 +744,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             }
 #pragma unroll 1
             for (; j <= Jmax; ++j) __syncthreads();
-            finish_k(mh, lsum, false);
+            finish_k(mh, lsum);
         } else {
             float acc[kG][16];
 #pragma unroll
@@ -710,8 +786,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                         }
                     }
                     const float4 pa = *(const float4*)&P.p[slot][0][0];
-                    const float4 pb = *(const float4*)&P.p[slot][2][0];
-                    const float pp[4][2] = {{pa.x, pa.y}, {pa.z, pa.w}, {pb.x, pb.y}, {pb.z, pb.w}};
+                    const float4 pb = *(const float4*)&P.p[slot][1][0];
+                    const float pp[4][2] = {{pa.x, pb.x}, {pa.y, pb.y}, {pa.z, pb.z}, {pa.w, pb.w}};
 #pragma unroll
                     for (int h = 0; h < kG; ++h)
 #pragma unroll
@@ -736,7 +812,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         for (int p = 0; p < 2; ++p) {
             const float ew = __builtin_amdgcn_exp2f(S.wm[p][h] - M);
             L += S.wl[p][h] * ew;
-            A += reinterpret_cast<const float (*)[kD]>(&S.st[2 + p][0])[h][d] * ew;
+            A += S.wacc[p][h][d] * ew;
         }
         part_out[2 * kMaxGroup + h * kD + d] = A;
         if (d == 0) { part_out[h] = M; part_out[kMaxGroup + h] = L; }
