@@ -47,6 +47,7 @@ constexpr int kStages = 3;               // LDS ring depth per wave
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ const char* sptr(const CacheGeom& g, int seq, int layer, int head, int isv)
 {
@@ -153,7 +154,7 @@ struct alignas(16) Stage {
 };
 
 struct alignas(16) PBuf {
-    float p[16][2][4];       // [pair slot][token of the pair][head] probabilities of the step
+    float p[kG][32];         // [head][token of the step] probabilities of the step
     float alpha[4];          // accumulator rescale of the step (running max grew)
     float pad[4];
 };
@@ -465,8 +466,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             if (q4 < 2) {
 #pragma unroll
                 for (int T = 0; T < 2; ++T) {
-                    const int t = 16 * T + n16;
-                    *(float2*)&P.p[t >> 1][t & 1][2 * hp] = make_float2(p[T][0], p[T][1]);
+                    P.p[2 * hp][16 * T + n16] = p[T][0];
+                    P.p[2 * hp + 1][16 * T + n16] = p[T][1];
                 }
             }
             if (n16 == 0 && q4 < 2) *(float2*)&P.alpha[2 * hp] = make_float2(al0, al1);
@@ -539,93 +540,91 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             issue(0);
             issue(1);
         }
-        float acc[kG][16], wsum[kG], msum[kG], cv[16];
+        // Lane = (token group tg = lane >> 4, block vblk = (lane >> 2) & 3, slice vj = lane & 3)
+        // owns dims 32 vblk + 8 vj .. + 7.  In half `hf` of a step the group takes the token
+        // pairs s0 = 8 hf + tg and s1 = s0 + 4 (tokens 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1).  MFMA
+        // block (tg, vblk) = lanes 4 (lane >> 2) .. + 3: A row i = the binary16 weights p d of
+        // head i for the four tokens, B column i = the codes of dim 32 vblk + 8 i + r as
+        // binary16 subnormals u 2^-24 (r = 0..7, one MFMA each), K = the four tokens; D column i
+        // accumulates the four heads of that dim.
+        const int tg = lane >> 4, vblk = (lane >> 2) & 3, vj = lane & 3;
+        f32x4 D[8];
 #pragma unroll
-        for (int h = 0; h < kG; ++h) {
-            wsum[h] = 0.0f;
-            msum[h] = 0.0f;
+        for (int r = 0; r < 8; ++r) D[r] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        float ws = 0.0f, ms = 0.0f;   // sums of the weights p d and of p m, head vj, lane's tokens
+        float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
-        }
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) cv[jj] = 1.0f;
+        for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
+        auto quad_bcast = [&](float x, int h) -> float {     // lane h of the lane's quad
+            return h == 0 ? dpp<0x00>(x) : h == 1 ? dpp<0x55>(x) : h == 2 ? dpp<0xAA>(x) : dpp<0xFF>(x);
+        };
         auto vstep = [&](int j, bool page_start) __attribute__((always_inline)) {
             issue(j + 2);
             wait_vmcnt<2 * kLoads>();
             asm volatile("" ::: "memory");
             const Stage& B = ring[j % kStages];
             const PBuf& P = S.pb[pr][j & 1];
-            const float4 al = *(const float4*)P.alpha;
+            const f32x4 al = *(const f32x4*)P.alpha;
             if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
-                const float alv[kG] = {al.x, al.y, al.z, al.w};
 #pragma unroll
-                for (int h = 0; h < kG; ++h) {
-                    wsum[h] *= alv[h];
-                    msum[h] *= alv[h];
-#pragma unroll
-                    for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
-                }
+                for (int r = 0; r < 8; ++r) D[r] *= al;
+                const float aj = al[vj];
+                ws *= aj;
+                ms *= aj;
             }
             if (KVARN && page_start) {
-                // this page's value channel scales: rescale the accumulator to them (the
-                // accumulator is zero before the first page, so the first rescale is inert)
-                const uint4 c0 = *(const uint4*)(B.chan + 16 * vp);
-                const uint4 c1 = *(const uint4*)(B.chan + 16 * vp + 8);
-                const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                // this page's value channel scales: move the accumulator to them (it is zero
+                // before the first page, so the first move is inert)
+                const uint4 c = *(const uint4*)(B.chan + 32 * vblk + 8 * vj);
+                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+                const f32x4 wh = {quad_bcast(ws, 0), quad_bcast(ws, 1), quad_bcast(ws, 2), quad_bcast(ws, 3)};
 #pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const float cn = fp16_to_f32((cw[jj >> 1] >> (16 * (jj & 1))) & 0xFFFFu);
-                    const float r = cv[jj] * __builtin_amdgcn_rcpf(cn);
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) acc[h][jj] = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * r;
-                    cv[jj] = cn;
+                for (int r = 0; r < 8; ++r) {
+                    const float cn = fp16_to_f32((cw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+                    const float f = cvr[r] * __builtin_amdgcn_rcpf(cn);
+                    D[r] = (D[r] - (8.0f * kSub) * wh) * f;
+                    cvr[r] = cn;
                 }
-#pragma unroll
-                for (int h = 0; h < kG; ++h) wsum[h] = 0.0f;
+                ws = 0.0f;
             }
+            const uint32_t* cw32 = (const uint32_t*)B.codes;
 #pragma unroll 1
-            for (int half = 0; half < 2; ++half) {
-                const int slot = vg + 8 * half;
-                const uint2 a0 = *(const uint2*)(B.codes + 64 * slot + 8 * vp);
-                const uint2 a1 = *(const uint2*)(B.codes + 1024 + 64 * slot + 8 * vp);
-                uint32_t sv0, sv1;
-                if (AFF) {
-                    sv0 = ((const uint32_t*)B.scales)[8 * slot + vb];
-                    sv1 = ((const uint32_t*)B.scales)[8 * slot + 4 + vb];
-                } else {
-                    sv0 = ((const uint16_t*)B.scales)[8 * slot + vb];
-                    sv1 = ((const uint16_t*)B.scales)[8 * slot + 4 + vb];
-                }
-                const float vd0 = fp16_to_f32(sv0 & 0xFFFFu), vd1 = fp16_to_f32(sv1 & 0xFFFFu);
-                const float4 pa = *(const float4*)&P.p[slot][0][0];
-                const float4 pb = *(const float4*)&P.p[slot][1][0];
-                const float pp[4][2] = {{pa.x, pb.x}, {pa.y, pb.y}, {pa.z, pb.z}, {pa.w, pb.w}};
-                uint32_t wp[kG];
+            for (int hf = 0; hf < 2; ++hf) {
+                const int s0 = 8 * hf + tg, s1 = s0 + 4;
+                const int cofs = 4 * vblk + vj;
+                const uint32_t x0 = cw32[16 * s0 + cofs], x1 = cw32[16 * (16 + s0) + cofs];
+                const uint32_t x2 = cw32[16 * s1 + cofs], x3 = cw32[16 * (16 + s1) + cofs];
+                const float2 p01 = *(const float2*)&P.p[vj][2 * s0];
+                const float2 p23 = *(const float2*)&P.p[vj][2 * s1];
+                float d[4], m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                const int tk[4] = {2 * s0, 2 * s0 + 1, 2 * s1, 2 * s1 + 1};
 #pragma unroll
-                for (int h = 0; h < kG; ++h) {
-                    wp[h] = pack_h2(pp[h][0] * vd0, pp[h][1] * vd1);
-                    wsum[h] = fdot2(wp[h], 0x3C003C00u, wsum[h]);
+                for (int k = 0; k < 4; ++k) {
                     if (AFF) {
-                        const float mv0 = fp16_to_f32(sv0 >> 16), mv1 = fp16_to_f32(sv1 >> 16);
-                        msum[h] = fmaf(pp[h][0], mv0 + 8.0f * vd0, fmaf(pp[h][1], mv1 + 8.0f * vd1, msum[h]));
+                        const uint32_t w = ((const uint32_t*)B.scales)[4 * tk[k] + vblk];
+                        d[k] = fp16_to_f32(w & 0xFFFFu);
+                        m[k] = fp16_to_f32(w >> 16);
+                    } else {
+                        d[k] = fp16_to_f32(((const uint16_t*)B.scales)[4 * tk[k] + vblk]);
                     }
                 }
-                const uint32_t xw[2] = {a0.x, a0.y}, yw[2] = {a1.x, a1.y};
+                const uint32_t a01 = pack_h2(p01.x * d[0], p01.y * d[1]);
+                const uint32_t a23 = pack_h2(p23.x * d[2], p23.y * d[3]);
+                ws = fdot2(a23, 0x3C003C00u, fdot2(a01, 0x3C003C00u, ws));
+                if (AFF) ms = fmaf(p01.x, m[0], fmaf(p01.y, m[1], fmaf(p23.x, m[2], fmaf(p23.y, m[3], ms))));
+                const h16x4 A = __builtin_bit_cast(h16x4, make_uint2(a01, a23));
+                // (token 2s dims 0-3 | token 2s+1 dims 0-3) and the same for dims 4-7
+                const uint32_t lo01 = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
 #pragma unroll
-                for (int wdx = 0; wdx < 2; ++wdx) {
-                    // (t0 dims 0-3 | t1 dims 0-3) and (t0 dims 4-7 | t1 dims 4-7)
-                    const uint32_t lo = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(yw[wdx], xw[wdx], 0x07060302u);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) {
-                        const uint32_t pl = (lo >> (4 * n)) & 0x000F000Fu;
-                        const uint32_t ph = (hi >> (4 * n)) & 0x000F000Fu;
-#pragma unroll
-                        for (int h = 0; h < kG; ++h) {
-                            acc[h][8 * wdx + n] = fdot2(wp[h], pl, acc[h][8 * wdx + n]);
-                            acc[h][8 * wdx + 4 + n] = fdot2(wp[h], ph, acc[h][8 * wdx + 4 + n]);
-                        }
-                    }
+                for (int r = 0; r < 8; ++r) {
+                    const int n = r & 3;
+                    const uint32_t w01 = r < 4 ? lo01 : hi01, w23 = r < 4 ? lo23 : hi23;
+                    const uint32_t b01 = (w01 >> (4 * n)) & 0x000F000Fu;
+                    const uint32_t b23 = (w23 >> (4 * n)) & 0x000F000Fu;
+                    D[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(h16x4, make_uint2(b01, b23)), D[r], 0, 0, 0);
                 }
             }
             __syncthreads();
@@ -645,19 +644,34 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         }
 #pragma unroll 1
         for (++j; j <= Jmax; ++j) __syncthreads();
-        // raw units -> values: remove the code offset, apply 2^24 and the page's c_V
+        // sum the four token groups (lanes l ^ 16, l ^ 32); offsets of all heads of the block
 #pragma unroll
-        for (int h = 0; h < kG; ++h)
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                float v = fmaf(-8.0f * kSub, wsum[h], acc[h][jj]) * 16777216.0f;
-                if (KVARN) v *= cv[jj];
-                if (AFF) v += msum[h];
-                acc[h][jj] = v;
+            for (int c = 0; c < 4; ++c) {
+                float x = D[r][c];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                D[r][c] = x;
             }
+        ws += __shfl_xor(ws, 16);
+        ws += __shfl_xor(ws, 32);
+        ms += __shfl_xor(ms, 16);
+        ms += __shfl_xor(ms, 32);
+        const f32x4 wh = {quad_bcast(ws, 0), quad_bcast(ws, 1), quad_bcast(ws, 2), quad_bcast(ws, 3)};
+        const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};
         wait_vmcnt<0>();                          // stages past the end, before reusing the ring
         asm volatile("" ::: "memory");
-        finish_v(acc);
+        if (tg == 0) {
+            // raw units -> values: remove the code offset, apply 2^24 and the page's c_V
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                f32x4 v = AFF ? D[r] * 16777216.0f + mh4 : (D[r] - (8.0f * kSub) * wh) * 16777216.0f;
+                if (KVARN) v *= cvr[r];
+#pragma unroll
+                for (int h = 0; h < kG; ++h) S.wacc[pr][h][32 * vblk + 8 * vj + r] = v[h];
+            }
+        }
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
     } else {
@@ -734,8 +748,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                     const float p0 = (tb + off < te) ? __builtin_amdgcn_exp2f(x[half][0] - mh) : 0.0f;
                     const float p1 = (tb + off + 1 < te) ? __builtin_amdgcn_exp2f(x[half][1] - mh) : 0.0f;
                     if (vp < kG) {
-                        P.p[8 * half + vg][0][vp] = p0;
-                        P.p[8 * half + vg][1][vp] = p1;
+                        *(float2*)&P.p[vp][16 * half + 2 * vg] = make_float2(p0, p1);
                         lsum += p0 + p1;
                     }
                 }
@@ -785,9 +798,13 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                             vx[t][2 * i + 1] = bf16_to_f32(ww[i] >> 16);
                         }
                     }
-                    const float4 pa = *(const float4*)&P.p[slot][0][0];
-                    const float4 pb = *(const float4*)&P.p[slot][1][0];
-                    const float pp[4][2] = {{pa.x, pb.x}, {pa.y, pb.y}, {pa.z, pb.z}, {pa.w, pb.w}};
+                    float pp[4][2];
+#pragma unroll
+                    for (int h = 0; h < kG; ++h) {
+                        const float2 w = *(const float2*)&P.p[h][2 * slot];
+                        pp[h][0] = w.x;
+                        pp[h][1] = w.y;
+                    }
 #pragma unroll
                     for (int h = 0; h < kG; ++h)
 #pragma unroll
