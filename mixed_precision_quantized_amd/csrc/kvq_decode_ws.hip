@@ -2,32 +2,31 @@
 //
 // Same work split as the generic kernel (kvq_decode.hip): 128-token quantized pages and
 // 32-token ring chunks, balanced splits, partial results merged by kvq_merge.hip.  Inside a
-// workgroup the waves specialize, so each role fits in half the registers and four waves
-// share every SIMD:
+// workgroup the waves specialize, so each role fits in 128 VGPRs and four waves share every
+// SIMD:
 //
-//   waves 0,1  "K waves"  score 32 tokens per step and run the softmax;
-//   waves 2,3  "V waves"  accumulate the values of the step the K waves finished before.
+//   "K waves"  score 32 tokens per step and run the online softmax;
+//   "V waves"  accumulate the values of the step the K waves finished before.
 //
-// Wave w and wave w+2 form a pair that walks every other unit of the workgroup; the pair
+// A K wave and a V wave form a pair that walks every other unit of the workgroup; the pair
 // hands the probabilities of a step over through a double-buffered block of LDS, and the
-// whole workgroup takes one barrier per step.  Every wave streams its own rows (K codes or
-// V codes, block scales and, for KVarN, the page's channel scales) through a three-deep
-// LDS ring filled by direct global-to-LDS loads two steps ahead.
+// whole workgroup takes one barrier per step.  Waves 0,1 are the K waves of even
+// workgroups and waves 2,3 those of odd ones, so every SIMD runs both roles.
 //
-//  K: one lane per 32-dim block of a token pair.  Codes become signed nibbles u-8 with one
-//     XOR; the query of each head is a 16-bit fixed-point vector per block (scale
-//     S = max|q|/30583) split into four signed 4-bit digits, so q.k over 8 dims is four
-//     v_dot8_i32_i4 with exact integer sums.  Lane k of a quad holds the partial sums of
-//     head (k xor r) in slot r; a two-step DPP reduce-scatter leaves lane k with head k.
-//     One running max per head is shared by the wave; a step whose maximum grows passes the
-//     rescale factors to the V wave.
-//  V: 8 lanes per token pair, 16 dims per lane.  v_perm interleaves the codes of the two
-//     tokens so each word holds (u_t0, u_t1) as two binary16 subnormals u*2^-24, and
-//     v_dot2_f32_f16 with the binary16 weights (p*d_t0, p*d_t1) adds both tokens at once.
-//     The code offset is removed exactly with the running sum of the weights.
+//  K: the query of each head is a 16-bit fixed-point vector per 32-dim block (scale
+//     S = max|q| / 30583) split into a low and a high signed byte; the scores of 16 tokens
+//     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (block, head, byte) and whose
+//     other operand is the unpacked code nibbles.  The integer dot products are exact; the
+//     code offset 8 and the per-(token, block) scale apply afterwards.  Codes and scales go
+//     to registers, three steps in flight.
+//  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
+//     the binary16 weights p*d of the four heads, B = the centred codes u - 8 of one dim
+//     per column as exact binary16 integers (v_perm interleaves token pairs; 0x6400 | u is
+//     1024 + u), K = the four tokens.  The V codes stream through a three-deep LDS ring
+//     filled by direct global-to-LDS loads two steps ahead.
 //  KVarN: keys are scored in the rotated domain with q'' = (H q / 128) * c_K of the page;
 //     values accumulate in the rotated domain scaled by the page's c_V and are rotated back
-//     once in the final merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard).
+//     once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard matrix).
 //  Ring (BF16 tail) workgroups use the same pairing with binary32 arithmetic.
 #include <float.h>
 
@@ -41,7 +40,6 @@ constexpr int kG = 4;
 constexpr float kNeg = -1.0e30f;
 constexpr float kQLim = 30583.0f;        // |q_int| bound so that q_int + 34952 fits 16 bits
 constexpr int kQBias = 34952;            // 8 * (1 + 16 + 256 + 4096): offset 8 in each digit
-constexpr float kSub = 5.9604644775390625e-08f;   // 2^-24: unit of a binary16 subnormal code
 constexpr int kStages = 3;               // LDS ring depth per wave
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -544,14 +542,16 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         // owns dims 32 vblk + 8 vj .. + 7.  In half `hf` of a step the group takes the token
         // pairs s0 = 8 hf + tg and s1 = s0 + 4 (tokens 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1).  MFMA
         // block (tg, vblk) = lanes 4 (lane >> 2) .. + 3: A row i = the binary16 weights p d of
-        // head i for the four tokens, B column i = the codes of dim 32 vblk + 8 i + r as
-        // binary16 subnormals u 2^-24 (r = 0..7, one MFMA each), K = the four tokens; D column i
-        // accumulates the four heads of that dim.
+        // head i for the four tokens, B column i = the centred codes u - 8 of dim
+        // 32 vblk + 8 i + r as exact binary16 integers (r = 0..7, one MFMA each), K = the four
+        // tokens; D column i accumulates the four heads of that dim.  Centring before the sum
+        // matters at long context: with spread attention the output is far smaller than
+        // sum(w u) or 8 sum(w), and the fp32 rounding of either would be amplified.
         const int tg = lane >> 4, vblk = (lane >> 2) & 3, vj = lane & 3;
         f32x4 D[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) D[r] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        float ws = 0.0f, ms = 0.0f;   // sums of the weights p d and of p m, head vj, lane's tokens
+        float ms = 0.0f;              // sum of p (m + 8 d) of head vj over the lane's tokens (affine)
         float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
 #pragma unroll
         for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
@@ -568,24 +568,19 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) D[r] *= al;
-                const float aj = al[vj];
-                ws *= aj;
-                ms *= aj;
+                ms *= al[vj];
             }
             if (KVARN && page_start) {
                 // this page's value channel scales: move the accumulator to them (it is zero
                 // before the first page, so the first move is inert)
                 const uint4 c = *(const uint4*)(B.chan + 32 * vblk + 8 * vj);
                 const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-                const f32x4 wh = {quad_bcast(ws, 0), quad_bcast(ws, 1), quad_bcast(ws, 2), quad_bcast(ws, 3)};
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const float cn = fp16_to_f32((cw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
-                    const float f = cvr[r] * __builtin_amdgcn_rcpf(cn);
-                    D[r] = (D[r] - (8.0f * kSub) * wh) * f;
+                    D[r] *= cvr[r] * __builtin_amdgcn_rcpf(cn);
                     cvr[r] = cn;
                 }
-                ws = 0.0f;
             }
             const uint32_t* cw32 = (const uint32_t*)B.codes;
 #pragma unroll 1
@@ -610,8 +605,10 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 }
                 const uint32_t a01 = pack_h2(p01.x * d[0], p01.y * d[1]);
                 const uint32_t a23 = pack_h2(p23.x * d[2], p23.y * d[3]);
-                ws = fdot2(a23, 0x3C003C00u, fdot2(a01, 0x3C003C00u, ws));
-                if (AFF) ms = fmaf(p01.x, m[0], fmaf(p01.y, m[1], fmaf(p23.x, m[2], fmaf(p23.y, m[3], ms))));
+                if (AFF) {
+                    ms = fmaf(p01.x, fmaf(8.0f, d[0], m[0]), fmaf(p01.y, fmaf(8.0f, d[1], m[1]), ms));
+                    ms = fmaf(p23.x, fmaf(8.0f, d[2], m[2]), fmaf(p23.y, fmaf(8.0f, d[3], m[3]), ms));
+                }
                 const h16x4 A = __builtin_bit_cast(h16x4, make_uint2(a01, a23));
                 // (token 2s dims 0-3 | token 2s+1 dims 0-3) and the same for dims 4-7
                 const uint32_t lo01 = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
@@ -622,9 +619,12 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 for (int r = 0; r < 8; ++r) {
                     const int n = r & 3;
                     const uint32_t w01 = r < 4 ? lo01 : hi01, w23 = r < 4 ? lo23 : hi23;
-                    const uint32_t b01 = (w01 >> (4 * n)) & 0x000F000Fu;
-                    const uint32_t b23 = (w23 >> (4 * n)) & 0x000F000Fu;
-                    D[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(h16x4, make_uint2(b01, b23)), D[r], 0, 0, 0);
+                    // 0x6400 | u is the binary16 value 1024 + u; minus 1032 gives u - 8 exactly
+                    const half2_t c8 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+                    const half2_t b01 = __builtin_bit_cast(half2_t, ((w01 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
+                    const half2_t b23 = __builtin_bit_cast(half2_t, ((w23 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
+                    const h16x4 Bm = {b01.x, b01.y, b23.x, b23.y};
+                    D[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bm, D[r], 0, 0, 0);
                 }
             }
             __syncthreads();
@@ -654,19 +654,16 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 x += __shfl_xor(x, 32);
                 D[r][c] = x;
             }
-        ws += __shfl_xor(ws, 16);
-        ws += __shfl_xor(ws, 32);
         ms += __shfl_xor(ms, 16);
         ms += __shfl_xor(ms, 32);
-        const f32x4 wh = {quad_bcast(ws, 0), quad_bcast(ws, 1), quad_bcast(ws, 2), quad_bcast(ws, 3)};
         const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};
         wait_vmcnt<0>();                          // stages past the end, before reusing the ring
         asm volatile("" ::: "memory");
         if (tg == 0) {
-            // raw units -> values: remove the code offset, apply 2^24 and the page's c_V
+            // the affine minimum (and the 8 d of the centring) and the page's c_V
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                f32x4 v = AFF ? D[r] * 16777216.0f + mh4 : (D[r] - (8.0f * kSub) * wh) * 16777216.0f;
+                f32x4 v = AFF ? D[r] + mh4 : D[r];
                 if (KVARN) v *= cvr[r];
 #pragma unroll
                 for (int h = 0; h < kG; ++h) S.wacc[pr][h][32 * vblk + 8 * vj + r] = v[h];
