@@ -27,6 +27,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic_kvarn4_ctx240000.md")
+DECODE_SOURCES = ["kvq_decode_ws.hip", "kvq_decode.hip", "kvq_merge.hip", "kvq_host.cpp",
+                  "kvq_internal.h", "kvq_device.h"]
+
+
+def measured_traffic(fmt, ctx, tail, kv_heads):
+    """HBM bytes of one decode call from the committed counter summary, or None when it
+    does not cover this workload or the decode sources changed since it was taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    want = {"fmt": fmt, "ctx": str(ctx), "tail": str(tail), "kv_heads": str(kv_heads),
+            "sources_sha256": h.hexdigest()}
+    for line in lines:
+        parts = line.split()
+        if parts[:1] != ["traffic_per_call"]:
+            continue
+        kv = dict(x.split("=", 1) for x in parts[1:])
+        if all(kv.get(k) == v for k, v in want.items()):
+            return int(kv["bytes"])
+    return None
 
 
 def parse():
@@ -245,7 +272,7 @@ def main():
         "metric": "decode-attn KV read GB/s (% of HBM peak) @240k ctx; append tokens/s",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32 accumulate (i8 and f16 MFMA operands)", "data": "synthetic",
         "config": {"workload": "decode step, 64 layers x 8 KV heads x 32 q heads x d128, ctx %d, %s, "
                                "BF16 tail %d, batch 1" % (args.ctx, args.fmt, args.tail),
                    "layers": L, "kv_heads": H, "q_heads": QH, "ctx": args.ctx, "fmt": args.fmt,
@@ -254,9 +281,10 @@ def main():
         "decode_ms_per_step": round(dec_ms, 4),
         "append_tokens_per_s": round(app_tps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_decode<%s>" % args.fmt, "bytes_per_launch": int(launch_bytes),
-                     "launch_us": round(launch_ms * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.fmt, args.ctx, args.tail, H),
+                     "kernel": "one decode call: split-K decode kernel + merge kernel (%s)" % args.fmt,
+                     "bytes_per_launch": int(launch_bytes), "launch_us": round(launch_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
