@@ -22,8 +22,9 @@
 //  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
 //     the binary16 weights p*d of the four heads, B = the centred codes u - 8 of one dim
 //     per column as exact binary16 integers (v_perm interleaves token pairs; 0x6400 | u is
-//     1024 + u), K = the four tokens.  The V codes stream through a three-deep LDS ring
-//     filled by direct global-to-LDS loads two steps ahead.
+//     1024 + u, one v_pk_add_f16 centres two codes), K = the four tokens.  The V codes stream through a three-deep LDS ring
+//     filled by direct global-to-LDS loads, each issued at the end of the step two
+//     before its use.
 //  KVarN: keys are scored in the rotated domain with q'' = (H q / 128) * c_K of the page;
 //     values accumulate in the rotated domain scaled by the page's c_V and are rotated back
 //     once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard matrix).
@@ -558,9 +559,13 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         auto quad_bcast = [&](float x, int h) -> float {     // lane h of the lane's quad
             return h == 0 ? dpp<0x00>(x) : h == 1 ? dpp<0x55>(x) : h == 2 ? dpp<0xAA>(x) : dpp<0xFF>(x);
         };
+        // Stage j + 2 is issued at the end of step j, once the step's LDS reads are done: a
+        // global-to-LDS load in flight holds lgkmcnt for a while after issue, and every LDS
+        // wait of the step would pay for it.  The V wave publishes nothing through LDS, so its
+        // barrier needs no lgkmcnt wait (bare s_barrier; the clobber keeps the compiler from
+        // moving LDS accesses across it).
         auto vstep = [&](int j, bool page_start) __attribute__((always_inline)) {
-            issue(j + 2);
-            wait_vmcnt<2 * kLoads>();
+            wait_vmcnt<kLoads>();
             asm volatile("" ::: "memory");
             const Stage& B = ring[j % kStages];
             const PBuf& P = S.pb[pr][j & 1];
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 }
             }
             const uint32_t* cw32 = (const uint32_t*)B.codes;
-#pragma unroll 1
+#pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int s0 = 8 * hf + tg, s1 = s0 + 4;
                 const int cofs = 4 * vblk + vj;
@@ -619,7 +624,9 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 for (int r = 0; r < 8; ++r) {
                     const int n = r & 3;
                     const uint32_t w01 = r < 4 ? lo01 : hi01, w23 = r < 4 ? lo23 : hi23;
-                    // 0x6400 | u is the binary16 value 1024 + u; minus 1032 gives u - 8 exactly
+                    // 0x6400 | u is the binary16 value 1024 + u; minus 1032 gives u - 8 exactly.
+                    // (Not u 2^-24 - 8 2^-24: the weights can be subnormal too, and products of
+                    // two binary16 subnormals lose precision in the matrix unit.)
                     const half2_t c8 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
                     const half2_t b01 = __builtin_bit_cast(half2_t, ((w01 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
                     const half2_t b23 = __builtin_bit_cast(half2_t, ((w23 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
@@ -627,7 +634,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                     D[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bm, D[r], 0, 0, 0);
                 }
             }
-            __syncthreads();
+            issue(j + 2);
+            asm volatile("s_barrier" ::: "memory");
         };
         // one idle barrier (the K wave scores the first step), J work steps, idle barriers
         __syncthreads();
