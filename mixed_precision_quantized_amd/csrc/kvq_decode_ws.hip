@@ -556,6 +556,11 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
 #pragma unroll
         for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
+        // 0x64006400 kept in a register so that the mask-and-or is one v_and_or_b32
+        uint32_t k6400 = 0x64006400u;
+        asm volatile("" : "+v"(k6400));
+        const half2_t c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};   // 1024 + 8
+        const half2_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};   // 1024 + 16 * 8
         auto quad_bcast = [&](float x, int h) -> float {     // lane h of the lane's quad
             return h == 0 ? dpp<0x00>(x) : h == 1 ? dpp<0x55>(x) : h == 2 ? dpp<0xAA>(x) : dpp<0xFF>(x);
         };
@@ -615,23 +620,25 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                     ms = fmaf(p23.x, fmaf(8.0f, d[2], m[2]), fmaf(p23.y, fmaf(8.0f, d[3], m[3]), ms));
                 }
                 const h16x4 A = __builtin_bit_cast(h16x4, make_uint2(a01, a23));
-                // (token 2s dims 0-3 | token 2s+1 dims 0-3) and the same for dims 4-7
-                const uint32_t lo01 = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-                const uint32_t hi01 = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-                const uint32_t lo23 = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-                const uint32_t hi23 = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
+                // Byte k of a code word holds dims 2k (low nibble) and 2k+1 (high nibble).  v_perm
+                // puts byte k of the two tokens of a pair in bytes 0 and 2; masking in 0x6400
+                // gives the binary16 values 1024 + u (low nibble) or 1024 + 16 u (high nibble);
+                // one packed add centres them to u - 8 or 16 (u - 8), both exact.  The factor 16
+                // of the odd dims is removed at the end.
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int n = r & 3;
-                    const uint32_t w01 = r < 4 ? lo01 : hi01, w23 = r < 4 ? lo23 : hi23;
-                    // 0x6400 | u is the binary16 value 1024 + u; minus 1032 gives u - 8 exactly.
-                    // (Not u 2^-24 - 8 2^-24: the weights can be subnormal too, and products of
-                    // two binary16 subnormals lose precision in the matrix unit.)
-                    const half2_t c8 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-                    const half2_t b01 = __builtin_bit_cast(half2_t, ((w01 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
-                    const half2_t b23 = __builtin_bit_cast(half2_t, ((w23 >> (4 * n)) & 0x000F000Fu) | 0x64006400u) + c8;
-                    const h16x4 Bm = {b01.x, b01.y, b23.x, b23.y};
-                    D[r] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bm, D[r], 0, 0, 0);
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t sel = (uint32_t)k | ((uint32_t)(4 + k) << 16) | 0x0C000C00u;
+                    const uint32_t q01 = __builtin_amdgcn_perm(x1, x0, sel);
+                    const uint32_t q23 = __builtin_amdgcn_perm(x3, x2, sel);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const uint32_t m = e ? 0x00F000F0u : 0x000F000Fu;
+                        const half2_t c = e ? c1152 : c1032;
+                        const half2_t b01 = __builtin_bit_cast(half2_t, (q01 & m) | k6400) + c;
+                        const half2_t b23 = __builtin_bit_cast(half2_t, (q23 & m) | k6400) + c;
+                        const h16x4 Bm = {b01.x, b01.y, b23.x, b23.y};
+                        D[2 * k + e] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bm, D[2 * k + e], 0, 0, 0);
+                    }
                 }
             }
             issue(j + 2);
@@ -671,7 +678,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             // the affine minimum (and the 8 d of the centring) and the page's c_V
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                f32x4 v = AFF ? D[r] + mh4 : D[r];
+                f32x4 v = (r & 1) ? D[r] * 0.0625f : D[r];     // odd dims carried a factor 16
+                if (AFF) v += mh4;
                 if (KVARN) v *= cvr[r];
 #pragma unroll
                 for (int h = 0; h < kG; ++h) S.wacc[pr][h][32 * vblk + 8 * vj + r] = v[h];
