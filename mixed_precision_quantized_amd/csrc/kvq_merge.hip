@@ -21,18 +21,22 @@ namespace {
 
 constexpr int kG = 4;
 constexpr int kCols = kD / 4;                 // float4 columns of one head's accumulator
-constexpr int kGroups = 256 / kCols;          // split groups in the accumulation phase
+constexpr int kGroups = 32;                   // split groups: thread = (group, column)
+constexpr int kThreads = kGroups * kCols;     // 1024
 
-// One workgroup per (sequence, KV head, query head of the group).
+// One workgroup per (sequence, KV head, query head of the group).  Thread (g, c) merges
+// float4 column c over the splits g, g + 32, ... with its own running maximum, so all its
+// loads are independent and issue together (a wave reads two splits' full rows); the 32
+// groups then combine through LDS.
 template <bool KVARN>
-__global__ __launch_bounds__(256) void k_merge(DecodeArgs a)
+__global__ __launch_bounds__(kThreads) void k_merge(DecodeArgs a)
 {
-    __shared__ float4 red[kGroups][2][kCols];  // [split group][quantized | ring][column]
+    __shared__ float4 rq[kGroups][kCols], rt[kGroups][kCols];   // [group][column]
+    __shared__ float gm[kGroups], gl[kGroups];
     __shared__ float vq[kD], vt[kD];
-    __shared__ float wm[4], wl[4];
     __shared__ float ML[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, c = tid % kCols, g = tid / kCols;
     const int H = a.g.n_kv_heads;
     const int e = blockIdx.x / (H * kG);
     const int head = (blockIdx.x / kG) % H;
@@ -41,62 +45,52 @@ __global__ __launch_bounds__(256) void k_merge(DecodeArgs a)
     const int SPL = sq.splits_q + sq.splits_t;
     const float* parts = a.partials + (int64_t)(sq.wg_base + head * SPL) * kPartialFloats;
 
-    // maximum and normalizer: one online pass per thread, then across the workgroup
     float mx = -1.0e30f, L = 0.0f;
-    for (int s = tid; s < SPL; s += 256) {
-        const float m = parts[(int64_t)s * kPartialFloats + h];
-        const float l = parts[(int64_t)s * kPartialFloats + kMaxGroup + h];
-        const float nm = fmaxf(mx, m);
-        L = L * __builtin_amdgcn_exp2f(mx - nm) + l * __builtin_amdgcn_exp2f(m - nm);
-        mx = nm;
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float m2 = __shfl_xor(mx, o), l2 = __shfl_xor(L, o);
-        const float nm = fmaxf(mx, m2);
-        L = L * __builtin_amdgcn_exp2f(mx - nm) + l2 * __builtin_amdgcn_exp2f(m2 - nm);
-        mx = nm;
-    }
-    if (lane == 0) { wm[wave] = mx; wl[wave] = L; }
-    __syncthreads();
-    if (tid == 0) {
-        float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
-        float T = 0.0f;
-        for (int w = 0; w < 4; ++w) T += wl[w] * __builtin_amdgcn_exp2f(wm[w] - M);
-        ML[0] = M;
-        ML[1] = T;
-    }
-    __syncthreads();
-    const float M = ML[0];
-
-    // rescaled accumulators: thread = (split group, float4 column)
-    {
-        const int c = tid % kCols, sg = tid / kCols;
-        float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), at = aq;
+    float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), at = aq;
 #pragma unroll 4
-        for (int s = sg; s < SPL; s += kGroups) {
-            const float* pp = parts + (int64_t)s * kPartialFloats;
-            const float w = __builtin_amdgcn_exp2f(pp[h] - M);
-            const float4 v = *(const float4*)(pp + 2 * kMaxGroup + h * kD + 4 * c);
-            float4& d = s < sq.splits_q ? aq : at;
-            d.x = fmaf(v.x, w, d.x);
-            d.y = fmaf(v.y, w, d.y);
-            d.z = fmaf(v.z, w, d.z);
-            d.w = fmaf(v.w, w, d.w);
-        }
-        red[sg][0][c] = aq;
-        red[sg][1][c] = at;
+    for (int s = g; s < SPL; s += kGroups) {
+        const float* pp = parts + (int64_t)s * kPartialFloats;
+        const float m = pp[h];
+        const float l = pp[kMaxGroup + h];
+        const float4 v = *(const float4*)(pp + 2 * kMaxGroup + h * kD + 4 * c);
+        const float nm = fmaxf(mx, m);
+        const float r = __builtin_amdgcn_exp2f(mx - nm), w = __builtin_amdgcn_exp2f(m - nm);
+        mx = nm;
+        L = fmaf(L, r, l * w);
+        const bool isq = s < sq.splits_q;
+        aq.x = fmaf(aq.x, r, isq ? v.x * w : 0.0f); aq.y = fmaf(aq.y, r, isq ? v.y * w : 0.0f);
+        aq.z = fmaf(aq.z, r, isq ? v.z * w : 0.0f); aq.w = fmaf(aq.w, r, isq ? v.w * w : 0.0f);
+        at.x = fmaf(at.x, r, isq ? 0.0f : v.x * w); at.y = fmaf(at.y, r, isq ? 0.0f : v.y * w);
+        at.z = fmaf(at.z, r, isq ? 0.0f : v.z * w); at.w = fmaf(at.w, r, isq ? 0.0f : v.w * w);
+    }
+    if (c == 0) { gm[g] = mx; gl[g] = L; }
+    __syncthreads();
+    if (tid < 64) {                           // one wave: maximum and normalizer over groups
+        const float m = tid < kGroups ? gm[tid] : -1.0e30f;
+        float M = m;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        float T = tid < kGroups ? gl[tid] * __builtin_amdgcn_exp2f(m - M) : 0.0f;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) T += __shfl_xor(T, o);
+        if (tid == 0) { ML[0] = M; ML[1] = T; }
     }
     __syncthreads();
-    if (tid < kD) {
-        const int c = tid >> 2, k = tid & 3;
-        float sq_ = 0.0f, st = 0.0f;
-        for (int g = 0; g < kGroups; ++g) {
-            sq_ += reinterpret_cast<const float*>(&red[g][0][c])[k];
-            st += reinterpret_cast<const float*>(&red[g][1][c])[k];
-        }
-        vq[tid] = sq_;
-        vt[tid] = st;
+    {
+        // rescale to the common maximum before the sum, so the column sums below are plain adds
+        const float w = __builtin_amdgcn_exp2f(mx - ML[0]);
+        rq[g][c] = make_float4(aq.x * w, aq.y * w, aq.z * w, aq.w * w);
+        rt[g][c] = make_float4(at.x * w, at.y * w, at.z * w, at.w * w);
+    }
+    __syncthreads();
+    if (tid < 2 * kD) {
+        // thread = (quantized | ring part, dim): 32 adds down the groups
+        const int part = tid / kD, d = tid % kD, cc = d >> 2, k = d & 3;
+        const float4 (*r)[kCols] = part ? rt : rq;
+        float sum = 0.0f;
+#pragma unroll 8
+        for (int gg = 0; gg < kGroups; ++gg) sum += reinterpret_cast<const float*>(&r[gg][cc])[k];
+        (part ? vt : vq)[d] = sum;
     }
     if (KVARN) {
         // x = H yhat / 128, butterflies of span 1, 2, .., 64
@@ -126,9 +120,9 @@ int launch_merge(const DecodeArgs& a, void* stream)
     hipStream_t st = (hipStream_t)stream;
     const int n = a.n_seqs * a.g.n_kv_heads * kG;
     if (fkind(a.g.fmt_k) == KIND_KVARN)
-        hipLaunchKernelGGL(k_merge<true>, dim3(n), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_merge<true>, dim3(n), dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL(k_merge<false>, dim3(n), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(k_merge<false>, dim3(n), dim3(kThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
