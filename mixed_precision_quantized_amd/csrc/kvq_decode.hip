@@ -204,9 +204,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
     const int head = r / S;
     const int sp = r % S;
     const bool quant = sp < sq.splits_q;
-    const int u_lo = (quant ? sp : sp - sq.splits_q) * a.units_per_wg;
+    const int upw = quant ? a.units_per_wg : a.units_per_wg_t;
+    const int u_lo = (quant ? sp : sp - sq.splits_q) * upw;
     const int u_cnt = quant ? sq.units_q : sq.units_t;
-    const int u_hi = min(u_lo + a.units_per_wg, u_cnt);
+    const int u_hi = min(u_lo + upw, u_cnt);
     const CacheGeom& g = a.g;
     const char* kst = stream_cptr(g, sq.seq, a.layer, head, 0);
     const char* vst = stream_cptr(g, sq.seq, a.layer, head, 1);

@@ -41,7 +41,7 @@ constexpr int kG = 4;
 constexpr float kNeg = -1.0e30f;
 constexpr float kQLim = 30583.0f;        // |q_int| bound so that q_int + 34952 fits 16 bits
 constexpr int kQBias = 34952;            // 8 * (1 + 16 + 256 + 4096): offset 8 in each digit
-constexpr int kStages = 3;               // LDS ring depth per wave
+constexpr int kStages = 4;               // LDS ring depth per wave
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -142,6 +142,61 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Raw buffer resource over [p, p + bytes): loads at or past `bytes` return zero, so a
+// step's loads need no clamping of rows past the end of a page.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, int off)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, int off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Buffer loads straight to LDS (lane l writes at lds + 16 l, or 4 l); like lds_load16, the
+// waits are explicit.
+__device__ __forceinline__ void lds_buf16(rsrc_t r, int voff, const void* lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_nop 0"
+                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_buf4(rsrc_t r, int voff, const void* lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds\n\ts_nop 0"
+                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
+}
+
+__device__ __forceinline__ _Float16 lo_half(uint32_t w)
+{
+    return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ _Float16 hi_half(uint32_t w)
+{
+    return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Maximum over the 16 lanes of a DPP row, in every lane of the row: four v_max_f32 with a
+// row rotation on the first operand (each preceded by the two wait states a DPP read of a
+// just-written VGPR needs).  Finite inputs only.
+__device__ __forceinline__ float row_max16(float x)
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+                 : "+v"(x));
+    return x;
+}
+
 // One 32-token step of one stream in LDS.  Code rows are stored even tokens first
 // (rows 0..15 = tokens 0,2,..,30) then odd tokens (rows 16..31), so both the score lanes
 // (16 bytes of one token) and the value lanes (8 bytes of one token) read without bank
@@ -153,7 +208,10 @@ struct alignas(16) Stage {
 };
 
 struct alignas(16) PBuf {
-    float p[kG][32];         // [head][token of the step] probabilities of the step
+    union {
+        float p[kG][32];     // [head][token of the step] probabilities of the step (ring)
+        _Float16 ph[kG][32]; // the same in binary16 (quantized pages)
+    };
     float alpha[4];          // accumulator rescale of the step (running max grew)
     float pad[4];
 };
@@ -171,7 +229,7 @@ struct alignas(16) QMat {
 struct alignas(16) WsLds {
     float qs[kG][kD];
     Stage st[2][kStages];    // LDS rings of the two value waves
-    PBuf pb[2][2];
+    PBuf pb[2][4];           // [pair][step % 4]
     QMat qm[2];
     float wm[2][kG], wl[2][kG];
     float wacc[2][kG][kD];   // slot-summed value accumulators of the pairs
@@ -270,9 +328,11 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     const int head = rr / SPL;
     const int sp = rr % SPL;
     const bool quant = sp < sq.splits_q;
-    const int u_lo = (quant ? sp : sp - sq.splits_q) * a.units_per_wg;
-    const int u_hi = min(u_lo + a.units_per_wg, quant ? sq.units_q : sq.units_t);
+    const int upw = quant ? a.units_per_wg : a.units_per_wg_t;
+    const int u_lo = (quant ? sp : sp - sq.splits_q) * upw;
+    const int u_hi = min(u_lo + upw, quant ? sq.units_q : sq.units_t);
     const CacheGeom& g = a.g;
+    const int nq = (int)sq.n_q;                      // token counts fit 31 bits
     const char* kst = sptr(g, sq.seq, a.layer, head, 0);
     const char* vst = sptr(g, sq.seq, a.layer, head, 1);
 
@@ -327,53 +387,55 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     };
     if (quant && kwave) {
         // ============================ K wave (MFMA scores) ============================
-        // One v_mfma_i32_16x16x64_i8 per (16-token tile, block pair): rows = (block of the
-        // pair, head, byte of q_int), columns = tokens, K = the 64 dims of the two blocks (a
-        // row is zero over the other block's dims).  Lane (n = lane & 15, q = lane >> 4)
-        // supplies the codes of token n, dims 16q..16q+15 of the pair, and receives the four
-        // rows 4q..4q+3: block 2bp + (q >> 1), heads 2(q & 1) and 2(q & 1) + 1, both bytes.
+        // One v_mfma_i32_16x16x64_i8 per (16-token tile, block pair): rows = (head, block of
+        // the pair, byte of q_int), columns = tokens, K = the 64 dims of the two blocks (a row
+        // is zero over the other block's dims).  Lane (n = lane & 15, q = lane >> 4) supplies
+        // the codes of token n, dims 16q..16q+15 of the pair, and receives rows 4q..4q+3:
+        // head q, both blocks of the pair, both bytes.  So a lane scores one head of one token
+        // per tile on its own, and the running maximum of a head is a 16-lane row reduction.
+        // The MFMA accumulator starts at -8 sum(q_int) of the block (symmetric formats), which
+        // takes the code offset 8 out of the integer sum.
         const int n16 = lane & 15, q4 = lane >> 4;
-        const int hp = q4 & 1, bsel = q4 >> 1;
         const char* kcodes = kst + g.k.codes;
         const char* kscales = kst + g.k.scales;
         const char* kchan = kst + g.k.cscale;
         QMat& Q = S.qm[pr];
-        i32x4 A[2];
-        float Sc[2][2], Qs[2][2];
-        int Of[2][2];
+        i32x4 A[2], Ci[2];
+        float Sc[4], Qs[4];
         auto load_a = [&]() {
-            const int m = n16, dig = m & 1, h = (m >> 1) & 3, sel = m >> 3;
+            const int m = n16, dig = m & 1, sel = (m >> 1) & 1, h = m >> 2;
 #pragma unroll
             for (int bp = 0; bp < 2; ++bp) {
-                const int b = 2 * bp + sel;
                 const i32x4 z = {0, 0, 0, 0};
-                A[bp] = sel == bsel ? *(const i32x4*)&Q.qa[dig][h][32 * b + 16 * (q4 & 1)] : z;
+                A[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[dig][h][32 * (2 * bp + sel) + 16 * (q4 & 1)] : z;
+                Ci[bp] = AFF ? z : (i32x4){-Q.off[q4][2 * bp], 0, -Q.off[q4][2 * bp + 1], 0};
+            }
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int hq = 2 * hp + hh, bq = 2 * bp + bsel;
-                    Sc[bp][hh] = Q.S[hq][bq];
-                    Of[bp][hh] = AFF ? 0 : Q.off[hq][bq];
-                    Qs[bp][hh] = AFF ? Q.qsum[hq][bq] : 0.0f;
-                }
+            for (int b = 0; b < 4; ++b) {
+                Sc[b] = Q.S[q4][b];
+                Qs[b] = AFF ? Q.qsum[q4][b] : 0.0f;
             }
         };
-        // codes and scales of one step, straight to registers (tokens clamped to the page)
+        // Codes and scales of one step, straight to registers through buffer loads whose
+        // resource covers the step's valid tokens: rows past the end of the page read as zero
+        // (their scores are masked).  Stages past the last step repeat it.
         struct KLoad { uint2 c[2][2]; uint4 s[2]; };
+        const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB;
         auto kload = [&](int j, KLoad& L) {
             const int jj = j < J ? j : J - 1;
             const int u = u_first + 2 * (jj >> 2);
-            const int64_t tp = (int64_t)u * kPage;
-            const int64_t te = min<int64_t>(tp + kPage, sq.n_q);
-            const int64_t tb = tp + 32 * (jj & 3);
+            const int tb = u * kPage + 32 * (jj & 3);
+            const int nv = min(32, min(u * kPage + kPage, nq) - tb);
+            const rsrc_t rc = make_rsrc(kcodes + (int64_t)tb * 64, nv * 64);
+            const rsrc_t rs = make_rsrc(kscales + (int64_t)tb * SB, nv * SB);
 #pragma unroll
             for (int T = 0; T < 2; ++T) {
-                const int64_t t = min<int64_t>(tb + 16 * T + n16, te - 1);
 #pragma unroll
-                for (int bp = 0; bp < 2; ++bp) L.c[T][bp] = *(const uint2*)(kcodes + t * 64 + 32 * bp + 8 * q4);
+                for (int bp = 0; bp < 2; ++bp) L.c[T][bp] = buf_load8(rc, cofs + 1024 * T + 32 * bp);
                 if (AFF) {
-                    L.s[T] = *(const uint4*)(kscales + t * 16);
+                    L.s[T] = buf_load16(rs, sofs + 16 * SB * T);
                 } else {
-                    const uint2 w = *(const uint2*)(kscales + t * 8);
+                    const uint2 w = buf_load8(rs, sofs + 16 * SB * T);
                     L.s[T] = make_uint4(w.x, w.y, 0u, 0u);
                 }
             }
@@ -383,8 +445,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             const int u = u_first + 2 * min(i, nu - 1);
             return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
         };
-        float mh0 = kNeg, mh1 = kNeg;              // running max of heads 2hp, 2hp + 1
-        float ls0 = 0.0f, ls1 = 0.0f;              // sums of p over the lane's tokens
+        float mh = kNeg;                           // running max of head q4
+        float ls = 0.0f;                           // sum of p over the lane's tokens
         uint4 cnext = make_uint4(0u, 0u, 0u, 0u);
         if (!KVARN) {
             build_qmat<AFF>(Q, S.qs, nullptr, lane);
@@ -395,8 +457,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         }
         auto kstep = [&](int j, const KLoad& L) __attribute__((always_inline)) {
             const int u = u_first + 2 * (j >> 2);
-            const int64_t t_page = (int64_t)u * kPage;
-            const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
+            const int t_page = u * kPage;
+            const int t_end = min(t_page + kPage, nq);
             if (KVARN && (j & 3) == 0) {
                 const uint4 cw = cnext;
                 cnext = chan_load((j >> 2) + 1);
@@ -405,71 +467,52 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 wave_sync_lds();
                 load_a();
             }
-            float sc[2][2];
+            float sc[2];
 #pragma unroll
             for (int T = 0; T < 2; ++T) {
-                float a0 = 0.0f, a1 = 0.0f;
+                float acc = 0.0f;
 #pragma unroll
                 for (int bp = 0; bp < 2; ++bp) {
                     const uint2 x = L.c[T][bp];
                     const i32x4 Bm = {(int)(x.x & 0x0F0F0F0Fu), (int)((x.x >> 4) & 0x0F0F0F0Fu),
                                       (int)(x.y & 0x0F0F0F0Fu), (int)((x.y >> 4) & 0x0F0F0F0Fu)};
-                    const i32x4 z = {0, 0, 0, 0};
-                    const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, z, 0, 0, 0);
-                    const int b = 2 * bp + bsel;
-                    float d, mm = 0.0f;
+                    const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, Ci[bp], 0, 0, 0);
+                    const int t0 = (C.y << 8) + C.x, t1 = (C.w << 8) + C.z;
+                    // block scales as binary16 operands of v_fma_mix (no conversion)
+                    uint32_t w0, w1;
                     if (AFF) {
-                        const uint32_t w = (b & 2) ? (bsel ? L.s[T].w : L.s[T].z) : (bsel ? L.s[T].y : L.s[T].x);
-                        d = fp16_to_f32(w & 0xFFFFu);
-                        mm = fp16_to_f32(w >> 16);
+                        w0 = bp ? L.s[T].z : L.s[T].x;
+                        w1 = bp ? L.s[T].w : L.s[T].y;
+                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
+                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)lo_half(w1), acc);
+                        acc = fmaf(Qs[2 * bp], (float)hi_half(w0), acc);
+                        acc = fmaf(Qs[2 * bp + 1], (float)hi_half(w1), acc);
                     } else {
-                        const uint32_t w = bp ? L.s[T].y : L.s[T].x;
-                        d = fp16_to_f32((w >> (16 * bsel)) & 0xFFFFu);
-                    }
-                    const int t0 = (C.y << 8) + C.x - Of[bp][0];
-                    const int t1 = (C.w << 8) + C.z - Of[bp][1];
-                    a0 = fmaf((float)t0, Sc[bp][0] * d, a0);
-                    a1 = fmaf((float)t1, Sc[bp][1] * d, a1);
-                    if (AFF) {
-                        a0 = fmaf(mm, Qs[bp][0], a0);
-                        a1 = fmaf(mm, Qs[bp][1], a1);
+                        w0 = bp ? L.s[T].y : L.s[T].x;
+                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
+                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)hi_half(w0), acc);
                     }
                 }
-                // the other two blocks are in lane ^ 32
-                const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a0), __float_as_uint(a0), false, false);
-                const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a1), __float_as_uint(a1), false, false);
-                const bool valid = t_page + 32 * (j & 3) + 16 * T + n16 < t_end;
-                sc[T][0] = valid ? __uint_as_float(r0[0]) + __uint_as_float(r0[1]) : kNeg;
-                sc[T][1] = valid ? __uint_as_float(r1[0]) + __uint_as_float(r1[1]) : kNeg;
+                sc[T] = acc;
             }
-            // running max per head over the 16 lanes of the row
-            float x0 = fmaxf(sc[0][0], sc[1][0]), x1 = fmaxf(sc[0][1], sc[1][1]);
-            x0 = fmaxf(x0, dpp<ROW_ROR8>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR8>(x1));
-            x0 = fmaxf(x0, dpp<ROW_ROR4>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR4>(x1));
-            x0 = fmaxf(x0, dpp<ROW_ROR2>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR2>(x1));
-            x0 = fmaxf(x0, dpp<ROW_ROR1>(x0)); x1 = fmaxf(x1, dpp<ROW_ROR1>(x1));
-            const float n0 = fmaxf(mh0, x0), n1 = fmaxf(mh1, x1);
-            const float al0 = __builtin_amdgcn_exp2f(mh0 - n0);     // exactly 1 if unchanged
-            const float al1 = __builtin_amdgcn_exp2f(mh1 - n1);
-            mh0 = n0;
-            mh1 = n1;
-            float p[2][2];
+            if (t_end - (t_page + 32 * (j & 3)) < 32) {
+                // the page ends inside this step: mask the rows past its end
 #pragma unroll
-            for (int T = 0; T < 2; ++T) {
-                p[T][0] = __builtin_amdgcn_exp2f(sc[T][0] - n0);
-                p[T][1] = __builtin_amdgcn_exp2f(sc[T][1] - n1);
+                for (int T = 0; T < 2; ++T)
+                    if (t_page + 32 * (j & 3) + 16 * T + n16 >= t_end) sc[T] = kNeg;
             }
-            ls0 = fmaf(ls0, al0, p[0][0] + p[1][0]);
-            ls1 = fmaf(ls1, al1, p[0][1] + p[1][1]);
-            PBuf& P = S.pb[pr][j & 1];
-            if (q4 < 2) {
-#pragma unroll
-                for (int T = 0; T < 2; ++T) {
-                    P.p[2 * hp][16 * T + n16] = p[T][0];
-                    P.p[2 * hp + 1][16 * T + n16] = p[T][1];
-                }
-            }
-            if (n16 == 0 && q4 < 2) *(float2*)&P.alpha[2 * hp] = make_float2(al0, al1);
+            // running max of head q4 over the step (a 16-lane row)
+            const float x = row_max16(fmaxf(sc[0], sc[1]));
+            const float nm = fmaxf(mh, x);
+            const float al = __builtin_amdgcn_exp2f(mh - nm);     // exactly 1 if unchanged
+            mh = nm;
+            const float p0 = __builtin_amdgcn_exp2f(sc[0] - nm);
+            const float p1 = __builtin_amdgcn_exp2f(sc[1] - nm);
+            ls = fmaf(ls, al, p0 + p1);
+            PBuf& P = S.pb[pr][j & 3];
+            P.ph[q4][n16] = (_Float16)p0;
+            P.ph[q4][16 + n16] = (_Float16)p1;
+            if (n16 == 0) P.alpha[q4] = al;
             __syncthreads();
         };
         // three register stages, loads issued two steps ahead of their use
@@ -493,17 +536,15 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         if (j < J) { kstep(j, Y); ++j; }
 #pragma unroll 1
         for (; j <= Jmax; ++j) __syncthreads();
-        // normalizers over the row; lanes 0 and 16 hold heads (0, 1) and (2, 3)
-        float l0 = ls0, l1 = ls1;
-        l0 += dpp<ROW_ROR8>(l0); l1 += dpp<ROW_ROR8>(l1);
-        l0 += dpp<ROW_ROR4>(l0); l1 += dpp<ROW_ROR4>(l1);
-        l0 += dpp<ROW_ROR2>(l0); l1 += dpp<ROW_ROR2>(l1);
-        l0 += dpp<ROW_ROR1>(l0); l1 += dpp<ROW_ROR1>(l1);
-        if (n16 == 0 && q4 < 2) {
-            S.wl[pr][2 * hp] = l0;
-            S.wl[pr][2 * hp + 1] = l1;
-            S.wm[pr][2 * hp] = mh0;
-            S.wm[pr][2 * hp + 1] = mh1;
+        // normalizer of head q4 over its row
+        float l = ls;
+        l += dpp<ROW_ROR8>(l);
+        l += dpp<ROW_ROR4>(l);
+        l += dpp<ROW_ROR2>(l);
+        l += dpp<ROW_ROR1>(l);
+        if (n16 == 0) {
+            S.wl[pr][q4] = l;
+            S.wm[pr][q4] = mh;
         }
     } else if (quant) {
         // ================================ V wave ================================
@@ -513,31 +554,39 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         Stage* ring = S.st[pr];
         // stage j -> ring slot j % kStages; the number of load instructions per stage is
         // fixed (stages past the end repeat the last), so one vmcnt value covers a stage.
-        auto issue = [&](int j) {
+        // Buffer resources over the step's valid rows: rows past the end of the page read as
+        // zero (the ring is zeroed first, so no slot ever holds non-finite bytes either way;
+        // the weights of those rows are zero).
+        const int ve = (lane >> 2) * 128 + (lane & 3) * 16;      // even rows of the stage
+        auto issue = [&](int j, int slot) {
             const int jj = j < J ? j : J - 1;
             const int u = u_first + 2 * (jj >> 2);
-            const int64_t tp = (int64_t)u * kPage;
-            const int64_t te = min<int64_t>(tp + kPage, sq.n_q);
-            const int64_t tb = tp + 32 * (jj & 3);
-            Stage& B = ring[j % kStages];
-            int64_t r = min<int64_t>(tb + 2 * (lane >> 2), te - 1);
-            lds_load16(cbase + r * 64 + 16 * (lane & 3), B.codes);
-            r = min<int64_t>(tb + 2 * (lane >> 2) + 1, te - 1);
-            lds_load16(cbase + r * 64 + 16 * (lane & 3), B.codes + 1024);
+            const int tb = u * kPage + 32 * (jj & 3);
+            const int nv = min(32, min(u * kPage + kPage, nq) - tb);
+            Stage& B = ring[slot];
+            const rsrc_t rc = make_rsrc(cbase + (int64_t)tb * 64, nv * 64);
+            lds_buf16(rc, ve, B.codes);
+            lds_buf16(rc, ve + 64, B.codes + 1024);
+            const rsrc_t rs = make_rsrc(sbase + (int64_t)tb * SB, nv * SB);
             if (AFF) {
-                r = min<int64_t>(tb + (lane & 31), te - 1);
-                if (lane < 32) lds_load16(sbase + r * 16, B.scales);
+                if (lane < 32) lds_buf16(rs, 16 * lane, B.scales);
             } else {
-                r = min<int64_t>(tb + (lane >> 1), te - 1);
-                lds_load4(sbase + r * 8 + 4 * (lane & 1), B.scales);
+                lds_buf4(rs, 4 * lane, B.scales);
             }
             if (KVARN) {
-                if (lane < 16) lds_load16(chbase + (int64_t)u * 256 + 16 * lane, B.chan);
+                if (lane < 16) lds_buf16(make_rsrc(chbase + (int64_t)u * 256, 256), 16 * lane, B.chan);
             }
         };
+        {
+            // zero the ring once
+            uint4* z = (uint4*)ring;
+            for (int i = lane; i < (int)(kStages * sizeof(Stage) / 16); i += 64) z[i] = make_uint4(0u, 0u, 0u, 0u);
+            wave_sync_lds();
+        }
         if (J > 0) {
-            issue(0);
-            issue(1);
+            issue(0, 0);
+            issue(1, 1);
+            issue(2, 2);
         }
         // Lane = (token group tg = lane >> 4, block vblk = (lane >> 2) & 3, slice vj = lane & 3)
         // owns dims 32 vblk + 8 vj .. + 7.  In half `hf` of a step the group takes the token
@@ -552,7 +601,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         f32x4 D[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) D[r] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        float ms = 0.0f;              // sum of p (m + 8 d) of head vj over the lane's tokens (affine)
+        float ms = 0.0f, msd = 0.0f;  // sums of p m and p d of head vj over the lane's tokens (affine)
         float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
 #pragma unroll
         for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
@@ -564,21 +613,23 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         auto quad_bcast = [&](float x, int h) -> float {     // lane h of the lane's quad
             return h == 0 ? dpp<0x00>(x) : h == 1 ? dpp<0x55>(x) : h == 2 ? dpp<0xAA>(x) : dpp<0xFF>(x);
         };
-        // Stage j + 2 is issued at the end of step j, once the step's LDS reads are done: a
+        // Stage j + 3 is issued at the end of step j, once the step's LDS reads are done: a
         // global-to-LDS load in flight holds lgkmcnt for a while after issue, and every LDS
         // wait of the step would pay for it.  The V wave publishes nothing through LDS, so its
         // barrier needs no lgkmcnt wait (bare s_barrier; the clobber keeps the compiler from
         // moving LDS accesses across it).
-        auto vstep = [&](int j, bool page_start) __attribute__((always_inline)) {
-            wait_vmcnt<kLoads>();
+        auto vstep = [&](int j, int slot) __attribute__((always_inline)) {
+            const bool page_start = (j & 3) == 0;
+            wait_vmcnt<2 * kLoads>();
             asm volatile("" ::: "memory");
-            const Stage& B = ring[j % kStages];
-            const PBuf& P = S.pb[pr][j & 1];
+            const Stage& B = ring[slot];
+            const PBuf& P = S.pb[pr][slot];
             const f32x4 al = *(const f32x4*)P.alpha;
             if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) D[r] *= al;
                 ms *= al[vj];
+                msd *= al[vj];
             }
             if (KVARN && page_start) {
                 // this page's value channel scales: move the accumulator to them (it is zero
@@ -599,25 +650,24 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 const int cofs = 4 * vblk + vj;
                 const uint32_t x0 = cw32[16 * s0 + cofs], x1 = cw32[16 * (16 + s0) + cofs];
                 const uint32_t x2 = cw32[16 * s1 + cofs], x3 = cw32[16 * (16 + s1) + cofs];
-                const float2 p01 = *(const float2*)&P.p[vj][2 * s0];
-                const float2 p23 = *(const float2*)&P.p[vj][2 * s1];
-                float d[4], m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                const int tk[4] = {2 * s0, 2 * s0 + 1, 2 * s1, 2 * s1 + 1};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (AFF) {
-                        const uint32_t w = ((const uint32_t*)B.scales)[4 * tk[k] + vblk];
-                        d[k] = fp16_to_f32(w & 0xFFFFu);
-                        m[k] = fp16_to_f32(w >> 16);
-                    } else {
-                        d[k] = fp16_to_f32(((const uint16_t*)B.scales)[4 * tk[k] + vblk]);
-                    }
-                }
-                const uint32_t a01 = pack_h2(p01.x * d[0], p01.y * d[1]);
-                const uint32_t a23 = pack_h2(p23.x * d[2], p23.y * d[3]);
+                // A: binary16 p (written by the K wave) times the binary16 block scales, two
+                // tokens per packed multiply; the scale pairs are gathered by 16-bit LDS loads
+                const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
+                const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
+                const _Float16* sc16 = (const _Float16*)B.scales;
+                constexpr int SW = SB / 2;                   // binary16 words per scale row
+                const int so = (AFF ? 2 : 1) * vblk;
+                const half2_t d01 = {sc16[SW * (2 * s0) + so], sc16[SW * (2 * s0 + 1) + so]};
+                const half2_t d23 = {sc16[SW * (2 * s1) + so], sc16[SW * (2 * s1 + 1) + so]};
+                const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * d01);
+                const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * d23);
                 if (AFF) {
-                    ms = fmaf(p01.x, fmaf(8.0f, d[0], m[0]), fmaf(p01.y, fmaf(8.0f, d[1], m[1]), ms));
-                    ms = fmaf(p23.x, fmaf(8.0f, d[2], m[2]), fmaf(p23.y, fmaf(8.0f, d[3], m[3]), ms));
+                    const half2_t m01 = {sc16[SW * (2 * s0) + so + 1], sc16[SW * (2 * s0 + 1) + so + 1]};
+                    const half2_t m23 = {sc16[SW * (2 * s1) + so + 1], sc16[SW * (2 * s1 + 1) + so + 1]};
+                    msd = __builtin_amdgcn_fdot2(p01, d01, msd, false);
+                    msd = __builtin_amdgcn_fdot2(p23, d23, msd, false);
+                    ms = __builtin_amdgcn_fdot2(p01, m01, ms, false);
+                    ms = __builtin_amdgcn_fdot2(p23, m23, ms, false);
                 }
                 const h16x4 A = __builtin_bit_cast(h16x4, make_uint2(a01, a23));
                 // Byte k of a code word holds dims 2k (low nibble) and 2k+1 (high nibble).  v_perm
@@ -641,22 +691,23 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                     }
                 }
             }
-            issue(j + 2);
+            issue(j + 3, (slot + 3) & 3);
             asm volatile("s_barrier" ::: "memory");
         };
         // one idle barrier (the K wave scores the first step), J work steps, idle barriers
         __syncthreads();
+        // steps in fours so that ring and probability slots are static
         int j = 0;
 #pragma unroll 1
-        for (int u = u_first; u < u_hi; u += 2) {
-            const int64_t t_page = (int64_t)u * kPage;
-            const int64_t t_end = min<int64_t>(t_page + kPage, sq.n_q);
-            const int ns = (int)((t_end - t_page + 31) / 32);
-            vstep(j, true);
-            ++j;
-#pragma unroll 1
-            for (int js = 1; js < ns; ++js, ++j) vstep(j, false);
+        for (; j + 3 < J; j += 4) {
+            vstep(j, 0);
+            vstep(j + 1, 1);
+            vstep(j + 2, 2);
+            vstep(j + 3, 3);
         }
+        if (j < J) { vstep(j, 0); ++j; }
+        if (j < J) { vstep(j, 1); ++j; }
+        if (j < J) { vstep(j, 2); ++j; }
 #pragma unroll 1
         for (++j; j <= Jmax; ++j) __syncthreads();
         // sum the four token groups (lanes l ^ 16, l ^ 32); offsets of all heads of the block
@@ -669,6 +720,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
                 x += __shfl_xor(x, 32);
                 D[r][c] = x;
             }
+        ms = fmaf(8.0f, msd, ms);       // sum of p (m + 8 d)
         ms += __shfl_xor(ms, 16);
         ms += __shfl_xor(ms, 32);
         const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};

@@ -87,10 +87,10 @@ struct DecodeArgs {
     CacheGeom g;
     int32_t layer;
     int32_t n_seqs;
-    int32_t units_per_wg;
+    int32_t units_per_wg;   // quantized pages per workgroup
     int32_t q_dtype;      // 0 bf16, 1 fp32
     float scale_log2;     // softmax_scale * log2(e)
-    int32_t pad_;
+    int32_t units_per_wg_t; // ring units per workgroup
     const void* q;        // [n_seqs][n_q_heads][128]
     float* out;           // [n_seqs][n_q_heads][128]
     float* partials;      // [max_wgs][kPartialFloats]

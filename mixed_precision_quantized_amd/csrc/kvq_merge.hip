@@ -47,21 +47,34 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeArgs a)
 
     float mx = -1.0e30f, L = 0.0f;
     float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), at = aq;
-#pragma unroll 4
-    for (int s = g; s < SPL; s += kGroups) {
-        const float* pp = parts + (int64_t)s * kPartialFloats;
-        const float m = pp[h];
-        const float l = pp[kMaxGroup + h];
-        const float4 v = *(const float4*)(pp + 2 * kMaxGroup + h * kD + 4 * c);
-        const float nm = fmaxf(mx, m);
-        const float r = __builtin_amdgcn_exp2f(mx - nm), w = __builtin_amdgcn_exp2f(m - nm);
-        mx = nm;
-        L = fmaf(L, r, l * w);
-        const bool isq = s < sq.splits_q;
-        aq.x = fmaf(aq.x, r, isq ? v.x * w : 0.0f); aq.y = fmaf(aq.y, r, isq ? v.y * w : 0.0f);
-        aq.z = fmaf(aq.z, r, isq ? v.z * w : 0.0f); aq.w = fmaf(aq.w, r, isq ? v.w * w : 0.0f);
-        at.x = fmaf(at.x, r, isq ? 0.0f : v.x * w); at.y = fmaf(at.y, r, isq ? 0.0f : v.y * w);
-        at.z = fmaf(at.z, r, isq ? 0.0f : v.z * w); at.w = fmaf(at.w, r, isq ? 0.0f : v.w * w);
+    // batches of kBatch splits per thread: all loads of a batch are issued before any is used
+    // (indices clamped to the last split, the surplus is masked out)
+    constexpr int kBatch = 4;
+    for (int s0 = g; s0 < SPL; s0 += kBatch * kGroups) {
+        float m[kBatch], l[kBatch];
+        float4 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const float* pp = parts + (int64_t)min(s0 + i * kGroups, SPL - 1) * kPartialFloats;
+            m[i] = pp[h];
+            l[i] = pp[kMaxGroup + h];
+            v[i] = *(const float4*)(pp + 2 * kMaxGroup + h * kD + 4 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int s = s0 + i * kGroups;
+            if (s >= SPL) break;
+            const float nm = fmaxf(mx, m[i]);
+            const float r = __builtin_amdgcn_exp2f(mx - nm), w = __builtin_amdgcn_exp2f(m[i] - nm);
+            mx = nm;
+            L = fmaf(L, r, l[i] * w);
+            const bool isq = s < sq.splits_q;
+            const float4 x = v[i];
+            aq.x = fmaf(aq.x, r, isq ? x.x * w : 0.0f); aq.y = fmaf(aq.y, r, isq ? x.y * w : 0.0f);
+            aq.z = fmaf(aq.z, r, isq ? x.z * w : 0.0f); aq.w = fmaf(aq.w, r, isq ? x.w * w : 0.0f);
+            at.x = fmaf(at.x, r, isq ? 0.0f : x.x * w); at.y = fmaf(at.y, r, isq ? 0.0f : x.y * w);
+            at.z = fmaf(at.z, r, isq ? 0.0f : x.z * w); at.w = fmaf(at.w, r, isq ? 0.0f : x.w * w);
+        }
     }
     if (c == 0) { gm[g] = mx; gl[g] = L; }
     __syncthreads();
