@@ -42,6 +42,8 @@ constexpr float kNeg = -1.0e30f;
 constexpr float kQLim = 30583.0f;        // |q_int| bound so that q_int + 34952 fits 16 bits
 constexpr int kQBias = 34952;            // 8 * (1 + 16 + 256 + 4096): offset 8 in each digit
 constexpr int kStages = 4;               // LDS ring depth per wave
+constexpr int kP = 8;                    // (K wave, V wave) pairs per workgroup
+constexpr int kThreads = 128 * kP;       // one workgroup per CU
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -228,55 +230,93 @@ struct alignas(16) QMat {
 
 struct alignas(16) WsLds {
     float qs[kG][kD];
-    Stage st[2][kStages];    // LDS rings of the two value waves
-    PBuf pb[2][4];           // [pair][step % 4]
-    QMat qm[2];
-    float wm[2][kG], wl[2][kG];
-    float wacc[2][kG][kD];   // slot-summed value accumulators of the pairs
+    Stage st[kP][kStages];   // LDS rings of the value waves
+    PBuf pb[kP][4];          // [pair][step % 4]
+    QMat qm[kP][2];          // [pair][page parity] (KVarN builds the next page's ahead)
+    float wm[kP][kG], wl[kP][kG];
+    float wacc[kP][kG][kD];  // slot-summed value accumulators of the pairs
 };
 
+// x * (binary16 half of w), one v_fma_mix_f32 (no separate conversion).
+__device__ __forceinline__ float mul_lo16(float x, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+    return r;
+}
+__device__ __forceinline__ float mul_hi16(float x, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+    return r;
+}
+
+// Maximum over the four lanes of a DPP quad (finite inputs).
+__device__ __forceinline__ float quad_max(float x)
+{
+    asm volatile("s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+                 "s_nop 1\n\t"
+                 "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                 : "+v"(x));
+    return x;
+}
+
 // Fixed-point query operand (one page or the whole split).  Lane = head h (lane >> 4) x
-// 8-dim group g8 (lane & 15).  cw: the 8 key channel scales of the group (KVarN) or null.
+// 8-dim group g8 (lane & 15); the four lanes of a quad hold one 32-dim block.  q: the lane's
+// 8 query values; cw: the 8 key channel scales of the group (KVarN) or null.
+//   q_int = round(q * inv), inv = 30583 / max|q| of the block, |q_int| <= 30583; one fma
+//   with 1.5 * 2^23 + 128 leaves q_int + 128 in the low 16 bits of the result (the sum
+//   stays in [2^23, 2^24), where the float spacing is 1).  Its high byte is the signed high
+//   digit h8 and its low byte l8 + 128, so q_int = 256 h8 + l8 with l8 in [-128, 127]
+//   (flipping bit 7 of the low byte gives l8).
 template <bool AFFINE>
-__device__ __forceinline__ void build_qmat(QMat& Q, const float (*src)[kD], const uint4* cw, int lane)
+__device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const uint4* cw, int lane)
 {
     const int h = lane >> 4, g8 = lane & 15, kb = g8 >> 2;
     float v[8];
-    const uint32_t cc[4] = {cw ? cw->x : 0u, cw ? cw->y : 0u, cw ? cw->z : 0u, cw ? cw->w : 0u};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float q = src[h][8 * g8 + e];
-        if (cw) q *= fp16_to_f32((cc[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        v[e] = q;
+    for (int e = 0; e < 8; ++e) v[e] = q[e];
+    if (cw) {
+        const uint32_t cc[4] = {cw->x, cw->y, cw->z, cw->w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? mul_hi16(v[e], cc[e >> 1]) : mul_lo16(v[e], cc[e >> 1]);
     }
-    float amax = 0.0f, sum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { amax = fmaxf(amax, fabsf(v[e])); sum += v[e]; }
-    amax = fmaxf(amax, dpp<QP_XOR1>(amax));
-    amax = fmaxf(amax, dpp<QP_XOR2>(amax));
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+    amax = fmaxf(fmaxf(amax, fabsf(v[3])), fabsf(v[4]));
+    amax = fmaxf(fmaxf(amax, fabsf(v[5])), fabsf(v[6]));
+    amax = quad_max(fmaxf(amax, fabsf(v[7])));
+    float sum = 0.0f;
     if (AFFINE) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += v[e];
         sum += dpp<QP_XOR1>(sum);
         sum += dpp<QP_XOR2>(sum);
     }
     const float inv = amax > 0.0f ? kQLim * __builtin_amdgcn_rcpf(amax) : 0.0f;
-    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
-    int isum = 0;
+    uint32_t qb[8];
+    uint32_t bsum = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int qi = (int)__builtin_rintf(fminf(fmaxf(v[e] * inv, -kQLim), kQLim));
-        const int l8 = ((qi + 128) & 255) - 128;       // signed low byte
-        const int h8 = (qi - l8) >> 8;                 // signed high byte
-        const int pos = (e & 1) * 4 + (e >> 1);        // even dims first
-        lo[pos >> 2] |= ((uint32_t)l8 & 255u) << (8 * (pos & 3));
-        hi[pos >> 2] |= ((uint32_t)h8 & 255u) << (8 * (pos & 3));
-        isum += qi;
+        qb[e] = __float_as_uint(fmaf(v[e], inv, 12583040.0f));      // 1.5 * 2^23 + 128
+        bsum += qb[e];
     }
+    // bytes (0, 1) of elements (a, b) -> [a.0, b.0, a.1, b.1]; then low and high digits of
+    // (even | odd) elements, even dims first within the 8-dim group
+    auto pair = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05010400u); };
+    const uint32_t t02 = pair(qb[0], qb[2]), t46 = pair(qb[4], qb[6]);
+    const uint32_t t13 = pair(qb[1], qb[3]), t57 = pair(qb[5], qb[7]);
+    const uint32_t lo0 = __builtin_amdgcn_perm(t46, t02, 0x05040100u) ^ 0x80808080u;
+    const uint32_t lo1 = __builtin_amdgcn_perm(t57, t13, 0x05040100u) ^ 0x80808080u;
+    const uint32_t hi0 = __builtin_amdgcn_perm(t46, t02, 0x07060302u);
+    const uint32_t hi1 = __builtin_amdgcn_perm(t57, t13, 0x07060302u);
+    int isum = (int)(bsum - 8u * 0x4B400080u);                        // sum of q_int
     isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR1, 0xF, 0xF, false);
     isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR2, 0xF, 0xF, false);
-    *(uint2*)&Q.qa[0][h][8 * g8] = make_uint2(lo[0], lo[1]);
-    *(uint2*)&Q.qa[1][h][8 * g8] = make_uint2(hi[0], hi[1]);
+    *(uint2*)&Q.qa[0][h][8 * g8] = make_uint2(lo0, lo1);
+    *(uint2*)&Q.qa[1][h][8 * g8] = make_uint2(hi0, hi1);
     if ((g8 & 3) == 0) {
-        Q.S[h][kb] = inv > 0.0f ? 1.0f / inv : 0.0f;
+        Q.S[h][kb] = amax * (1.0f / kQLim);
         Q.off[h][kb] = 8 * isum;
         Q.qsum[h][kb] = sum;
     }
@@ -301,7 +341,7 @@ __device__ __forceinline__ void lds_fwht4(float (*buf)[kD])
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
+__global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 {
     constexpr int KIND = fkind(FMT);
     constexpr bool KVARN = KIND == KIND_KVARN;
@@ -315,10 +355,12 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bid = blockIdx.x;
-    const int pr = wave & 1;                          // pair
-    // score waves are 0,1 in even workgroups and 2,3 in odd ones, so that every SIMD runs both
-    // roles (wave w of a workgroup runs on SIMD w)
-    const bool kwave = ((wave >> 1) ^ (bid & 1)) == 0;
+    // Wave w runs on SIMD w % 4.  In each group of four waves two are K waves and two V
+    // waves, on SIMDs (0, 1) and (2, 3) in even groups and the other way round in odd ones,
+    // so every SIMD runs two waves of each role; pair 2g + b = the waves b and b + 2 of group g.
+    const int wg4 = wave >> 2, w4 = wave & 3;
+    const int pr = 2 * wg4 + (w4 & 1);
+    const bool kwave = ((w4 >> 1) ^ (wg4 & 1)) == 0;
     int e = 0;
     for (int i = 1; i < a.n_seqs; ++i)
         if (a.seqs[i].wg_base <= bid) e = i;
@@ -336,31 +378,37 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     const char* kst = sptr(g, sq.seq, a.layer, head, 0);
     const char* vst = sptr(g, sq.seq, a.layer, head, 1);
 
-    for (int i = tid; i < kG * kD; i += blockDim.x) {
-        int hh = i / kD, d = i % kD;
-        int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + hh) * kD + d;
-        float qv = a.q_dtype ? ((const float*)a.q)[qi] : bf16_to_f32(((const uint16_t*)a.q)[qi]);
-        S.qs[hh][d] = qv * a.scale_log2;
-    }
-    __syncthreads();
-    if (KVARN && quant) {
-        lds_fwht4(S.qs);
-        for (int i = tid; i < kG * kD; i += blockDim.x) S.qs[i / kD][i % kD] *= (1.0f / 128.0f);
+    // The query of the group, scaled to the log2 domain (KVarN pages: rotated, H q / 128),
+    // into LDS.  Every role calls this once, after issuing its first loads, so that the
+    // transform runs while they are in flight.
+    auto load_query = [&]() {
+        for (int i = tid; i < kG * kD; i += blockDim.x) {
+            int hh = i / kD, d = i % kD;
+            int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + hh) * kD + d;
+            float qv = a.q_dtype ? ((const float*)a.q)[qi] : bf16_to_f32(((const uint16_t*)a.q)[qi]);
+            S.qs[hh][d] = qv * a.scale_log2;
+        }
         __syncthreads();
-    }
+        if (KVARN && quant) {
+            lds_fwht4(S.qs);
+            for (int i = tid; i < kG * kD; i += blockDim.x) S.qs[i / kD][i % kD] *= (1.0f / 128.0f);
+            __syncthreads();
+        }
+    };
 
-    // steps of each pair: the pair walks units u_lo + pr + 2i
+    // steps of each pair: the pair walks units u_lo + pr + kP i
     auto steps_of = [&](int p) -> int {
         const int uf = u_lo + p;
         if (uf >= u_hi) return 0;
-        const int nu = (u_hi - uf + 1) / 2;
+        const int nu = (u_hi - uf + kP - 1) / kP;
         if (!quant) return nu;
-        const int ul = uf + 2 * (nu - 1);
+        const int ul = uf + kP * (nu - 1);
         const int64_t len = min<int64_t>((int64_t)ul * kPage + kPage, sq.n_q) - (int64_t)ul * kPage;
         return 4 * (nu - 1) + (int)((len + 31) / 32);
     };
     const int J = steps_of(pr);
-    const int Jmax = max(steps_of(0), steps_of(1));
+    int Jmax = 0;
+    for (int p = 0; p < kP; ++p) Jmax = max(Jmax, steps_of(p));
     const int u_first = u_lo + pr;
 
     const int vg = lane >> 3, vp = lane & 7;          // V layout: pair slot (of 8), 16-dim part
@@ -399,10 +447,10 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         const char* kcodes = kst + g.k.codes;
         const char* kscales = kst + g.k.scales;
         const char* kchan = kst + g.k.cscale;
-        QMat& Q = S.qm[pr];
+        QMat* Qb = S.qm[pr];
         i32x4 A[2], Ci[2];
         float Sc[4], Qs[4];
-        auto load_a = [&]() {
+        auto load_a = [&](const QMat& Q) {
             const int m = n16, dig = m & 1, sel = (m >> 1) & 1, h = m >> 2;
 #pragma unroll
             for (int bp = 0; bp < 2; ++bp) {
@@ -423,7 +471,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB;
         auto kload = [&](int j, KLoad& L) {
             const int jj = j < J ? j : J - 1;
-            const int u = u_first + 2 * (jj >> 2);
+            const int u = u_first + kP * (jj >> 2);
             const int tb = u * kPage + 32 * (jj & 3);
             const int nv = min(32, min(u * kPage + kPage, nq) - tb);
             const rsrc_t rc = make_rsrc(kcodes + (int64_t)tb * 64, nv * 64);
@@ -441,31 +489,90 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             }
         };
         auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
-            const int nu = (u_hi - u_first + 1) / 2;
-            const int u = u_first + 2 * min(i, nu - 1);
+            const int nu = (u_hi - u_first + kP - 1) / kP;
+            const int u = u_first + kP * min(i, nu - 1);
             return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
         };
         float mh = kNeg;                           // running max of head q4
         float ls = 0.0f;                           // sum of p over the lane's tokens
         uint4 cnext = make_uint4(0u, 0u, 0u, 0u);
+        // three register stages, loads issued two steps ahead of their use
+        KLoad X, Y, Z;
+        if (J > 0) {
+            kload(0, X);
+            kload(1, Y);
+            kload(2, Z);
+            if (KVARN) cnext = chan_load(0);
+        }
+        // the lane's 8 query values (head lane >> 4, dims 8 (lane & 15) ..), log2 domain;
+        // KVarN: rotated, H q / 128 (spans 1, 2, 4 in the lane, 8 .. 64 across lanes)
+        float qv[8];
+        {
+            const int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + (lane >> 4)) * kD + 8 * n16;
+            if (a.q_dtype) {
+                const float4 x0 = *(const float4*)((const float*)a.q + qi);
+                const float4 x1 = *(const float4*)((const float*)a.q + qi + 4);
+                qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
+                qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
+            } else {
+                const uint4 w = *(const uint4*)((const uint16_t*)a.q + qi);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qv[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
+                    qv[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] *= a.scale_log2;
+            if (KVARN) {
+#pragma unroll
+                for (int sp = 1; sp < 8; sp <<= 1)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if ((e & sp) == 0) {
+                            const float x = qv[e], y = qv[e + sp];
+                            qv[e] = x + y;
+                            qv[e + sp] = x - y;
+                        }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bool up = (lane >> k) & 1;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float y = __shfl_xor(qv[e], 1 << k);
+                        qv[e] = up ? y - qv[e] : qv[e] + y;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[e] *= (1.0f / 128.0f);
+            }
+        }
         if (!KVARN) {
-            build_qmat<AFF>(Q, S.qs, nullptr, lane);
+            build_qmat<AFF>(Qb[0], qv, nullptr, lane);
             wave_sync_lds();
-            load_a();
+            load_a(Qb[0]);
         } else if (J > 0) {
-            cnext = chan_load(0);
+            // first page now; each later page's operand is built two steps before it starts
+            const uint4 cw = cnext;
+            cnext = chan_load(1);
+            build_qmat<false>(Qb[0], qv, &cw, lane);
+            wave_sync_lds();
+            load_a(Qb[0]);
         }
         auto kstep = [&](int j, const KLoad& L) __attribute__((always_inline)) {
-            const int u = u_first + 2 * (j >> 2);
+            const int u = u_first + kP * (j >> 2);
             const int t_page = u * kPage;
             const int t_end = min(t_page + kPage, nq);
-            if (KVARN && (j & 3) == 0) {
-                const uint4 cw = cnext;
+            if (KVARN && (j & 3) == 0 && j > 0) {
+                wave_sync_lds();
+                load_a(Qb[(j >> 2) & 1]);
                 cnext = chan_load((j >> 2) + 1);
-                wave_sync_lds();
-                build_qmat<false>(Q, S.qs, &cw, lane);
-                wave_sync_lds();
-                load_a();
+            }
+            if (KVARN && (j & 3) == 2) {
+                // the next page's operand into the other buffer (read at that page's start)
+                const uint4 cw = cnext;
+                build_qmat<false>(Qb[((j >> 2) + 1) & 1], qv, &cw, lane);
             }
             float sc[2];
 #pragma unroll
@@ -515,13 +622,6 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             if (n16 == 0) P.alpha[q4] = al;
             __syncthreads();
         };
-        // three register stages, loads issued two steps ahead of their use
-        KLoad X, Y, Z;
-        if (J > 0) {
-            kload(0, X);
-            kload(1, Y);
-            kload(2, Z);
-        }
         int j = 0;
 #pragma unroll 1
         for (; j + 2 < J; j += 3) {
@@ -560,7 +660,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         const int ve = (lane >> 2) * 128 + (lane & 3) * 16;      // even rows of the stage
         auto issue = [&](int j, int slot) {
             const int jj = j < J ? j : J - 1;
-            const int u = u_first + 2 * (jj >> 2);
+            const int u = u_first + kP * (jj >> 2);
             const int tb = u * kPage + 32 * (jj & 3);
             const int nv = min(32, min(u * kPage + kPage, nq) - tb);
             Stage& B = ring[slot];
@@ -743,6 +843,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
         // ========================= BF16 ring chunks (binary32) =========================
         // units of 32 tokens; a step is two halves of 16 tokens (8 lanes per token pair)
         const int R = g.ring_slots;
+        load_query();
         if (kwave) {
             float mh = kNeg;                           // running max of the lane's head kb
             float lsum = 0.0f;                         // sum of p of the lane's head
@@ -754,7 +855,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             int j = 0;
 #pragma unroll 1
             for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + 2 * j) * kTailUnit;
+                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
                 const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
                 const uint32_t tbm = (uint32_t)(tb % R);
                 float sc[2][kG][2];
@@ -833,7 +934,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
             int j = 0;
 #pragma unroll 1
             for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + 2 * j) * kTailUnit;
+                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
                 const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
                 const uint32_t tbm = (uint32_t)(tb % R);
                 const PBuf& P = S.pb[pr][j & 1];
@@ -888,10 +989,12 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
     float* part_out = a.partials + (int64_t)bid * kPartialFloats;
     for (int i = tid; i < kG * kD; i += blockDim.x) {
         const int h = i / kD, d = i % kD;
-        const float M = fmaxf(S.wm[0][h], S.wm[1][h]);
+        float M = S.wm[0][h];
+#pragma unroll
+        for (int p = 1; p < kP; ++p) M = fmaxf(M, S.wm[p][h]);
         float L = 0.0f, A = 0.0f;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
+        for (int p = 0; p < kP; ++p) {
             const float ew = __builtin_amdgcn_exp2f(S.wm[p][h] - M);
             L += S.wl[p][h] * ew;
             A += S.wacc[p][h][d] * ew;
@@ -904,7 +1007,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_ws(DecodeArgs a)
 template <int FMT>
 int launch_ws_fmt(const DecodeArgs& a, int n_wgs, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_decode_ws<FMT>, dim3(n_wgs), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_decode_ws<FMT>, dim3(n_wgs), dim3(kThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
@@ -912,7 +1015,7 @@ template <int FMT>
 int occ_ws()
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_ws<FMT>, 256, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_ws<FMT>, kThreads, 0) != hipSuccess) return 0;
     return n;
 }
 

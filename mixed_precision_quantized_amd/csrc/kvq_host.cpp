@@ -383,34 +383,43 @@ int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* se
         s.n_q = nq_at(c, seq_ids[i], layer);
         s.units_q = (int32_t)((s.n_q + kPage - 1) / kPage);
         s.units_t = (int32_t)((s.n - s.n_q + kTailUnit - 1) / kTailUnit);
-        total_units += (int64_t)H * (2 * s.units_q + s.units_t);
+        total_units += (int64_t)H * (4 * s.units_q + 5 * s.units_t);
         max_uq = std::max<int64_t>(max_uq, s.units_q);
         max_ut = std::max<int64_t>(max_ut, s.units_t);
     }
     // Balanced split, sized so that the whole grid is resident at once.  A 32-token ring
-    // unit (16 KB of BF16 rows, binary32 arithmetic) takes about twice the time of a 128-token
-    // quantized page, so ring workgroups get half as many units.
+    // unit (16 KB of BF16 rows, binary32 arithmetic) takes about 1.25 times as long as a
+    // 128-token quantized page, so ring workgroups get 0.8 as many units.
     int cus = device_cu_count();
     int per_cu = decode_wgs_per_cu(c->cfg.fmt_k, c->cfg.fmt_v, c->geom.group);
     if (cus <= 0 || per_cu <= 0) return KV_EDEVICE;
     const int64_t target = (int64_t)cus * per_cu;
-    int64_t upw = std::max<int64_t>(1, (total_units + 2 * target - 1) / (2 * target));
-    int64_t upw_t, wgs;
-    for (;;) {
-        upw_t = std::max<int64_t>(1, upw / 2);
-        wgs = 0;
+    int64_t upw = std::max<int64_t>(1, (total_units + 4 * target - 1) / (4 * target));
+    auto plan = [&](int64_t uq, int64_t ut) {
+        int64_t w = 0;
         for (int i = 0; i < n_seqs; ++i) {
             DecodeSeq& s = a.seqs[i];
             // quantized and ring units never share a workgroup: KVarN accumulates the
             // quantized values in the rotated domain, the ring values in the original one
-            s.splits_q = (int32_t)((s.units_q + upw - 1) / upw);
-            s.splits_t = (int32_t)((s.units_t + upw_t - 1) / upw_t);
-            s.wg_base = (int32_t)wgs;
-            wgs += (int64_t)H * (s.splits_q + s.splits_t);
+            s.splits_q = (int32_t)((s.units_q + uq - 1) / uq);
+            s.splits_t = (int32_t)((s.units_t + ut - 1) / ut);
+            s.wg_base = (int32_t)w;
+            w += (int64_t)H * (s.splits_q + s.splits_t);
         }
-        if (wgs <= target || (upw >= max_uq && upw_t >= max_ut)) break;
-        upw += std::max<int64_t>(1, upw / 16);
+        return w;
+    };
+    int64_t upw_t = 1, wgs = 0;
+    for (;;) {
+        // ring workgroups take 0.8 as many units, up to 0.9x when that saves a workgroup
+        bool fit = false;
+        const int64_t t_hi = std::max<int64_t>(1, (9 * upw + 9) / 10);
+        for (upw_t = std::max<int64_t>(1, 4 * upw / 5); upw_t <= t_hi; ++upw_t)
+            if (plan(upw, upw_t) <= target) { fit = true; break; }
+        if (!fit) upw_t = t_hi;
+        if (fit || (upw >= max_uq && upw_t >= max_ut)) break;
+        ++upw;
     }
+    wgs = plan(upw, upw_t);
     if (wgs > kMaxDecodeWGs) return KV_EUNSUPPORTED;
     a.units_per_wg = (int32_t)upw;
     a.units_per_wg_t = (int32_t)upw_t;
