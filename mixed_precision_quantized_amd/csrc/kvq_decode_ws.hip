@@ -1,33 +1,37 @@
 // kvq_decode_ws.hip -- fast decode attention for 4-bit caches (q4_0, q4_1, kvarn4), gfx950.
 //
 // Same work split as the generic kernel (kvq_decode.hip): 128-token quantized pages and
-// 32-token ring chunks, balanced splits, partial results merged by kvq_merge.hip.  Inside a
-// workgroup the waves specialize, so each role fits in 128 VGPRs and four waves share every
-// SIMD:
+// 32-token ring chunks, balanced splits, partial results merged by kvq_merge.hip.  One
+// workgroup of 16 waves per CU; inside it the waves specialize, so each role fits in 128
+// VGPRs and four waves share every SIMD:
 //
 //   "K waves"  score 32 tokens per step and run the online softmax;
 //   "V waves"  accumulate the values of the step the K waves finished before.
 //
-// A K wave and a V wave form a pair that walks every other unit of the workgroup; the pair
-// hands the probabilities of a step over through a double-buffered block of LDS, and the
-// whole workgroup takes one barrier per step.  Waves 0,1 are the K waves of even
-// workgroups and waves 2,3 those of odd ones, so every SIMD runs both roles.
+// A K wave and a V wave form a pair; the 8 pairs of a workgroup walk interleaved pages and
+// hand the probabilities of a step over through LDS, and the whole workgroup takes one
+// barrier per step, which keeps all 16 waves in lockstep (separate smaller workgroups
+// drift apart: the oldest wins instruction issue).  In each group of four waves the K
+// waves sit on SIMDs 0, 1 or 2, 3 alternately, so every SIMD runs both roles.
 //
 //  K: the query of each head is a 16-bit fixed-point vector per 32-dim block (scale
 //     S = max|q| / 30583) split into a low and a high signed byte; the scores of 16 tokens
-//     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (block, head, byte) and whose
-//     other operand is the unpacked code nibbles.  The integer dot products are exact; the
-//     code offset 8 and the per-(token, block) scale apply afterwards.  Codes and scales go
-//     to registers, three steps in flight.
+//     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (head, block, byte) and
+//     whose other operand is the unpacked code nibbles, so each lane scores one head of
+//     one token.  The integer dot products are exact; the accumulator starts at the code
+//     offset's share and the per-(token, block) scale applies afterwards.  Codes and
+//     scales go to registers, three steps in flight, through buffer loads that read rows
+//     past the end of a page as zero.
 //  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
 //     the binary16 weights p*d of the four heads, B = the centred codes u - 8 of one dim
 //     per column as exact binary16 integers (v_perm interleaves token pairs; 0x6400 | u is
-//     1024 + u, one v_pk_add_f16 centres two codes), K = the four tokens.  The V codes stream through a three-deep LDS ring
-//     filled by direct global-to-LDS loads, each issued at the end of the step two
-//     before its use.
+//     1024 + u, one v_pk_add_f16 centres two codes), K = the four tokens.  The V rows
+//     stream through a four-deep LDS ring filled by buffer loads straight to LDS, each
+//     issued at the end of the step three before its use.
 //  KVarN: keys are scored in the rotated domain with q'' = (H q / 128) * c_K of the page;
-//     values accumulate in the rotated domain scaled by the page's c_V and are rotated back
-//     once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard matrix).
+//     values accumulate in the rotated domain scaled by the page's c_V and are rotated
+//     back once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard
+//     matrix).
 //  Ring (BF16 tail) workgroups use the same pairing with binary32 arithmetic.
 #include <float.h>
 
