@@ -471,8 +471,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         // Codes and scales of one step, straight to registers through buffer loads whose
         // resource covers the step's valid tokens: rows past the end of the page read as zero
         // (their scores are masked).  Stages past the last step repeat it.
-        struct KLoad { uint2 c[2][2]; uint4 s[2]; };
+        // ch (KVarN): the key channel scales of the page after the step's page, loaded with the
+        // step's rows so that the waits the compiler places for them stay exact
+        struct KLoad { uint2 c[2][2]; uint4 s[2]; uint4 ch; };
         const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB;
+        auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
+            const int nu = (u_hi - u_first + kP - 1) / kP;
+            const int u = u_first + kP * min(i, nu - 1);
+            return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
+        };
         auto kload = [&](int j, KLoad& L) {
             const int jj = j < J ? j : J - 1;
             const int u = u_first + kP * (jj >> 2);
@@ -491,22 +498,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     L.s[T] = make_uint4(w.x, w.y, 0u, 0u);
                 }
             }
-        };
-        auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
-            const int nu = (u_hi - u_first + kP - 1) / kP;
-            const int u = u_first + kP * min(i, nu - 1);
-            return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
+            if (KVARN) L.ch = chan_load((jj >> 2) + 1);
         };
         float mh = kNeg;                           // running max of head q4
         float ls = 0.0f;                           // sum of p over the lane's tokens
-        uint4 cnext = make_uint4(0u, 0u, 0u, 0u);
+        uint4 cfirst = make_uint4(0u, 0u, 0u, 0u);
         // three register stages, loads issued two steps ahead of their use
         KLoad X, Y, Z;
         if (J > 0) {
+            if (KVARN) cfirst = chan_load(0);        // first, so that its wait is exact
             kload(0, X);
             kload(1, Y);
             kload(2, Z);
-            if (KVARN) cnext = chan_load(0);
         }
         // the lane's 8 query values (head lane >> 4, dims 8 (lane & 15) ..), log2 domain;
         // KVarN: rotated, H q / 128 (spans 1, 2, 4 in the lane, 8 .. 64 across lanes)
@@ -558,9 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             load_a(Qb[0]);
         } else if (J > 0) {
             // first page now; each later page's operand is built two steps before it starts
-            const uint4 cw = cnext;
-            cnext = chan_load(1);
-            build_qmat<false>(Qb[0], qv, &cw, lane);
+            build_qmat<false>(Qb[0], qv, &cfirst, lane);
             wave_sync_lds();
             load_a(Qb[0]);
         }
@@ -571,12 +572,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             if (KVARN && (j & 3) == 0 && j > 0) {
                 wave_sync_lds();
                 load_a(Qb[(j >> 2) & 1]);
-                cnext = chan_load((j >> 2) + 1);
             }
             if (KVARN && (j & 3) == 2) {
                 // the next page's operand into the other buffer (read at that page's start)
-                const uint4 cw = cnext;
-                build_qmat<false>(Qb[((j >> 2) + 1) & 1], qv, &cw, lane);
+                build_qmat<false>(Qb[((j >> 2) + 1) & 1], qv, &L.ch, lane);
             }
             float sc[2];
 #pragma unroll
