@@ -611,13 +611,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 for (int T = 0; T < 2; ++T)
                     if (t_page + 32 * (j & 3) + 16 * T + n16 >= t_end) sc[T] = kNeg;
             }
-            // running max of head q4 over the step (a 16-lane row)
-            const float x = row_max16(fmaxf(sc[0], sc[1]));
-            const float nm = fmaxf(mh, x);
-            const float al = __builtin_amdgcn_exp2f(mh - nm);     // exactly 1 if unchanged
-            mh = nm;
-            const float p0 = __builtin_amdgcn_exp2f(sc[0] - nm);
-            const float p1 = __builtin_amdgcn_exp2f(sc[1] - nm);
+            // running max of head q4 (a 16-lane row): once the first steps have set it, a new
+            // maximum is rare, so the row reduction and the rescale factor are only computed
+            // when some lane's score exceeds it (the result is the same either way)
+            float al = 1.0f;
+            if (__builtin_amdgcn_ballot_w64(fmaxf(sc[0], sc[1]) > mh)) {
+                const float nm = fmaxf(mh, row_max16(fmaxf(sc[0], sc[1])));
+                al = __builtin_amdgcn_exp2f(mh - nm);                // exactly 1 if unchanged
+                mh = nm;
+            }
+            const float p0 = __builtin_amdgcn_exp2f(sc[0] - mh);
+            const float p1 = __builtin_amdgcn_exp2f(sc[1] - mh);
             ls = fmaf(ls, al, p0 + p1);
             PBuf& P = S.pb[pr][j & 3];
             P.ph[q4][n16] = (_Float16)p0;
