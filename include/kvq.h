@@ -84,7 +84,7 @@ typedef struct {
     int32_t n_kv_heads;    /* >= 1 */
     int32_t n_q_heads;     /* multiple of n_kv_heads; n_q_heads / n_kv_heads <= 8 */
     int32_t head_dim;      /* must be 128 */
-    int32_t fmt_k, fmt_v;  /* kv_format of the key and value caches */
+    int32_t fmt_k, fmt_v;  /* kv_format of the key and value caches (may differ) */
     int32_t tail_tokens;   /* T: newest tokens kept in BF16 (0 = quantize everything) */
     int32_t n_seqs;        /* sequences (batch slots) held by the cache */
     int64_t max_tokens;    /* capacity per sequence, in tokens */

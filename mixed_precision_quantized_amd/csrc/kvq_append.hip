@@ -191,8 +191,9 @@ struct PageCount { __device__ int64_t operator()(const AppendSeq& s) const { ret
 
 // ------------------------------------------------------------------ qN / bf16 encoder
 // Lane work item: (layer, head, stream, token, block), token-fastest within a stream.
+// sv_sel: 0 or 1 encodes only the K or the V stream (their formats differ), 2 both.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_encode_q(AppendArgs a, int64_t tokens)
+__global__ __launch_bounds__(256) void k_encode_q(AppendArgs a, int64_t tokens, int sv_sel)
 {
     constexpr int N = fbits(FMT);
     constexpr int KIND = fkind(FMT);
@@ -201,8 +202,11 @@ __global__ __launch_bounds__(256) void k_encode_q(AppendArgs a, int64_t tokens)
     int64_t w = gid >> 2;
     const int64_t tg = w % tokens;
     w /= tokens;
-    const int sv = (int)(w & 1);
-    w >>= 1;
+    int sv = sv_sel;
+    if (sv_sel == 2) {
+        sv = (int)(w & 1);
+        w >>= 1;
+    }
     const int head = (int)(w % a.g.n_kv_heads);
     const int lrel = (int)(w / a.g.n_kv_heads);
     if (lrel >= a.layers_in) return;
@@ -450,12 +454,32 @@ inline int64_t total_of(const AppendArgs& a, int which)
 }
 
 template <int FMT>
-int launch_enc(const AppendArgs& a, int64_t tokens, hipStream_t st)
+int launch_enc(const AppendArgs& a, int64_t tokens, int sv_sel, hipStream_t st)
 {
-    int64_t lanes = 4 * tokens * 2 * a.g.n_kv_heads * (int64_t)a.layers_in;
+    int64_t lanes = 4 * tokens * (sv_sel == 2 ? 2 : 1) * a.g.n_kv_heads * (int64_t)a.layers_in;
     int64_t blocks = (lanes + 255) / 256;
-    hipLaunchKernelGGL(k_encode_q<FMT>, dim3((unsigned)blocks), dim3(256), 0, st, a, tokens);
+    hipLaunchKernelGGL(k_encode_q<FMT>, dim3((unsigned)blocks), dim3(256), 0, st, a, tokens, sv_sel);
     return (int)hipGetLastError();
+}
+
+int launch_enc_fmt(int fmt, const AppendArgs& a, int64_t tokens, int sv_sel, hipStream_t st)
+{
+    switch (fmt) {
+    case 0: return launch_enc<0>(a, tokens, sv_sel, st);
+    case 1: return launch_enc<1>(a, tokens, sv_sel, st);
+    case 2: return launch_enc<2>(a, tokens, sv_sel, st);
+    case 3: return launch_enc<3>(a, tokens, sv_sel, st);
+    case 4: return launch_enc<4>(a, tokens, sv_sel, st);
+    case 5: return launch_enc<5>(a, tokens, sv_sel, st);
+    case 6: return launch_enc<6>(a, tokens, sv_sel, st);
+    case 7: return launch_enc<7>(a, tokens, sv_sel, st);
+    case 8: return launch_enc<8>(a, tokens, sv_sel, st);
+    case 9: return launch_enc<9>(a, tokens, sv_sel, st);
+    case 10: return launch_enc<10>(a, tokens, sv_sel, st);
+    case 11: return launch_enc<11>(a, tokens, sv_sel, st);
+    case 12: return launch_enc<12>(a, tokens, sv_sel, st);
+    default: return (int)hipErrorInvalidValue;
+    }
 }
 
 template <int N>
@@ -473,23 +497,13 @@ int launch_append_encode(const AppendArgs& a, void* stream)
     int64_t tokens = total_of(a, 0);
     if (tokens <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
-    // K and V share one format (checked at init); a KVarN format never reaches here.
-    switch (a.g.fmt_k) {
-    case 0: return launch_enc<0>(a, tokens, st);
-    case 1: return launch_enc<1>(a, tokens, st);
-    case 2: return launch_enc<2>(a, tokens, st);
-    case 3: return launch_enc<3>(a, tokens, st);
-    case 4: return launch_enc<4>(a, tokens, st);
-    case 5: return launch_enc<5>(a, tokens, st);
-    case 6: return launch_enc<6>(a, tokens, st);
-    case 7: return launch_enc<7>(a, tokens, st);
-    case 8: return launch_enc<8>(a, tokens, st);
-    case 9: return launch_enc<9>(a, tokens, st);
-    case 10: return launch_enc<10>(a, tokens, st);
-    case 11: return launch_enc<11>(a, tokens, st);
-    case 12: return launch_enc<12>(a, tokens, st);
-    default: return (int)hipErrorInvalidValue;
-    }
+    // token-wise formats only; a KVarN stream is encoded page-wise (launch_append_kvarn)
+    const bool kq = fkind(a.g.fmt_k) != KIND_KVARN, vq = fkind(a.g.fmt_v) != KIND_KVARN;
+    if (kq && vq && a.g.fmt_k == a.g.fmt_v) return launch_enc_fmt(a.g.fmt_k, a, tokens, 2, st);
+    int rc = 0;
+    if (kq) rc = launch_enc_fmt(a.g.fmt_k, a, tokens, 0, st);
+    if (!rc && vq) rc = launch_enc_fmt(a.g.fmt_v, a, tokens, 1, st);
+    return rc;
 }
 
 int launch_append_kvarn(const AppendArgs& a, void* stream)
@@ -497,16 +511,24 @@ int launch_append_kvarn(const AppendArgs& a, void* stream)
     int64_t pages = total_of(a, 2);
     if (pages <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
-    int mask = (fkind(a.g.fmt_k) == KIND_KVARN ? 1 : 0) | (fkind(a.g.fmt_v) == KIND_KVARN ? 2 : 0);
-    switch (fbits(a.g.fmt_k)) {
-    case 2: return launch_kv<2>(a, pages, mask, st);
-    case 3: return launch_kv<3>(a, pages, mask, st);
-    case 4: return launch_kv<4>(a, pages, mask, st);
-    case 5: return launch_kv<5>(a, pages, mask, st);
-    case 6: return launch_kv<6>(a, pages, mask, st);
-    case 8: return launch_kv<8>(a, pages, mask, st);
-    default: return (int)hipErrorInvalidValue;
-    }
+    // one launch per code width: mask bit 0 = K stream, bit 1 = V stream
+    auto launch_n = [&](int fmt, int mask) -> int {
+        switch (fbits(fmt)) {
+        case 2: return launch_kv<2>(a, pages, mask, st);
+        case 3: return launch_kv<3>(a, pages, mask, st);
+        case 4: return launch_kv<4>(a, pages, mask, st);
+        case 5: return launch_kv<5>(a, pages, mask, st);
+        case 6: return launch_kv<6>(a, pages, mask, st);
+        case 8: return launch_kv<8>(a, pages, mask, st);
+        default: return (int)hipErrorInvalidValue;
+        }
+    };
+    const bool kk = fkind(a.g.fmt_k) == KIND_KVARN, vk = fkind(a.g.fmt_v) == KIND_KVARN;
+    if (kk && vk && a.g.fmt_k == a.g.fmt_v) return launch_n(a.g.fmt_k, 3);
+    int rc = 0;
+    if (kk) rc = launch_n(a.g.fmt_k, 1);
+    if (!rc && vk) rc = launch_n(a.g.fmt_v, 2);
+    return rc;
 }
 
 int launch_append_ring(const AppendArgs& a, void* stream)

@@ -128,6 +128,33 @@ __device__ __forceinline__ void ring16(const char* st, const StreamLayout& L, in
     }
 }
 
+// dequant16 for a format known only at run time (one uniform branch per row).
+__device__ __forceinline__ void dequant16_rt(int fmt, const char* st, const StreamLayout& L, int64_t t,
+                                             int part, const float (&crow)[16], float (&x)[16])
+{
+    switch (fmt) {
+    case 0: dequant16<0>(st, L, t, part, crow, x); break;
+    case 1: dequant16<1>(st, L, t, part, crow, x); break;
+    case 2: dequant16<2>(st, L, t, part, crow, x); break;
+    case 3: dequant16<3>(st, L, t, part, crow, x); break;
+    case 4: dequant16<4>(st, L, t, part, crow, x); break;
+    case 5: dequant16<5>(st, L, t, part, crow, x); break;
+    case 6: dequant16<6>(st, L, t, part, crow, x); break;
+    case 7: dequant16<7>(st, L, t, part, crow, x); break;
+    case 8: dequant16<8>(st, L, t, part, crow, x); break;
+    case 9: dequant16<9>(st, L, t, part, crow, x); break;
+    case 10: dequant16<10>(st, L, t, part, crow, x); break;
+    case 11: dequant16<11>(st, L, t, part, crow, x); break;
+    case 12: dequant16<12>(st, L, t, part, crow, x); break;
+    case 13: dequant16<13>(st, L, t, part, crow, x); break;
+    case 14: dequant16<14>(st, L, t, part, crow, x); break;
+    case 15: dequant16<15>(st, L, t, part, crow, x); break;
+    case 16: dequant16<16>(st, L, t, part, crow, x); break;
+    case 17: dequant16<17>(st, L, t, part, crow, x); break;
+    default: dequant16<18>(st, L, t, part, crow, x); break;
+    }
+}
+
 struct Online {
     float m[kG], l[kG], acc[kG][16];
 };
@@ -184,10 +211,14 @@ __device__ __forceinline__ void lds_fwht(float (*buf)[kD])
     __syncthreads();
 }
 
-template <int FMT>
+// FK: key format.  FV: value format, or -1 for "a.g.fmt_v, read at run time" (the kernel for
+// caches whose K and V formats differ).
+template <int FK, int FV>
 __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
 {
-    constexpr int KIND = fkind(FMT);
+    constexpr int KIND = fkind(FK);
+    const int fv = FV >= 0 ? FV : a.g.fmt_v;
+    const bool v_kvarn = fkind(fv) == KIND_KVARN;
     __shared__ float qs[kG][kD];
     __shared__ float wm[4][kG], wl[4][kG];
     __shared__ float wacc[4][kG][kD];
@@ -249,17 +280,22 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
             float ck[16], cv[16];
             if constexpr (KIND == KIND_KVARN) {
                 const uint16_t* cks = (const uint16_t*)(kst + g.k.cscale + (int64_t)u * 256) + 16 * part;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) ck[j] = fp16_to_f32(cks[j]);
+            }
+            if (v_kvarn) {
                 const uint16_t* cvs = (const uint16_t*)(vst + g.v.cscale + (int64_t)u * 256) + 16 * part;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) { ck[j] = fp16_to_f32(cks[j]); cv[j] = fp16_to_f32(cvs[j]); }
+                for (int j = 0; j < 16; ++j) cv[j] = fp16_to_f32(cvs[j]);
             }
             for (int64_t tb = t0; tb < t1; tb += 8) {
                 const int64_t t = tb + slot;
                 const bool valid = t < t1;
                 const int64_t tc = valid ? t : t1 - 1;
                 float k[16], v[16];
-                dequant16<FMT>(kst, g.k, tc, part, ck, k);
-                dequant16<FMT>(vst, g.v, tc, part, cv, v);
+                dequant16<FK>(kst, g.k, tc, part, ck, k);
+                if constexpr (FV >= 0) dequant16<FV>(vst, g.v, tc, part, cv, v);
+                else dequant16_rt(fv, vst, g.v, tc, part, cv, v);
                 online_step(o, qr, k, v, valid);
             }
         } else {
@@ -320,16 +356,18 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
 template <int FMT>
 int launch_fmt(const DecodeArgs& a, int n_wgs, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_decode<FMT>, dim3(n_wgs), dim3(256), 0, st, a);
+    if (a.g.fmt_v == FMT) hipLaunchKernelGGL((k_decode<FMT, FMT>), dim3(n_wgs), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_decode<FMT, -1>), dim3(n_wgs), dim3(256), 0, st, a);
     return (int)hipGetLastError();
 }
 
 template <int FMT>
-int occ_fmt()
+int occ_fmt(bool mixed)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT>, 256, 0) != hipSuccess) return 0;
-    return n;
+    hipError_t e = mixed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT, -1>, 256, 0)
+                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT, FMT>, 256, 0);
+    return e == hipSuccess ? n : 0;
 }
 
 }  // namespace
@@ -373,33 +411,34 @@ int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
 {
     (void)group;
     if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k);
-    static int cache[19] = {0};
-    if (fmt_k < 0 || fmt_k >= 19) return 0;
-    if (cache[fmt_k]) return cache[fmt_k];
+    static int cache[19][2] = {{0}};
+    if (fmt_k < 0 || fmt_k >= 19 || fmt_v < 0 || fmt_v >= 19) return 0;
+    const int mx = fmt_v != fmt_k ? 1 : 0;
+    if (cache[fmt_k][mx]) return cache[fmt_k][mx];
     int n = 0;
     switch (fmt_k) {
-    case 0: n = occ_fmt<0>(); break;
-    case 1: n = occ_fmt<1>(); break;
-    case 2: n = occ_fmt<2>(); break;
-    case 3: n = occ_fmt<3>(); break;
-    case 4: n = occ_fmt<4>(); break;
-    case 5: n = occ_fmt<5>(); break;
-    case 6: n = occ_fmt<6>(); break;
-    case 7: n = occ_fmt<7>(); break;
-    case 8: n = occ_fmt<8>(); break;
-    case 9: n = occ_fmt<9>(); break;
-    case 10: n = occ_fmt<10>(); break;
-    case 11: n = occ_fmt<11>(); break;
-    case 12: n = occ_fmt<12>(); break;
-    case 13: n = occ_fmt<13>(); break;
-    case 14: n = occ_fmt<14>(); break;
-    case 15: n = occ_fmt<15>(); break;
-    case 16: n = occ_fmt<16>(); break;
-    case 17: n = occ_fmt<17>(); break;
-    case 18: n = occ_fmt<18>(); break;
+    case 0: n = occ_fmt<0>(mx); break;
+    case 1: n = occ_fmt<1>(mx); break;
+    case 2: n = occ_fmt<2>(mx); break;
+    case 3: n = occ_fmt<3>(mx); break;
+    case 4: n = occ_fmt<4>(mx); break;
+    case 5: n = occ_fmt<5>(mx); break;
+    case 6: n = occ_fmt<6>(mx); break;
+    case 7: n = occ_fmt<7>(mx); break;
+    case 8: n = occ_fmt<8>(mx); break;
+    case 9: n = occ_fmt<9>(mx); break;
+    case 10: n = occ_fmt<10>(mx); break;
+    case 11: n = occ_fmt<11>(mx); break;
+    case 12: n = occ_fmt<12>(mx); break;
+    case 13: n = occ_fmt<13>(mx); break;
+    case 14: n = occ_fmt<14>(mx); break;
+    case 15: n = occ_fmt<15>(mx); break;
+    case 16: n = occ_fmt<16>(mx); break;
+    case 17: n = occ_fmt<17>(mx); break;
+    case 18: n = occ_fmt<18>(mx); break;
     default: break;
     }
-    cache[fmt_k] = n;
+    cache[fmt_k][mx] = n;
     return n;
 }
 

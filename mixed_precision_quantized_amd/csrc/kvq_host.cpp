@@ -103,8 +103,7 @@ int plan_config(const kv_config* cfg, CacheGeom* geom, int64_t* total, int64_t* 
     if (cfg->head_dim != kD) return KV_EUNSUPPORTED;
     int group = cfg->n_q_heads / cfg->n_kv_heads;
     if (group > kMaxGroup) return KV_EUNSUPPORTED;
-    // decode kernels are built for one format shared by K and V, and GQA groups of 4
-    if (cfg->fmt_k != cfg->fmt_v) return KV_EUNSUPPORTED;
+    // decode kernels are built for GQA groups of 4
     if (group != 4) return KV_EUNSUPPORTED;
     if (cfg->max_tokens > (int64_t(1) << 31) - kPage) return KV_EINVAL;
     int64_t g = granule_of(cfg->fmt_k, cfg->fmt_v);

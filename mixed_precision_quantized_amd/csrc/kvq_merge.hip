@@ -132,7 +132,7 @@ int launch_merge(const DecodeArgs& a, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
     const int n = a.n_seqs * a.g.n_kv_heads * kG;
-    if (fkind(a.g.fmt_k) == KIND_KVARN)
+    if (fkind(a.g.fmt_v) == KIND_KVARN)      // values accumulated in the rotated domain
         hipLaunchKernelGGL(k_merge<true>, dim3(n), dim3(kThreads), 0, st, a);
     else
         hipLaunchKernelGGL(k_merge<false>, dim3(n), dim3(kThreads), 0, st, a);

@@ -64,6 +64,16 @@ def canon_rows(wl, seq, layer, head, is_v, t0, t1) -> np.ndarray:
     return O.canon_bf16(x.numpy())
 
 
+def split_fmt(fmt: str):
+    """'q8_0/q4_0' -> ('q8_0', 'q4_0'): key and value formats; a single name is both."""
+    return tuple(fmt.split("/")) if "/" in fmt else (fmt, fmt)
+
+
+def make_cache(fmt: str, *args, **kw):
+    fk, fv = split_fmt(fmt)
+    return kvq.Cache(*args, fmt_k=fk, fmt_v=fv, **kw)
+
+
 def oracle_stream(fmt: str, rows: np.ndarray, n: int, n_q: int, R: int):
     """(codes, scales, cscale, ring) of one stream with n tokens and boundary n_q."""
     f = O.FORMAT_NAMES.index(fmt)
@@ -83,6 +93,7 @@ def compare_stream(cache, fmt, rows, seq, layer, head, is_v, what=""):
     """Byte-exact comparison of one stream against the oracle; returns n_q."""
     n, n_q = cache.seq_get(seq, layer)
     R = cache.layout(seq, layer, head, is_v)[1]
+    fmt = split_fmt(fmt)[1 if is_v else 0]
     oc, osc, ocs, oring = oracle_stream(fmt, rows, n, n_q, R)
     dc, dsc, dcs, dring = device_stream(cache, seq, layer, head, is_v)
     tag = "%s %s seq%d layer%d head%d %s" % (what, fmt, seq, layer, head, "V" if is_v else "K")
@@ -103,11 +114,12 @@ def compare_stream(cache, fmt, rows, seq, layer, head, is_v, what=""):
 
 
 def oracle_attention(fmt, krows, vrows, n, n_q, q_heads_vals, sigma):
-    """Binary64 attention of one (seq, layer, kv head) for its query heads."""
-    f = O.FORMAT_NAMES.index(fmt)
-    kq = O.encode_stream(f, n_q, krows)
-    vq = O.encode_stream(f, n_q, vrows)
-    return O.attention(n, n_q, f, f, kq, vq, krows[n_q:n], vrows[n_q:n], q_heads_vals, sigma)
+    """Binary64 attention of one (seq, layer, kv head) for its query heads; fmt is a
+    format name or a 'key/value' pair."""
+    fk, fv = (O.FORMAT_NAMES.index(x) for x in split_fmt(fmt))
+    kq = O.encode_stream(fk, n_q, krows)
+    vq = O.encode_stream(fv, n_q, vrows)
+    return O.attention(n, n_q, fk, fv, kq, vq, krows[n_q:n], vrows[n_q:n], q_heads_vals, sigma)
 
 
 def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:

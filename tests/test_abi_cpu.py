@@ -73,7 +73,11 @@ def test_format_table_matches_sizes():
 def test_config_validation():
     assert kvq.cache_bytes(cfg(D=64)) == kvq.KV_EUNSUPPORTED
     assert kvq.cache_bytes(cfg(QH=6, H=4)) == kvq.KV_EINVAL
-    assert kvq.cache_bytes(cfg(fk="q4_0", fv="q8_0")) == kvq.KV_EUNSUPPORTED
+    # K and V may use different formats: the cache holds one stream of each
+    mixed = kvq.cache_bytes(cfg(fk="q8_0", fv="q4_0"))
+    assert mixed > 0
+    assert kvq.cache_bytes(cfg(fk="q8_0", fv="q8_0")) > mixed > kvq.cache_bytes(cfg(fk="q4_0", fv="q4_0"))
+    assert kvq.cache_bytes(cfg(fk="kvarn4", fv="q4_0")) > 0
     assert kvq.cache_bytes(cfg(T=-1)) == kvq.KV_EINVAL
     assert kvq.cache_bytes(cfg(M=0)) == kvq.KV_EINVAL
     c = cfg()

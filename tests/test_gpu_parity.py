@@ -124,6 +124,31 @@ def test_every_format_small(fmt):
     _attn_check(cache, fmt, wl, 0, 1, [0, 1], n, q, out, 4)
 
 
+# Key and value formats may differ (keys are often kept at more bits): every pairing of
+# kinds, widths that differ, a KVarN stream beside a block or bf16 stream, and two KVarN
+# widths (whole pages for both streams as soon as one of them is KVarN).
+MIXED_PAIRS = ["q8_0/q4_0", "q4_0/q4_1", "q4_1/q4_0", "q6_1/q2_0", "bf16/q4_0", "q5_0/bf16",
+               "kvarn4/q4_0", "q4_0/kvarn4", "kvarn8/kvarn3", "kvarn4/q8_0", "q3_1/kvarn5",
+               "kvarn4/q4_1", "q4_1/kvarn4"]
+
+
+@pytest.mark.parametrize("fmt", MIXED_PAIRS)
+def test_mixed_key_value_formats_small(fmt):
+    """Same shape as the per-format test, with different key and value formats."""
+    wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
+    n, Tt = 1000, 200
+    cache = T.make_cache(fmt, 2, 2, 8, tail_tokens=Tt, n_seqs=1, max_tokens=1200)
+    T.fill(cache, wl, 0, [0, 1], 2, n, T.chunk_list(n, [333, 1, 250]))
+    torch.cuda.synchronize()
+    for layer in (0, 1):
+        for h in (0, 1):
+            _check_unit(cache, fmt, wl, 0, layer, h, n, None, 4)
+    q = T.query(wl, 0, 1, 0, 8, "cuda").unsqueeze(0)
+    out = cache.decode(1, [0], q)
+    torch.cuda.synchronize()
+    _attn_check(cache, fmt, wl, 0, 1, [0, 1], n, q, out, 4)
+
+
 @pytest.mark.parametrize("fmt", ["q4_0", "q3_1", "kvarn4"])
 def test_tail_covers_context_equals_bf16_attention(fmt):
     wl = "c2_sweep_ctx65536"
