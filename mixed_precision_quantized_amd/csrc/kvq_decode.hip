@@ -410,7 +410,7 @@ int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
 {
     (void)group;
-    if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k);
+    if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k, fmt_v);
     static int cache[19][2] = {{0}};
     if (fmt_k < 0 || fmt_k >= 19 || fmt_v < 0 || fmt_v >= 19) return 0;
     const int mx = fmt_v != fmt_k ? 1 : 0;

@@ -15,7 +15,7 @@
 // waves sit on SIMDs 0, 1 or 2, 3 alternately, so every SIMD runs both roles.
 //
 //  K: the query of each head is a 16-bit fixed-point vector per 32-dim block (scale
-//     S = max|q| / 30583) split into a low and a high signed byte; the scores of 16 tokens
+//     S = max|q| / 32639) split into a low and a high signed byte; the scores of 16 tokens
 //     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (head, block, byte) and
 //     whose other operand is the unpacked code nibbles, so each lane scores one head of
 //     one token.  The integer dot products are exact; the accumulator starts at the code
@@ -43,8 +43,7 @@ namespace {
 
 constexpr int kG = 4;
 constexpr float kNeg = -1.0e30f;
-constexpr float kQLim = 30583.0f;        // |q_int| bound so that q_int + 34952 fits 16 bits
-constexpr int kQBias = 34952;            // 8 * (1 + 16 + 256 + 4096): offset 8 in each digit
+constexpr float kQLim = 32639.0f;        // |q_int| bound: q_int + 128 fits a signed 16-bit word
 constexpr int kStages = 4;               // LDS ring depth per wave
 constexpr int kP = 8;                    // (K wave, V wave) pairs per workgroup
 constexpr int kThreads = 128 * kP;       // one workgroup per CU
@@ -228,8 +227,7 @@ struct alignas(16) PBuf {
 struct alignas(16) QMat {
     int8_t qa[2][kG][kD];    // [byte: lo, hi][head][permuted dim]
     float S[kG][4];          // [head][block] scale of q_int
-    int off[kG][4];          // [head][block] 8 * sum of q_int (symmetric formats)
-    float qsum[kG][4];       // [head][block] sum of the query (affine formats)
+    int off[kG][4];          // [head][block] 8 * sum of q_int
 };
 
 struct alignas(16) WsLds {
@@ -269,12 +267,11 @@ __device__ __forceinline__ float quad_max(float x)
 // Fixed-point query operand (one page or the whole split).  Lane = head h (lane >> 4) x
 // 8-dim group g8 (lane & 15); the four lanes of a quad hold one 32-dim block.  q: the lane's
 // 8 query values; cw: the 8 key channel scales of the group (KVarN) or null.
-//   q_int = round(q * inv), inv = 30583 / max|q| of the block, |q_int| <= 30583; one fma
+//   q_int = round(q * inv), inv = 32639 / max|q| of the block, |q_int| <= 32639; one fma
 //   with 1.5 * 2^23 + 128 leaves q_int + 128 in the low 16 bits of the result (the sum
 //   stays in [2^23, 2^24), where the float spacing is 1).  Its high byte is the signed high
 //   digit h8 and its low byte l8 + 128, so q_int = 256 h8 + l8 with l8 in [-128, 127]
 //   (flipping bit 7 of the low byte gives l8).
-template <bool AFFINE>
 __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const uint4* cw, int lane)
 {
     const int h = lane >> 4, g8 = lane & 15, kb = g8 >> 2;
@@ -290,13 +287,6 @@ __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const u
     amax = fmaxf(fmaxf(amax, fabsf(v[3])), fabsf(v[4]));
     amax = fmaxf(fmaxf(amax, fabsf(v[5])), fabsf(v[6]));
     amax = quad_max(fmaxf(amax, fabsf(v[7])));
-    float sum = 0.0f;
-    if (AFFINE) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += v[e];
-        sum += dpp<QP_XOR1>(sum);
-        sum += dpp<QP_XOR2>(sum);
-    }
     const float inv = amax > 0.0f ? kQLim * __builtin_amdgcn_rcpf(amax) : 0.0f;
     uint32_t qb[8];
     uint32_t bsum = 0u;
@@ -322,7 +312,6 @@ __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const u
     if ((g8 & 3) == 0) {
         Q.S[h][kb] = amax * (1.0f / kQLim);
         Q.off[h][kb] = 8 * isum;
-        Q.qsum[h][kb] = sum;
     }
 }
 
@@ -344,15 +333,15 @@ __device__ __forceinline__ void lds_fwht4(float (*buf)[kD])
     __syncthreads();
 }
 
-template <int FMT>
+// FK, FV: key and value formats (4-bit: q4_0, q4_1 or kvarn4, independently).
+template <int FK, int FV>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 {
-    constexpr int KIND = fkind(FMT);
-    constexpr bool KVARN = KIND == KIND_KVARN;
-    constexpr bool AFF = KIND == KIND_Q1;
-    constexpr int SB = AFF ? 16 : 8;                  // scale bytes per token row
-    constexpr int kLoads = 3 + (KVARN ? 1 : 0);      // load instructions per stage
-    static_assert(fbits(FMT) == 4, "4-bit formats only");
+    constexpr bool KVARN_K = fkind(FK) == KIND_KVARN, KVARN_V = fkind(FV) == KIND_KVARN;
+    constexpr bool AFF_K = fkind(FK) == KIND_Q1, AFF_V = fkind(FV) == KIND_Q1;
+    constexpr int SB_K = AFF_K ? 16 : 8, SB_V = AFF_V ? 16 : 8;   // scale bytes per token row
+    constexpr int kLoads = 3 + (KVARN_V ? 1 : 0);                   // V load instructions per stage
+    static_assert(fbits(FK) == 4 && fbits(FV) == 4, "4-bit formats only");
 
     __shared__ WsLds S;
 
@@ -393,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             S.qs[hh][d] = qv * a.scale_log2;
         }
         __syncthreads();
-        if (KVARN && quant) {
+        if (KVARN_K && quant) {
             lds_fwht4(S.qs);
             for (int i = tid; i < kG * kD; i += blockDim.x) S.qs[i / kD][i % kD] *= (1.0f / 128.0f);
             __syncthreads();
@@ -460,12 +449,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             for (int bp = 0; bp < 2; ++bp) {
                 const i32x4 z = {0, 0, 0, 0};
                 A[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[dig][h][32 * (2 * bp + sel) + 16 * (q4 & 1)] : z;
-                Ci[bp] = AFF ? z : (i32x4){-Q.off[q4][2 * bp], 0, -Q.off[q4][2 * bp + 1], 0};
+                Ci[bp] = AFF_K ? z : (i32x4){-Q.off[q4][2 * bp], 0, -Q.off[q4][2 * bp + 1], 0};
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 Sc[b] = Q.S[q4][b];
-                Qs[b] = AFF ? Q.qsum[q4][b] : 0.0f;
+                // affine keys: the sum of the rounded query, S * sum(q_int), so that the score
+                // is the rounded query against the dequantized key, d u + m, exactly; its
+                // error is then sum((q - q_hat) k), small where a block holds one outlier
+                // channel (the other keys are near 0, while d u - 8 d or d u are not)
+                Qs[b] = AFF_K ? Q.S[q4][b] * (float)(Q.off[q4][b] / 8) : 0.0f;
             }
         };
         // Codes and scales of one step, straight to registers through buffer loads whose
@@ -474,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         // ch (KVarN): the key channel scales of the page after the step's page, loaded with the
         // step's rows so that the waits the compiler places for them stay exact
         struct KLoad { uint2 c[2][2]; uint4 s[2]; uint4 ch; };
-        const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB;
+        const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB_K;
         auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
             const int nu = (u_hi - u_first + kP - 1) / kP;
             const int u = u_first + kP * min(i, nu - 1);
@@ -486,19 +479,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             const int tb = u * kPage + 32 * (jj & 3);
             const int nv = min(32, min(u * kPage + kPage, nq) - tb);
             const rsrc_t rc = make_rsrc(kcodes + (int64_t)tb * 64, nv * 64);
-            const rsrc_t rs = make_rsrc(kscales + (int64_t)tb * SB, nv * SB);
+            const rsrc_t rs = make_rsrc(kscales + (int64_t)tb * SB_K, nv * SB_K);
 #pragma unroll
             for (int T = 0; T < 2; ++T) {
 #pragma unroll
                 for (int bp = 0; bp < 2; ++bp) L.c[T][bp] = buf_load8(rc, cofs + 1024 * T + 32 * bp);
-                if (AFF) {
-                    L.s[T] = buf_load16(rs, sofs + 16 * SB * T);
+                if (AFF_K) {
+                    L.s[T] = buf_load16(rs, sofs + 16 * SB_K * T);
                 } else {
-                    const uint2 w = buf_load8(rs, sofs + 16 * SB * T);
+                    const uint2 w = buf_load8(rs, sofs + 16 * SB_K * T);
                     L.s[T] = make_uint4(w.x, w.y, 0u, 0u);
                 }
             }
-            if (KVARN) L.ch = chan_load((jj >> 2) + 1);
+            if (KVARN_K) L.ch = chan_load((jj >> 2) + 1);
         };
         float mh = kNeg;                           // running max of head q4
         float ls = 0.0f;                           // sum of p over the lane's tokens
@@ -506,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         // three register stages, loads issued two steps ahead of their use
         KLoad X, Y, Z;
         if (J > 0) {
-            if (KVARN) cfirst = chan_load(0);        // first, so that its wait is exact
+            if (KVARN_K) cfirst = chan_load(0);        // first, so that its wait is exact
             kload(0, X);
             kload(1, Y);
             kload(2, Z);
@@ -532,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) qv[e] *= a.scale_log2;
-            if (KVARN) {
+            if (KVARN_K) {
 #pragma unroll
                 for (int sp = 1; sp < 8; sp <<= 1)
 #pragma unroll
@@ -555,13 +548,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 for (int e = 0; e < 8; ++e) qv[e] *= (1.0f / 128.0f);
             }
         }
-        if (!KVARN) {
-            build_qmat<AFF>(Qb[0], qv, nullptr, lane);
+        if (!KVARN_K) {
+            build_qmat(Qb[0], qv, nullptr, lane);
             wave_sync_lds();
             load_a(Qb[0]);
         } else if (J > 0) {
             // first page now; each later page's operand is built two steps before it starts
-            build_qmat<false>(Qb[0], qv, &cfirst, lane);
+            build_qmat(Qb[0], qv, &cfirst, lane);
             wave_sync_lds();
             load_a(Qb[0]);
         }
@@ -569,13 +562,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             const int u = u_first + kP * (j >> 2);
             const int t_page = u * kPage;
             const int t_end = min(t_page + kPage, nq);
-            if (KVARN && (j & 3) == 0 && j > 0) {
+            if (KVARN_K && (j & 3) == 0 && j > 0) {
                 wave_sync_lds();
                 load_a(Qb[(j >> 2) & 1]);
             }
-            if (KVARN && (j & 3) == 2) {
+            if (KVARN_K && (j & 3) == 2) {
                 // the next page's operand into the other buffer (read at that page's start)
-                build_qmat<false>(Qb[((j >> 2) + 1) & 1], qv, &L.ch, lane);
+                build_qmat(Qb[((j >> 2) + 1) & 1], qv, &L.ch, lane);
             }
             float sc[2];
 #pragma unroll
@@ -590,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     const int t0 = (C.y << 8) + C.x, t1 = (C.w << 8) + C.z;
                     // block scales as binary16 operands of v_fma_mix (no conversion)
                     uint32_t w0, w1;
-                    if (AFF) {
+                    if (AFF_K) {
                         w0 = bp ? L.s[T].z : L.s[T].x;
                         w1 = bp ? L.s[T].w : L.s[T].y;
                         acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
@@ -674,13 +667,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             const rsrc_t rc = make_rsrc(cbase + (int64_t)tb * 64, nv * 64);
             lds_buf16(rc, ve, B.codes);
             lds_buf16(rc, ve + 64, B.codes + 1024);
-            const rsrc_t rs = make_rsrc(sbase + (int64_t)tb * SB, nv * SB);
-            if (AFF) {
+            const rsrc_t rs = make_rsrc(sbase + (int64_t)tb * SB_V, nv * SB_V);
+            if (AFF_V) {
                 if (lane < 32) lds_buf16(rs, 16 * lane, B.scales);
             } else {
                 lds_buf4(rs, 4 * lane, B.scales);
             }
-            if (KVARN) {
+            if (KVARN_V) {
                 if (lane < 16) lds_buf16(make_rsrc(chbase + (int64_t)u * 256, 256), 16 * lane, B.chan);
             }
         };
@@ -738,7 +731,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 ms *= al[vj];
                 msd *= al[vj];
             }
-            if (KVARN && page_start) {
+            if (KVARN_V && page_start) {
                 // this page's value channel scales: move the accumulator to them (it is zero
                 // before the first page, so the first move is inert)
                 const uint4 c = *(const uint4*)(B.chan + 32 * vblk + 8 * vj);
@@ -762,13 +755,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
                 const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
                 const _Float16* sc16 = (const _Float16*)B.scales;
-                constexpr int SW = SB / 2;                   // binary16 words per scale row
-                const int so = (AFF ? 2 : 1) * vblk;
+                constexpr int SW = SB_V / 2;                   // binary16 words per scale row
+                const int so = (AFF_V ? 2 : 1) * vblk;
                 const half2_t d01 = {sc16[SW * (2 * s0) + so], sc16[SW * (2 * s0 + 1) + so]};
                 const half2_t d23 = {sc16[SW * (2 * s1) + so], sc16[SW * (2 * s1 + 1) + so]};
                 const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * d01);
                 const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * d23);
-                if (AFF) {
+                if (AFF_V) {
                     const half2_t m01 = {sc16[SW * (2 * s0) + so + 1], sc16[SW * (2 * s0 + 1) + so + 1]};
                     const half2_t m23 = {sc16[SW * (2 * s1) + so + 1], sc16[SW * (2 * s1 + 1) + so + 1]};
                     msd = __builtin_amdgcn_fdot2(p01, d01, msd, false);
@@ -838,8 +831,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 f32x4 v = (r & 1) ? D[r] * 0.0625f : D[r];     // odd dims carried a factor 16
-                if (AFF) v += mh4;
-                if (KVARN) v *= cvr[r];
+                if (AFF_V) v += mh4;
+                if (KVARN_V) v *= cvr[r];
 #pragma unroll
                 for (int h = 0; h < kG; ++h) S.wacc[pr][h][32 * vblk + 8 * vj + r] = v[h];
             }
@@ -1011,52 +1004,77 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
     }
 }
 
-template <int FMT>
-int launch_ws_fmt(const DecodeArgs& a, int n_wgs, hipStream_t st)
+template <int FK, int FV>
+int launch_ws_pair(const DecodeArgs& a, int n_wgs, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_decode_ws<FMT>, dim3(n_wgs), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_decode_ws<FK, FV>), dim3(n_wgs), dim3(kThreads), 0, st, a);
     return (int)hipGetLastError();
 }
 
-template <int FMT>
+template <int FK, int FV>
 int occ_ws()
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_ws<FMT>, kThreads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_ws<FK, FV>, kThreads, 0) != hipSuccess) return 0;
     return n;
+}
+
+// index of a fast format: q4_0, q4_1, kvarn4
+int fast_index(int fmt) { return fmt == 5 ? 0 : fmt == 6 ? 1 : fmt == 15 ? 2 : -1; }
+
+template <int FK>
+int launch_fk(int fmt_v, const DecodeArgs& a, int n_wgs, hipStream_t st)
+{
+    switch (fmt_v) {
+    case 5: return launch_ws_pair<FK, 5>(a, n_wgs, st);
+    case 6: return launch_ws_pair<FK, 6>(a, n_wgs, st);
+    case 15: return launch_ws_pair<FK, 15>(a, n_wgs, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <int FK>
+int occ_fk(int fmt_v)
+{
+    switch (fmt_v) {
+    case 5: return occ_ws<FK, 5>();
+    case 6: return occ_ws<FK, 6>();
+    case 15: return occ_ws<FK, 15>();
+    default: return 0;
+    }
 }
 
 }  // namespace
 
 bool decode_fast_supported(int fmt_k, int fmt_v)
 {
-    return fmt_k == fmt_v && (fmt_k == 5 || fmt_k == 6 || fmt_k == 15);
+    return fast_index(fmt_k) >= 0 && fast_index(fmt_v) >= 0;
 }
 
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
     switch (a.g.fmt_k) {
-    case 5: return launch_ws_fmt<5>(a, n_wgs, st);
-    case 6: return launch_ws_fmt<6>(a, n_wgs, st);
-    case 15: return launch_ws_fmt<15>(a, n_wgs, st);
+    case 5: return launch_fk<5>(a.g.fmt_v, a, n_wgs, st);
+    case 6: return launch_fk<6>(a.g.fmt_v, a, n_wgs, st);
+    case 15: return launch_fk<15>(a.g.fmt_v, a, n_wgs, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
 
-int decode_fast_wgs_per_cu(int fmt)
+int decode_fast_wgs_per_cu(int fmt_k, int fmt_v)
 {
-    static int cache[19] = {0};
-    if (fmt < 0 || fmt >= 19) return 0;
-    if (!cache[fmt]) {
-        switch (fmt) {
-        case 5: cache[fmt] = occ_ws<5>(); break;
-        case 6: cache[fmt] = occ_ws<6>(); break;
-        case 15: cache[fmt] = occ_ws<15>(); break;
-        default: return 0;
+    static int cache[3][3] = {{0}};
+    const int ik = fast_index(fmt_k), iv = fast_index(fmt_v);
+    if (ik < 0 || iv < 0) return 0;
+    if (!cache[ik][iv]) {
+        switch (fmt_k) {
+        case 5: cache[ik][iv] = occ_fk<5>(fmt_v); break;
+        case 6: cache[ik][iv] = occ_fk<6>(fmt_v); break;
+        default: cache[ik][iv] = occ_fk<15>(fmt_v); break;
         }
     }
-    return cache[fmt];
+    return cache[ik][iv];
 }
 
 }  // namespace kvq

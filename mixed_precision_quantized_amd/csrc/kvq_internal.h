@@ -112,7 +112,7 @@ int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of t
 // 4-bit fast path (kvq_decode_ws.hip), used by launch_decode when it applies.
 bool decode_fast_supported(int fmt_k, int fmt_v);
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream);
-int decode_fast_wgs_per_cu(int fmt);
+int decode_fast_wgs_per_cu(int fmt_k, int fmt_v);
 bool decode_generic_forced();
 int device_cu_count();
 

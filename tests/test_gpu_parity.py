@@ -149,6 +149,26 @@ def test_mixed_key_value_formats_small(fmt):
     _attn_check(cache, fmt, wl, 0, 1, [0, 1], n, q, out, 4)
 
 
+FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4_1", "q4_1/kvarn4"]
+
+
+@pytest.mark.parametrize("fmt", FAST_PAIRS)
+def test_fast_kernel_mixed_pairs_many_pages(fmt):
+    """The 4-bit kernel with different key and value formats: 8 KV heads, 24k tokens (many
+    pages per pair of waves, a partial last page, a 1024-token tail), all heads checked."""
+    wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
+    n, Tt = 24000, 1024
+    cache = T.make_cache(fmt, 1, 8, 32, tail_tokens=Tt, n_seqs=1, max_tokens=n)
+    T.fill(cache, wl, 0, [0], 8, n, T.chunk_list(n, [7001, 1, 5000]))
+    torch.cuda.synchronize()
+    for h in (0, 7):
+        _check_unit(cache, fmt, wl, 0, 0, h, n, None, 4)
+    q = T.query(wl, 0, 0, 0, 32, "cuda").unsqueeze(0)
+    out = cache.decode(0, [0], q)
+    torch.cuda.synchronize()
+    _attn_check(cache, fmt, wl, 0, 0, range(8), n, q, out, 4)
+
+
 @pytest.mark.parametrize("fmt", ["q4_0", "q3_1", "kvarn4"])
 def test_tail_covers_context_equals_bf16_attention(fmt):
     wl = "c2_sweep_ctx65536"
