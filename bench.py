@@ -61,7 +61,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--fmt", default="kvarn4")
+    p.add_argument("--fmt", default="kvarn4", help="cache format, or KEY/VALUE formats (e.g. q8_0/q4_0)")
     p.add_argument("--ctx", type=int, default=240000)
     p.add_argument("--layers", type=int, default=64)
     p.add_argument("--tail", type=int, default=2048)
@@ -80,10 +80,17 @@ def stream_bytes(fmt):
     return cb + sb + pb / 128.0
 
 
+def split_fmt(fmt):
+    """'q8_0/q4_0' -> ('q8_0', 'q4_0'); a single name is both streams' format."""
+    fk, _, fv = fmt.partition("/")
+    return fk, fv or fk
+
+
 def decode_bytes_layer(fmt, n, n_q, heads):
     """Algorithmic bytes of one decode launch: every quantized row of K and V (codes,
     block scales, amortized channel scales) plus every BF16 ring row, read once."""
-    return heads * (n_q * 2 * stream_bytes(fmt) + (n - n_q) * 2 * 256)
+    fk, fv = split_fmt(fmt)
+    return heads * (n_q * (stream_bytes(fk) + stream_bytes(fv)) + (n - n_q) * 2 * 256)
 
 
 def copy_probe(nbytes):
@@ -119,8 +126,8 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
     import numpy as np
     import oracle as O
     from mixed_precision_quantized_amd import synth
-    f = O.FORMAT_NAMES.index(fmt)
-    G = O.granule(f, f)
+    fk, fv = (O.FORMAT_NAMES.index(x) for x in split_fmt(fmt))
+    G = O.granule(fk, fv)
     n_q = O.nq_after(0, ctx, tail, G)
     cores = min(units, os.cpu_count() or 1, 16)
     units = cores
@@ -135,14 +142,14 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
 
     def enc(i):
         k, v = data[i][0], data[i][1]
-        data[i][2] = O.encode_stream(f, n_q, k)
-        data[i][3] = O.encode_stream(f, n_q, v)
+        data[i][2] = O.encode_stream(fk, n_q, k)
+        data[i][3] = O.encode_stream(fv, n_q, v)
 
     def att(i):
         layer, h = work[i]
         k, v, kq, vq = data[i]
         q = synth.q_rows(wl, 0, layer, 0, 32)[4 * h: 4 * h + 4].double().numpy()
-        O.attention(ctx, n_q, f, f, kq, vq, k[n_q:], v[n_q:], q, 1.0 / math.sqrt(128))
+        O.attention(ctx, n_q, fk, fv, kq, vq, k[n_q:], v[n_q:], q, 1.0 / math.sqrt(128))
 
     def run(fn):
         ths = [threading.Thread(target=fn, args=(i,)) for i in range(units)]
@@ -186,7 +193,8 @@ def main():
     extra = warm + steps + args.append_chunk * args.append_reps + 256
     print("bench: %s, %d layers, ctx %d, tail %d, %s" % (args.fmt, L, args.ctx, args.tail,
           torch.cuda.get_device_name(0)), file=sys.stderr, flush=True)
-    cache = kvq.Cache(L, H, QH, args.fmt, tail_tokens=args.tail, n_seqs=1, max_tokens=args.ctx + extra)
+    fk, fv = split_fmt(args.fmt)
+    cache = kvq.Cache(L, H, QH, fmt_k=fk, fmt_v=fv, tail_tokens=args.tail, n_seqs=1, max_tokens=args.ctx + extra)
     t0 = time.time()
     fill_cache(cache, wl, L, H, args.ctx)
     torch.cuda.synchronize()

@@ -25,6 +25,10 @@ UNITS = [
     ("kvq_append.hip", ["-ffp-contract=off"]),
     ("kvq_decode.hip", []),
     ("kvq_decode_ws.hip", []),
+    ("kvq_decode_ws_k2.hip", []),
+    ("kvq_decode_ws_k3.hip", []),
+    ("kvq_decode_ws_k4.hip", []),
+    ("kvq_decode_ws_k8.hip", []),
     ("kvq_merge.hip", []),
     ("kvq_debug.hip", ["-ffp-contract=off"]),
 ]
@@ -40,7 +44,7 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every translation unit and link libkvq.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     objs = []

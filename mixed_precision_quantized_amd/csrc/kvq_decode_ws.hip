@@ -1,1046 +1,30 @@
-// kvq_decode_ws.hip -- fast decode attention for 4-bit caches (q4_0, q4_1, kvarn4), gfx950.
-//
-// Same work split as the generic kernel (kvq_decode.hip): 128-token quantized pages and
-// 32-token ring chunks, balanced splits, partial results merged by kvq_merge.hip.  One
-// workgroup of 16 waves per CU; inside it the waves specialize, so each role fits in 128
-// VGPRs and four waves share every SIMD:
-//
-//   "K waves"  score 32 tokens per step and run the online softmax;
-//   "V waves"  accumulate the values of the step the K waves finished before.
-//
-// A K wave and a V wave form a pair; the 8 pairs of a workgroup walk interleaved pages and
-// hand the probabilities of a step over through LDS, and the whole workgroup takes one
-// barrier per step, which keeps all 16 waves in lockstep (separate smaller workgroups
-// drift apart: the oldest wins instruction issue).  In each group of four waves the K
-// waves sit on SIMDs 0, 1 or 2, 3 alternately, so every SIMD runs both roles.
-//
-//  K: the query of each head is a 16-bit fixed-point vector per 32-dim block (scale
-//     S = max|q| / 32639) split into a low and a high signed byte; the scores of 16 tokens
-//     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (head, block, byte) and
-//     whose other operand is the unpacked code nibbles, so each lane scores one head of
-//     one token.  The integer dot products are exact; the accumulator starts at the code
-//     offset's share and the per-(token, block) scale applies afterwards.  Codes and
-//     scales go to registers, three steps in flight, through buffer loads that read rows
-//     past the end of a page as zero.
-//  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
-//     the binary16 weights p*d of the four heads, B = the centred codes u - 8 of one dim
-//     per column as exact binary16 integers (v_perm interleaves token pairs; 0x6400 | u is
-//     1024 + u, one v_pk_add_f16 centres two codes), K = the four tokens.  The V rows
-//     stream through a four-deep LDS ring filled by buffer loads straight to LDS, each
-//     issued at the end of the step three before its use.
-//  KVarN: keys are scored in the rotated domain with q'' = (H q / 128) * c_K of the page;
-//     values accumulate in the rotated domain scaled by the page's c_V and are rotated
-//     back once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard
-//     matrix).
-//  Ring (BF16 tail) workgroups use the same pairing with binary32 arithmetic.
-#include <float.h>
-
+// kvq_decode_ws.hip -- dispatch of the fast decode kernel (kvq_decode_ws.h) by key width.
 #include "kvq_device.h"
 
 namespace kvq {
 
+int decode_fast_w2(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+int decode_fast_w3(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+int decode_fast_w4(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+int decode_fast_w8(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+
 namespace {
 
-constexpr int kG = 4;
-constexpr float kNeg = -1.0e30f;
-constexpr float kQLim = 32639.0f;        // |q_int| bound: q_int + 128 fits a signed 16-bit word
-constexpr int kStages = 4;               // LDS ring depth per wave
-constexpr int kP = 8;                    // (K wave, V wave) pairs per workgroup
-constexpr int kThreads = 128 * kP;       // one workgroup per CU
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ const char* sptr(const CacheGeom& g, int seq, int layer, int head, int isv)
+// formats of the fast kernel: qN_0, qN_1 and kvarnN for N = 2, 3, 4, 8
+bool fast_format(int f)
 {
-    int64_t unit = ((int64_t)seq * g.n_layers + layer) * g.n_kv_heads + head;
-    return g.base + unit * g.unit_bytes + (isv ? g.v_offset : 0);
+    return f >= 1 && f <= 18 && fkind(f) != KIND_BF16 &&
+           (fbits(f) == 2 || fbits(f) == 3 || fbits(f) == 4 || fbits(f) == 8);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x)
+int by_width(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-constexpr int QP_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int QP_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int ROW_ROR1 = 0x121;     // row_ror:1
-constexpr int ROW_ROR2 = 0x122;     // row_ror:2
-constexpr int ROW_ROR4 = 0x124;     // row_ror:4
-constexpr int ROW_ROR8 = 0x128;     // row_ror:8
-constexpr int ROW_HMIRROR = 0x141;  // row_half_mirror
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b)
-{
-    half2_t v = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
-{
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
-}
-
-// reduction over lanes with equal (lane & 3)
-__device__ __forceinline__ float wave_max16(float x)
-{
-    x = fmaxf(x, dpp<ROW_ROR4>(x));
-    x = fmaxf(x, dpp<ROW_ROR8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float wave_sum16(float x)
-{
-    x += dpp<ROW_ROR4>(x);
-    x += dpp<ROW_ROR8>(x);
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
-}
-// reduction over lanes with equal (lane & 7)
-__device__ __forceinline__ float wave_max8(float x)
-{
-    x = fmaxf(x, dpp<ROW_ROR8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
-}
-__device__ __forceinline__ float wave_sum8(float x)
-{
-    x += dpp<ROW_ROR8>(x);
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
-}
-
-// Direct global -> LDS loads: lane l writes its 16 (or 4) bytes at lds + 16 l (4 l).
-// Issued from inline assembly so that the compiler does not attach a full vmcnt(0) wait to
-// every later LDS read (it cannot tell which ring slot a load targets); the ring's waits are
-// explicit (wait_vmcnt).  The assembly writes no VGPR (the data goes to LDS), sets M0 to the
-// wave-uniform LDS address in the same block, and the address VGPRs are read at issue.
-__device__ __forceinline__ uint32_t lds_addr(const void* p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void lds_load16(const void* gsrc, const void* lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off\n\ts_nop 0"
-                 :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load4(const void* gsrc, const void* lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off\n\ts_nop 0"
-                 :: "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N) only (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void wave_sync_lds()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Raw buffer resource over [p, p + bytes): loads at or past `bytes` return zero, so a
-// step's loads need no clamping of rows past the end of a page.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ uint2 buf_load8(rsrc_t r, int off)
-{
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, int off)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// Buffer loads straight to LDS (lane l writes at lds + 16 l, or 4 l); like lds_load16, the
-// waits are explicit.
-__device__ __forceinline__ void lds_buf16(rsrc_t r, int voff, const void* lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_nop 0"
-                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
-}
-__device__ __forceinline__ void lds_buf4(rsrc_t r, int voff, const void* lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds\n\ts_nop 0"
-                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds))) : "memory", "m0");
-}
-
-__device__ __forceinline__ _Float16 lo_half(uint32_t w)
-{
-    return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-}
-__device__ __forceinline__ _Float16 hi_half(uint32_t w)
-{
-    return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
-
-// Maximum over the 16 lanes of a DPP row, in every lane of the row: four v_max_f32 with a
-// row rotation on the first operand (each preceded by the two wait states a DPP read of a
-// just-written VGPR needs).  Finite inputs only.
-__device__ __forceinline__ float row_max16(float x)
-{
-    asm volatile("s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
-                 : "+v"(x));
-    return x;
-}
-
-// One 32-token step of one stream in LDS.  Code rows are stored even tokens first
-// (rows 0..15 = tokens 0,2,..,30) then odd tokens (rows 16..31), so both the score lanes
-// (16 bytes of one token) and the value lanes (8 bytes of one token) read without bank
-// conflicts; block-scale rows are in token order.
-struct alignas(16) Stage {
-    uint8_t codes[32 * 64];
-    uint8_t scales[32 * 16];
-    uint16_t chan[128];
-};
-
-struct alignas(16) PBuf {
-    union {
-        float p[kG][32];     // [head][token of the step] probabilities of the step (ring)
-        _Float16 ph[kG][32]; // the same in binary16 (quantized pages)
-    };
-    float alpha[4];          // accumulator rescale of the step (running max grew)
-    float pad[4];
-};
-
-// Query operand of the score MFMA for one pair: 16-bit fixed-point query per (head, 32-dim
-// block) split into a low and a high signed byte, q_int = 256 hi + lo, the dims of every
-// 8-dim group stored even dims first (the order in which the code nibbles unpack).
-struct alignas(16) QMat {
-    int8_t qa[2][kG][kD];    // [byte: lo, hi][head][permuted dim]
-    float S[kG][4];          // [head][block] scale of q_int
-    int off[kG][4];          // [head][block] 8 * sum of q_int
-};
-
-struct alignas(16) WsLds {
-    float qs[kG][kD];
-    Stage st[kP][kStages];   // LDS rings of the value waves
-    PBuf pb[kP][4];          // [pair][step % 4]
-    QMat qm[kP][2];          // [pair][page parity] (KVarN builds the next page's ahead)
-    float wm[kP][kG], wl[kP][kG];
-    float wacc[kP][kG][kD];  // slot-summed value accumulators of the pairs
-};
-
-// x * (binary16 half of w), one v_fma_mix_f32 (no separate conversion).
-__device__ __forceinline__ float mul_lo16(float x, uint32_t w)
-{
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-    return r;
-}
-__device__ __forceinline__ float mul_hi16(float x, uint32_t w)
-{
-    float r;
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-    return r;
-}
-
-// Maximum over the four lanes of a DPP quad (finite inputs).
-__device__ __forceinline__ float quad_max(float x)
-{
-    asm volatile("s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-                 "s_nop 1\n\t"
-                 "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
-                 : "+v"(x));
-    return x;
-}
-
-// Fixed-point query operand (one page or the whole split).  Lane = head h (lane >> 4) x
-// 8-dim group g8 (lane & 15); the four lanes of a quad hold one 32-dim block.  q: the lane's
-// 8 query values; cw: the 8 key channel scales of the group (KVarN) or null.
-//   q_int = round(q * inv), inv = 32639 / max|q| of the block, |q_int| <= 32639; one fma
-//   with 1.5 * 2^23 + 128 leaves q_int + 128 in the low 16 bits of the result (the sum
-//   stays in [2^23, 2^24), where the float spacing is 1).  Its high byte is the signed high
-//   digit h8 and its low byte l8 + 128, so q_int = 256 h8 + l8 with l8 in [-128, 127]
-//   (flipping bit 7 of the low byte gives l8).
-__device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const uint4* cw, int lane)
-{
-    const int h = lane >> 4, g8 = lane & 15, kb = g8 >> 2;
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = q[e];
-    if (cw) {
-        const uint32_t cc[4] = {cw->x, cw->y, cw->z, cw->w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? mul_hi16(v[e], cc[e >> 1]) : mul_lo16(v[e], cc[e >> 1]);
-    }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
-    amax = fmaxf(fmaxf(amax, fabsf(v[3])), fabsf(v[4]));
-    amax = fmaxf(fmaxf(amax, fabsf(v[5])), fabsf(v[6]));
-    amax = quad_max(fmaxf(amax, fabsf(v[7])));
-    const float inv = amax > 0.0f ? kQLim * __builtin_amdgcn_rcpf(amax) : 0.0f;
-    uint32_t qb[8];
-    uint32_t bsum = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        qb[e] = __float_as_uint(fmaf(v[e], inv, 12583040.0f));      // 1.5 * 2^23 + 128
-        bsum += qb[e];
-    }
-    // bytes (0, 1) of elements (a, b) -> [a.0, b.0, a.1, b.1]; then low and high digits of
-    // (even | odd) elements, even dims first within the 8-dim group
-    auto pair = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05010400u); };
-    const uint32_t t02 = pair(qb[0], qb[2]), t46 = pair(qb[4], qb[6]);
-    const uint32_t t13 = pair(qb[1], qb[3]), t57 = pair(qb[5], qb[7]);
-    const uint32_t lo0 = __builtin_amdgcn_perm(t46, t02, 0x05040100u) ^ 0x80808080u;
-    const uint32_t lo1 = __builtin_amdgcn_perm(t57, t13, 0x05040100u) ^ 0x80808080u;
-    const uint32_t hi0 = __builtin_amdgcn_perm(t46, t02, 0x07060302u);
-    const uint32_t hi1 = __builtin_amdgcn_perm(t57, t13, 0x07060302u);
-    int isum = (int)(bsum - 8u * 0x4B400080u);                        // sum of q_int
-    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR1, 0xF, 0xF, false);
-    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR2, 0xF, 0xF, false);
-    *(uint2*)&Q.qa[0][h][8 * g8] = make_uint2(lo0, lo1);
-    *(uint2*)&Q.qa[1][h][8 * g8] = make_uint2(hi0, hi1);
-    if ((g8 & 3) == 0) {
-        Q.S[h][kb] = amax * (1.0f / kQLim);
-        Q.off[h][kb] = 8 * isum;
-    }
-}
-
-// In-place unnormalized Walsh-Hadamard transform of rows [kG][128] held in LDS.
-__device__ __forceinline__ void lds_fwht4(float (*buf)[kD])
-{
-    const int tid = threadIdx.x;
-    for (int h = 1; h < kD; h <<= 1) {
-        __syncthreads();
-        for (int pi = tid; pi < kG * 64; pi += blockDim.x) {
-            int r = pi >> 6, k = pi & 63;
-            int lo = k & (h - 1);
-            int i = ((k - lo) << 1) | lo;
-            float a = buf[r][i], b = buf[r][i + h];
-            buf[r][i] = a + b;
-            buf[r][i + h] = a - b;
-        }
-    }
-    __syncthreads();
-}
-
-// FK, FV: key and value formats (4-bit: q4_0, q4_1 or kvarn4, independently).
-template <int FK, int FV>
-__global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
-{
-    constexpr bool KVARN_K = fkind(FK) == KIND_KVARN, KVARN_V = fkind(FV) == KIND_KVARN;
-    constexpr bool AFF_K = fkind(FK) == KIND_Q1, AFF_V = fkind(FV) == KIND_Q1;
-    constexpr int SB_K = AFF_K ? 16 : 8, SB_V = AFF_V ? 16 : 8;   // scale bytes per token row
-    constexpr int kLoads = 3 + (KVARN_V ? 1 : 0);                   // V load instructions per stage
-    static_assert(fbits(FK) == 4 && fbits(FV) == 4, "4-bit formats only");
-
-    __shared__ WsLds S;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bid = blockIdx.x;
-    // Wave w runs on SIMD w % 4.  In each group of four waves two are K waves and two V
-    // waves, on SIMDs (0, 1) and (2, 3) in even groups and the other way round in odd ones,
-    // so every SIMD runs two waves of each role; pair 2g + b = the waves b and b + 2 of group g.
-    const int wg4 = wave >> 2, w4 = wave & 3;
-    const int pr = 2 * wg4 + (w4 & 1);
-    const bool kwave = ((w4 >> 1) ^ (wg4 & 1)) == 0;
-    int e = 0;
-    for (int i = 1; i < a.n_seqs; ++i)
-        if (a.seqs[i].wg_base <= bid) e = i;
-    const DecodeSeq& sq = a.seqs[e];
-    const int SPL = sq.splits_q + sq.splits_t;
-    const int rr = bid - sq.wg_base;
-    const int head = rr / SPL;
-    const int sp = rr % SPL;
-    const bool quant = sp < sq.splits_q;
-    const int upw = quant ? a.units_per_wg : a.units_per_wg_t;
-    const int u_lo = (quant ? sp : sp - sq.splits_q) * upw;
-    const int u_hi = min(u_lo + upw, quant ? sq.units_q : sq.units_t);
-    const CacheGeom& g = a.g;
-    const int nq = (int)sq.n_q;                      // token counts fit 31 bits
-    const char* kst = sptr(g, sq.seq, a.layer, head, 0);
-    const char* vst = sptr(g, sq.seq, a.layer, head, 1);
-
-    // The query of the group, scaled to the log2 domain (KVarN pages: rotated, H q / 128),
-    // into LDS.  Every role calls this once, after issuing its first loads, so that the
-    // transform runs while they are in flight.
-    auto load_query = [&]() {
-        for (int i = tid; i < kG * kD; i += blockDim.x) {
-            int hh = i / kD, d = i % kD;
-            int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + hh) * kD + d;
-            float qv = a.q_dtype ? ((const float*)a.q)[qi] : bf16_to_f32(((const uint16_t*)a.q)[qi]);
-            S.qs[hh][d] = qv * a.scale_log2;
-        }
-        __syncthreads();
-        if (KVARN_K && quant) {
-            lds_fwht4(S.qs);
-            for (int i = tid; i < kG * kD; i += blockDim.x) S.qs[i / kD][i % kD] *= (1.0f / 128.0f);
-            __syncthreads();
-        }
-    };
-
-    // steps of each pair: the pair walks units u_lo + pr + kP i
-    auto steps_of = [&](int p) -> int {
-        const int uf = u_lo + p;
-        if (uf >= u_hi) return 0;
-        const int nu = (u_hi - uf + kP - 1) / kP;
-        if (!quant) return nu;
-        const int ul = uf + kP * (nu - 1);
-        const int64_t len = min<int64_t>((int64_t)ul * kPage + kPage, sq.n_q) - (int64_t)ul * kPage;
-        return 4 * (nu - 1) + (int)((len + 31) / 32);
-    };
-    const int J = steps_of(pr);
-    int Jmax = 0;
-    for (int p = 0; p < kP; ++p) Jmax = max(Jmax, steps_of(p));
-    const int u_first = u_lo + pr;
-
-    const int vg = lane >> 3, vp = lane & 7;          // V layout: pair slot (of 8), 16-dim part
-    const int vb = vp >> 1;
-
-    // end of a role: the K wave leaves (m, l) per head, the V wave its slot-summed accumulator
-    // end of a ring role: the K wave leaves (m, l) per head, the V wave its slot-summed
-    // accumulator (lane h < 4 of the K wave holds head h)
-    auto finish_k = [&](float mv, float lsum) {
-        const float t = wave_sum8(vp < kG ? lsum : 0.0f);
-        if (lane < kG) {
-            S.wl[pr][lane] = t;
-            S.wm[pr][lane] = mv;
-        }
-    };
-    auto finish_v = [&](float (&acc)[kG][16]) {
-#pragma unroll
-        for (int h = 0; h < kG; ++h)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const float y = wave_sum8(acc[h][jj]);
-                if (vg == 0) S.wacc[pr][h][16 * vp + jj] = y;
-            }
-    };
-    if (quant && kwave) {
-        // ============================ K wave (MFMA scores) ============================
-        // One v_mfma_i32_16x16x64_i8 per (16-token tile, block pair): rows = (head, block of
-        // the pair, byte of q_int), columns = tokens, K = the 64 dims of the two blocks (a row
-        // is zero over the other block's dims).  Lane (n = lane & 15, q = lane >> 4) supplies
-        // the codes of token n, dims 16q..16q+15 of the pair, and receives rows 4q..4q+3:
-        // head q, both blocks of the pair, both bytes.  So a lane scores one head of one token
-        // per tile on its own, and the running maximum of a head is a 16-lane row reduction.
-        // The MFMA accumulator starts at -8 sum(q_int) of the block (symmetric formats), which
-        // takes the code offset 8 out of the integer sum.
-        const int n16 = lane & 15, q4 = lane >> 4;
-        const char* kcodes = kst + g.k.codes;
-        const char* kscales = kst + g.k.scales;
-        const char* kchan = kst + g.k.cscale;
-        QMat* Qb = S.qm[pr];
-        i32x4 A[2], Ci[2];
-        float Sc[4], Qs[4];
-        auto load_a = [&](const QMat& Q) {
-            const int m = n16, dig = m & 1, sel = (m >> 1) & 1, h = m >> 2;
-#pragma unroll
-            for (int bp = 0; bp < 2; ++bp) {
-                const i32x4 z = {0, 0, 0, 0};
-                A[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[dig][h][32 * (2 * bp + sel) + 16 * (q4 & 1)] : z;
-                Ci[bp] = AFF_K ? z : (i32x4){-Q.off[q4][2 * bp], 0, -Q.off[q4][2 * bp + 1], 0};
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                Sc[b] = Q.S[q4][b];
-                // affine keys: the sum of the rounded query, S * sum(q_int), so that the score
-                // is the rounded query against the dequantized key, d u + m, exactly; its
-                // error is then sum((q - q_hat) k), small where a block holds one outlier
-                // channel (the other keys are near 0, while d u - 8 d or d u are not)
-                Qs[b] = AFF_K ? Q.S[q4][b] * (float)(Q.off[q4][b] / 8) : 0.0f;
-            }
-        };
-        // Codes and scales of one step, straight to registers through buffer loads whose
-        // resource covers the step's valid tokens: rows past the end of the page read as zero
-        // (their scores are masked).  Stages past the last step repeat it.
-        // ch (KVarN): the key channel scales of the page after the step's page, loaded with the
-        // step's rows so that the waits the compiler places for them stay exact
-        struct KLoad { uint2 c[2][2]; uint4 s[2]; uint4 ch; };
-        const int cofs = n16 * 64 + 8 * q4, sofs = n16 * SB_K;
-        auto chan_load = [&](int i) -> uint4 {      // key channel scales of the pair's i-th page
-            const int nu = (u_hi - u_first + kP - 1) / kP;
-            const int u = u_first + kP * min(i, nu - 1);
-            return *(const uint4*)(kchan + (int64_t)u * 256 + 16 * (lane & 15));
-        };
-        auto kload = [&](int j, KLoad& L) {
-            const int jj = j < J ? j : J - 1;
-            const int u = u_first + kP * (jj >> 2);
-            const int tb = u * kPage + 32 * (jj & 3);
-            const int nv = min(32, min(u * kPage + kPage, nq) - tb);
-            const rsrc_t rc = make_rsrc(kcodes + (int64_t)tb * 64, nv * 64);
-            const rsrc_t rs = make_rsrc(kscales + (int64_t)tb * SB_K, nv * SB_K);
-#pragma unroll
-            for (int T = 0; T < 2; ++T) {
-#pragma unroll
-                for (int bp = 0; bp < 2; ++bp) L.c[T][bp] = buf_load8(rc, cofs + 1024 * T + 32 * bp);
-                if (AFF_K) {
-                    L.s[T] = buf_load16(rs, sofs + 16 * SB_K * T);
-                } else {
-                    const uint2 w = buf_load8(rs, sofs + 16 * SB_K * T);
-                    L.s[T] = make_uint4(w.x, w.y, 0u, 0u);
-                }
-            }
-            if (KVARN_K) L.ch = chan_load((jj >> 2) + 1);
-        };
-        float mh = kNeg;                           // running max of head q4
-        float ls = 0.0f;                           // sum of p over the lane's tokens
-        uint4 cfirst = make_uint4(0u, 0u, 0u, 0u);
-        // three register stages, loads issued two steps ahead of their use
-        KLoad X, Y, Z;
-        if (J > 0) {
-            if (KVARN_K) cfirst = chan_load(0);        // first, so that its wait is exact
-            kload(0, X);
-            kload(1, Y);
-            kload(2, Z);
-        }
-        // the lane's 8 query values (head lane >> 4, dims 8 (lane & 15) ..), log2 domain;
-        // KVarN: rotated, H q / 128 (spans 1, 2, 4 in the lane, 8 .. 64 across lanes)
-        float qv[8];
-        {
-            const int64_t qi = ((int64_t)sq.in_idx * g.n_q_heads + head * kG + (lane >> 4)) * kD + 8 * n16;
-            if (a.q_dtype) {
-                const float4 x0 = *(const float4*)((const float*)a.q + qi);
-                const float4 x1 = *(const float4*)((const float*)a.q + qi + 4);
-                qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
-                qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
-            } else {
-                const uint4 w = *(const uint4*)((const uint16_t*)a.q + qi);
-                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qv[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                    qv[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] *= a.scale_log2;
-            if (KVARN_K) {
-#pragma unroll
-                for (int sp = 1; sp < 8; sp <<= 1)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if ((e & sp) == 0) {
-                            const float x = qv[e], y = qv[e + sp];
-                            qv[e] = x + y;
-                            qv[e + sp] = x - y;
-                        }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const bool up = (lane >> k) & 1;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float y = __shfl_xor(qv[e], 1 << k);
-                        qv[e] = up ? y - qv[e] : qv[e] + y;
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] *= (1.0f / 128.0f);
-            }
-        }
-        if (!KVARN_K) {
-            build_qmat(Qb[0], qv, nullptr, lane);
-            wave_sync_lds();
-            load_a(Qb[0]);
-        } else if (J > 0) {
-            // first page now; each later page's operand is built two steps before it starts
-            build_qmat(Qb[0], qv, &cfirst, lane);
-            wave_sync_lds();
-            load_a(Qb[0]);
-        }
-        auto kstep = [&](int j, const KLoad& L) __attribute__((always_inline)) {
-            const int u = u_first + kP * (j >> 2);
-            const int t_page = u * kPage;
-            const int t_end = min(t_page + kPage, nq);
-            if (KVARN_K && (j & 3) == 0 && j > 0) {
-                wave_sync_lds();
-                load_a(Qb[(j >> 2) & 1]);
-            }
-            if (KVARN_K && (j & 3) == 2) {
-                // the next page's operand into the other buffer (read at that page's start)
-                build_qmat(Qb[((j >> 2) + 1) & 1], qv, &L.ch, lane);
-            }
-            float sc[2];
-#pragma unroll
-            for (int T = 0; T < 2; ++T) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int bp = 0; bp < 2; ++bp) {
-                    const uint2 x = L.c[T][bp];
-                    const i32x4 Bm = {(int)(x.x & 0x0F0F0F0Fu), (int)((x.x >> 4) & 0x0F0F0F0Fu),
-                                      (int)(x.y & 0x0F0F0F0Fu), (int)((x.y >> 4) & 0x0F0F0F0Fu)};
-                    const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, Ci[bp], 0, 0, 0);
-                    const int t0 = (C.y << 8) + C.x, t1 = (C.w << 8) + C.z;
-                    // block scales as binary16 operands of v_fma_mix (no conversion)
-                    uint32_t w0, w1;
-                    if (AFF_K) {
-                        w0 = bp ? L.s[T].z : L.s[T].x;
-                        w1 = bp ? L.s[T].w : L.s[T].y;
-                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
-                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)lo_half(w1), acc);
-                        acc = fmaf(Qs[2 * bp], (float)hi_half(w0), acc);
-                        acc = fmaf(Qs[2 * bp + 1], (float)hi_half(w1), acc);
-                    } else {
-                        w0 = bp ? L.s[T].y : L.s[T].x;
-                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
-                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)hi_half(w0), acc);
-                    }
-                }
-                sc[T] = acc;
-            }
-            if (t_end - (t_page + 32 * (j & 3)) < 32) {
-                // the page ends inside this step: mask the rows past its end
-#pragma unroll
-                for (int T = 0; T < 2; ++T)
-                    if (t_page + 32 * (j & 3) + 16 * T + n16 >= t_end) sc[T] = kNeg;
-            }
-            // running max of head q4 (a 16-lane row): once the first steps have set it, a new
-            // maximum is rare, so the row reduction and the rescale factor are only computed
-            // when some lane's score exceeds it (the result is the same either way)
-            float al = 1.0f;
-            if (__builtin_amdgcn_ballot_w64(fmaxf(sc[0], sc[1]) > mh)) {
-                const float nm = fmaxf(mh, row_max16(fmaxf(sc[0], sc[1])));
-                al = __builtin_amdgcn_exp2f(mh - nm);                // exactly 1 if unchanged
-                mh = nm;
-            }
-            const float p0 = __builtin_amdgcn_exp2f(sc[0] - mh);
-            const float p1 = __builtin_amdgcn_exp2f(sc[1] - mh);
-            ls = fmaf(ls, al, p0 + p1);
-            PBuf& P = S.pb[pr][j & 3];
-            P.ph[q4][n16] = (_Float16)p0;
-            P.ph[q4][16 + n16] = (_Float16)p1;
-            if (n16 == 0) P.alpha[q4] = al;
-            __syncthreads();
-        };
-        int j = 0;
-#pragma unroll 1
-        for (; j + 2 < J; j += 3) {
-            kstep(j, X);
-            kload(j + 3, X);
-            kstep(j + 1, Y);
-            kload(j + 4, Y);
-            kstep(j + 2, Z);
-            kload(j + 5, Z);
-        }
-        if (j < J) { kstep(j, X); ++j; }
-        if (j < J) { kstep(j, Y); ++j; }
-#pragma unroll 1
-        for (; j <= Jmax; ++j) __syncthreads();
-        // normalizer of head q4 over its row
-        float l = ls;
-        l += dpp<ROW_ROR8>(l);
-        l += dpp<ROW_ROR4>(l);
-        l += dpp<ROW_ROR2>(l);
-        l += dpp<ROW_ROR1>(l);
-        if (n16 == 0) {
-            S.wl[pr][q4] = l;
-            S.wm[pr][q4] = mh;
-        }
-    } else if (quant) {
-        // ================================ V wave ================================
-        const char* cbase = vst + g.v.codes;
-        const char* sbase = vst + g.v.scales;
-        const char* chbase = vst + g.v.cscale;
-        Stage* ring = S.st[pr];
-        // stage j -> ring slot j % kStages; the number of load instructions per stage is
-        // fixed (stages past the end repeat the last), so one vmcnt value covers a stage.
-        // Buffer resources over the step's valid rows: rows past the end of the page read as
-        // zero (the ring is zeroed first, so no slot ever holds non-finite bytes either way;
-        // the weights of those rows are zero).
-        const int ve = (lane >> 2) * 128 + (lane & 3) * 16;      // even rows of the stage
-        auto issue = [&](int j, int slot) {
-            const int jj = j < J ? j : J - 1;
-            const int u = u_first + kP * (jj >> 2);
-            const int tb = u * kPage + 32 * (jj & 3);
-            const int nv = min(32, min(u * kPage + kPage, nq) - tb);
-            Stage& B = ring[slot];
-            const rsrc_t rc = make_rsrc(cbase + (int64_t)tb * 64, nv * 64);
-            lds_buf16(rc, ve, B.codes);
-            lds_buf16(rc, ve + 64, B.codes + 1024);
-            const rsrc_t rs = make_rsrc(sbase + (int64_t)tb * SB_V, nv * SB_V);
-            if (AFF_V) {
-                if (lane < 32) lds_buf16(rs, 16 * lane, B.scales);
-            } else {
-                lds_buf4(rs, 4 * lane, B.scales);
-            }
-            if (KVARN_V) {
-                if (lane < 16) lds_buf16(make_rsrc(chbase + (int64_t)u * 256, 256), 16 * lane, B.chan);
-            }
-        };
-        {
-            // zero the ring once
-            uint4* z = (uint4*)ring;
-            for (int i = lane; i < (int)(kStages * sizeof(Stage) / 16); i += 64) z[i] = make_uint4(0u, 0u, 0u, 0u);
-            wave_sync_lds();
-        }
-        if (J > 0) {
-            issue(0, 0);
-            issue(1, 1);
-            issue(2, 2);
-        }
-        // Lane = (token group tg = lane >> 4, block vblk = (lane >> 2) & 3, slice vj = lane & 3)
-        // owns dims 32 vblk + 8 vj .. + 7.  In half `hf` of a step the group takes the token
-        // pairs s0 = 8 hf + tg and s1 = s0 + 4 (tokens 2 s0, 2 s0 + 1, 2 s1, 2 s1 + 1).  MFMA
-        // block (tg, vblk) = lanes 4 (lane >> 2) .. + 3: A row i = the binary16 weights p d of
-        // head i for the four tokens, B column i = the centred codes u - 8 of dim
-        // 32 vblk + 8 i + r as exact binary16 integers (r = 0..7, one MFMA each), K = the four
-        // tokens; D column i accumulates the four heads of that dim.  Centring before the sum
-        // matters at long context: with spread attention the output is far smaller than
-        // sum(w u) or 8 sum(w), and the fp32 rounding of either would be amplified.
-        const int tg = lane >> 4, vblk = (lane >> 2) & 3, vj = lane & 3;
-        f32x4 D[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) D[r] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        float ms = 0.0f, msd = 0.0f;  // sums of p m and p d of head vj over the lane's tokens (affine)
-        float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
-        // 0x64006400 kept in a register so that the mask-and-or is one v_and_or_b32
-        uint32_t k6400 = 0x64006400u;
-        asm volatile("" : "+v"(k6400));
-        const half2_t c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};   // 1024 + 8
-        const half2_t c1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};   // 1024 + 16 * 8
-        auto quad_bcast = [&](float x, int h) -> float {     // lane h of the lane's quad
-            return h == 0 ? dpp<0x00>(x) : h == 1 ? dpp<0x55>(x) : h == 2 ? dpp<0xAA>(x) : dpp<0xFF>(x);
-        };
-        // Stage j + 3 is issued at the end of step j, once the step's LDS reads are done: a
-        // global-to-LDS load in flight holds lgkmcnt for a while after issue, and every LDS
-        // wait of the step would pay for it.  The V wave publishes nothing through LDS, so its
-        // barrier needs no lgkmcnt wait (bare s_barrier; the clobber keeps the compiler from
-        // moving LDS accesses across it).
-        auto vstep = [&](int j, int slot) __attribute__((always_inline)) {
-            const bool page_start = (j & 3) == 0;
-            wait_vmcnt<2 * kLoads>();
-            asm volatile("" ::: "memory");
-            const Stage& B = ring[slot];
-            const PBuf& P = S.pb[pr][slot];
-            const f32x4 al = *(const f32x4*)P.alpha;
-            if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) D[r] *= al;
-                ms *= al[vj];
-                msd *= al[vj];
-            }
-            if (KVARN_V && page_start) {
-                // this page's value channel scales: move the accumulator to them (it is zero
-                // before the first page, so the first move is inert)
-                const uint4 c = *(const uint4*)(B.chan + 32 * vblk + 8 * vj);
-                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float cn = fp16_to_f32((cw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
-                    D[r] *= cvr[r] * __builtin_amdgcn_rcpf(cn);
-                    cvr[r] = cn;
-                }
-            }
-            const uint32_t* cw32 = (const uint32_t*)B.codes;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int s0 = 8 * hf + tg, s1 = s0 + 4;
-                const int cofs = 4 * vblk + vj;
-                const uint32_t x0 = cw32[16 * s0 + cofs], x1 = cw32[16 * (16 + s0) + cofs];
-                const uint32_t x2 = cw32[16 * s1 + cofs], x3 = cw32[16 * (16 + s1) + cofs];
-                // A: binary16 p (written by the K wave) times the binary16 block scales, two
-                // tokens per packed multiply; the scale pairs are gathered by 16-bit LDS loads
-                const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
-                const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
-                const _Float16* sc16 = (const _Float16*)B.scales;
-                constexpr int SW = SB_V / 2;                   // binary16 words per scale row
-                const int so = (AFF_V ? 2 : 1) * vblk;
-                const half2_t d01 = {sc16[SW * (2 * s0) + so], sc16[SW * (2 * s0 + 1) + so]};
-                const half2_t d23 = {sc16[SW * (2 * s1) + so], sc16[SW * (2 * s1 + 1) + so]};
-                const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * d01);
-                const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * d23);
-                if (AFF_V) {
-                    const half2_t m01 = {sc16[SW * (2 * s0) + so + 1], sc16[SW * (2 * s0 + 1) + so + 1]};
-                    const half2_t m23 = {sc16[SW * (2 * s1) + so + 1], sc16[SW * (2 * s1 + 1) + so + 1]};
-                    msd = __builtin_amdgcn_fdot2(p01, d01, msd, false);
-                    msd = __builtin_amdgcn_fdot2(p23, d23, msd, false);
-                    ms = __builtin_amdgcn_fdot2(p01, m01, ms, false);
-                    ms = __builtin_amdgcn_fdot2(p23, m23, ms, false);
-                }
-                const h16x4 A = __builtin_bit_cast(h16x4, make_uint2(a01, a23));
-                // Byte k of a code word holds dims 2k (low nibble) and 2k+1 (high nibble).  v_perm
-                // puts byte k of the two tokens of a pair in bytes 0 and 2; masking in 0x6400
-                // gives the binary16 values 1024 + u (low nibble) or 1024 + 16 u (high nibble);
-                // one packed add centres them to u - 8 or 16 (u - 8), both exact.  The factor 16
-                // of the odd dims is removed at the end.
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t sel = (uint32_t)k | ((uint32_t)(4 + k) << 16) | 0x0C000C00u;
-                    const uint32_t q01 = __builtin_amdgcn_perm(x1, x0, sel);
-                    const uint32_t q23 = __builtin_amdgcn_perm(x3, x2, sel);
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const uint32_t m = e ? 0x00F000F0u : 0x000F000Fu;
-                        const half2_t c = e ? c1152 : c1032;
-                        const half2_t b01 = __builtin_bit_cast(half2_t, (q01 & m) | k6400) + c;
-                        const half2_t b23 = __builtin_bit_cast(half2_t, (q23 & m) | k6400) + c;
-                        const h16x4 Bm = {b01.x, b01.y, b23.x, b23.y};
-                        D[2 * k + e] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Bm, D[2 * k + e], 0, 0, 0);
-                    }
-                }
-            }
-            issue(j + 3, (slot + 3) & 3);
-            asm volatile("s_barrier" ::: "memory");
-        };
-        // one idle barrier (the K wave scores the first step), J work steps, idle barriers
-        __syncthreads();
-        // steps in fours so that ring and probability slots are static
-        int j = 0;
-#pragma unroll 1
-        for (; j + 3 < J; j += 4) {
-            vstep(j, 0);
-            vstep(j + 1, 1);
-            vstep(j + 2, 2);
-            vstep(j + 3, 3);
-        }
-        if (j < J) { vstep(j, 0); ++j; }
-        if (j < J) { vstep(j, 1); ++j; }
-        if (j < J) { vstep(j, 2); ++j; }
-#pragma unroll 1
-        for (++j; j <= Jmax; ++j) __syncthreads();
-        // sum the four token groups (lanes l ^ 16, l ^ 32); offsets of all heads of the block
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float x = D[r][c];
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                D[r][c] = x;
-            }
-        ms = fmaf(8.0f, msd, ms);       // sum of p (m + 8 d)
-        ms += __shfl_xor(ms, 16);
-        ms += __shfl_xor(ms, 32);
-        const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};
-        wait_vmcnt<0>();                          // stages past the end, before reusing the ring
-        asm volatile("" ::: "memory");
-        if (tg == 0) {
-            // the affine minimum (and the 8 d of the centring) and the page's c_V
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                f32x4 v = (r & 1) ? D[r] * 0.0625f : D[r];     // odd dims carried a factor 16
-                if (AFF_V) v += mh4;
-                if (KVARN_V) v *= cvr[r];
-#pragma unroll
-                for (int h = 0; h < kG; ++h) S.wacc[pr][h][32 * vblk + 8 * vj + r] = v[h];
-            }
-        }
-        wait_vmcnt<0>();
-        asm volatile("" ::: "memory");
-    } else {
-        // ========================= BF16 ring chunks (binary32) =========================
-        // units of 32 tokens; a step is two halves of 16 tokens (8 lanes per token pair)
-        const int R = g.ring_slots;
-        load_query();
-        if (kwave) {
-            float mh = kNeg;                           // running max of the lane's head kb
-            float lsum = 0.0f;                         // sum of p of the lane's head
-            float qr[kG][16];
-#pragma unroll
-            for (int h = 0; h < kG; ++h)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) qr[h][j] = S.qs[h][16 * vp + j];
-            int j = 0;
-#pragma unroll 1
-            for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
-                const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
-                const uint32_t tbm = (uint32_t)(tb % R);
-                float sc[2][kG][2];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int off = 16 * half + 2 * vg;
-                    uint4 w[2][2];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int o = min<int64_t>(off + t, te - tb - 1);
-                        const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
-                        const uint4* pk = (const uint4*)(kst + g.k.ring + (int64_t)rs * 256 + 32 * vp);
-                        w[t][0] = pk[0];
-                        w[t][1] = pk[1];
-                    }
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const uint32_t ww[8] = {w[t][0].x, w[t][0].y, w[t][0].z, w[t][0].w,
-                                                w[t][1].x, w[t][1].y, w[t][1].z, w[t][1].w};
-                        float kx[16];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            kx[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                            kx[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
-                        }
-#pragma unroll
-                        for (int h = 0; h < kG; ++h) {
-                            float x = 0.0f;
-#pragma unroll
-                            for (int jj = 0; jj < 16; ++jj) x = fmaf(qr[h][jj], kx[jj], x);
-                            x += dpp<QP_XOR1>(x);
-                            x += dpp<QP_XOR2>(x);
-                            x += dpp<ROW_HMIRROR>(x);
-                            sc[half][h][t] = (tb + off + t < te) ? x : kNeg;
-                        }
-                    }
-                }
-                // each lane keeps the scores of head vp & 3; lanes with equal vp share a head
-                const int hv = vp & 3;
-                float x[2][2];
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const f32x4 v = {sc[half][0][t], sc[half][1][t], sc[half][2][t], sc[half][3][t]};
-                        x[half][t] = v[hv];
-                    }
-                const float nm = fmaxf(mh, wave_max8(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[1][0], x[1][1]))));
-                const float al = __builtin_amdgcn_exp2f(mh - nm);    // exactly 1 if unchanged
-                mh = nm;
-                lsum *= al;
-                PBuf& P = S.pb[pr][j & 1];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int off = 16 * half + 2 * vg;
-                    const float p0 = (tb + off < te) ? __builtin_amdgcn_exp2f(x[half][0] - mh) : 0.0f;
-                    const float p1 = (tb + off + 1 < te) ? __builtin_amdgcn_exp2f(x[half][1] - mh) : 0.0f;
-                    if (vp < kG) {
-                        *(float2*)&P.p[vp][16 * half + 2 * vg] = make_float2(p0, p1);
-                        lsum += p0 + p1;
-                    }
-                }
-                if (lane < kG) P.alpha[lane] = al;
-                __syncthreads();
-            }
-#pragma unroll 1
-            for (; j <= Jmax; ++j) __syncthreads();
-            finish_k(mh, lsum);
-        } else {
-            float acc[kG][16];
-#pragma unroll
-            for (int h = 0; h < kG; ++h)
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
-            __syncthreads();
-            int j = 0;
-#pragma unroll 1
-            for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
-                const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
-                const uint32_t tbm = (uint32_t)(tb % R);
-                const PBuf& P = S.pb[pr][j & 1];
-                const float4 al = *(const float4*)P.alpha;
-                if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
-                    const float alv[kG] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-                    for (int h = 0; h < kG; ++h)
-#pragma unroll
-                        for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
-                }
-#pragma unroll 1
-                for (int half = 0; half < 2; ++half) {
-                    const int slot = vg + 8 * half;
-                    const int off = 2 * slot;
-                    float vx[2][16];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int o = min<int64_t>(off + t, te - tb - 1);
-                        const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
-                        const uint4* pv = (const uint4*)(vst + g.v.ring + (int64_t)rs * 256 + 32 * vp);
-                        const uint4 w0 = pv[0], w1 = pv[1];
-                        const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            vx[t][2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                            vx[t][2 * i + 1] = bf16_to_f32(ww[i] >> 16);
-                        }
-                    }
-                    float pp[4][2];
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) {
-                        const float2 w = *(const float2*)&P.p[h][2 * slot];
-                        pp[h][0] = w.x;
-                        pp[h][1] = w.y;
-                    }
-#pragma unroll
-                    for (int h = 0; h < kG; ++h)
-#pragma unroll
-                        for (int jj = 0; jj < 16; ++jj)
-                            acc[h][jj] = fmaf(pp[h][0], vx[0][jj], fmaf(pp[h][1], vx[1][jj], acc[h][jj]));
-                }
-                __syncthreads();
-            }
-#pragma unroll 1
-            for (++j; j <= Jmax; ++j) __syncthreads();
-            finish_v(acc);
-        }
-    }
-
-    __syncthreads();
-    float* part_out = a.partials + (int64_t)bid * kPartialFloats;
-    for (int i = tid; i < kG * kD; i += blockDim.x) {
-        const int h = i / kD, d = i % kD;
-        float M = S.wm[0][h];
-#pragma unroll
-        for (int p = 1; p < kP; ++p) M = fmaxf(M, S.wm[p][h]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int p = 0; p < kP; ++p) {
-            const float ew = __builtin_amdgcn_exp2f(S.wm[p][h] - M);
-            L += S.wl[p][h] * ew;
-            A += S.wacc[p][h][d] * ew;
-        }
-        part_out[2 * kMaxGroup + h * kD + d] = A;
-        if (d == 0) { part_out[h] = M; part_out[kMaxGroup + h] = L; }
-    }
-}
-
-template <int FK, int FV>
-int launch_ws_pair(const DecodeArgs& a, int n_wgs, hipStream_t st)
-{
-    hipLaunchKernelGGL((k_decode_ws<FK, FV>), dim3(n_wgs), dim3(kThreads), 0, st, a);
-    return (int)hipGetLastError();
-}
-
-template <int FK, int FV>
-int occ_ws()
-{
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode_ws<FK, FV>, kThreads, 0) != hipSuccess) return 0;
-    return n;
-}
-
-// index of a fast format: q4_0, q4_1, kvarn4
-int fast_index(int fmt) { return fmt == 5 ? 0 : fmt == 6 ? 1 : fmt == 15 ? 2 : -1; }
-
-template <int FK>
-int launch_fk(int fmt_v, const DecodeArgs& a, int n_wgs, hipStream_t st)
-{
-    switch (fmt_v) {
-    case 5: return launch_ws_pair<FK, 5>(a, n_wgs, st);
-    case 6: return launch_ws_pair<FK, 6>(a, n_wgs, st);
-    case 15: return launch_ws_pair<FK, 15>(a, n_wgs, st);
-    default: return (int)hipErrorInvalidValue;
-    }
-}
-
-template <int FK>
-int occ_fk(int fmt_v)
-{
-    switch (fmt_v) {
-    case 5: return occ_ws<FK, 5>();
-    case 6: return occ_ws<FK, 6>();
-    case 15: return occ_ws<FK, 15>();
-    default: return 0;
+    switch (fbits(fmt_k)) {
+    case 2: return decode_fast_w2(op, a, fmt_k, fmt_v, n_wgs, stream);
+    case 3: return decode_fast_w3(op, a, fmt_k, fmt_v, n_wgs, stream);
+    case 4: return decode_fast_w4(op, a, fmt_k, fmt_v, n_wgs, stream);
+    case 8: return decode_fast_w8(op, a, fmt_k, fmt_v, n_wgs, stream);
+    default: return op == 0 ? (int)hipErrorInvalidValue : 0;
     }
 }
 
@@ -1048,33 +32,21 @@ int occ_fk(int fmt_v)
 
 bool decode_fast_supported(int fmt_k, int fmt_v)
 {
-    return fast_index(fmt_k) >= 0 && fast_index(fmt_v) >= 0;
+    return fast_format(fmt_k) && fast_format(fmt_v);
 }
 
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream)
 {
-    hipStream_t st = (hipStream_t)stream;
-    switch (a.g.fmt_k) {
-    case 5: return launch_fk<5>(a.g.fmt_v, a, n_wgs, st);
-    case 6: return launch_fk<6>(a.g.fmt_v, a, n_wgs, st);
-    case 15: return launch_fk<15>(a.g.fmt_v, a, n_wgs, st);
-    default: return (int)hipErrorInvalidValue;
-    }
+    if (!decode_fast_supported(a.g.fmt_k, a.g.fmt_v)) return (int)hipErrorInvalidValue;
+    return by_width(0, &a, a.g.fmt_k, a.g.fmt_v, n_wgs, stream);
 }
 
 int decode_fast_wgs_per_cu(int fmt_k, int fmt_v)
 {
-    static int cache[3][3] = {{0}};
-    const int ik = fast_index(fmt_k), iv = fast_index(fmt_v);
-    if (ik < 0 || iv < 0) return 0;
-    if (!cache[ik][iv]) {
-        switch (fmt_k) {
-        case 5: cache[ik][iv] = occ_fk<5>(fmt_v); break;
-        case 6: cache[ik][iv] = occ_fk<6>(fmt_v); break;
-        default: cache[ik][iv] = occ_fk<15>(fmt_v); break;
-        }
-    }
-    return cache[ik][iv];
+    static int cache[19][19] = {{0}};
+    if (!decode_fast_supported(fmt_k, fmt_v)) return 0;
+    if (!cache[fmt_k][fmt_v]) cache[fmt_k][fmt_v] = by_width(1, nullptr, fmt_k, fmt_v, 0, nullptr);
+    return cache[fmt_k][fmt_v];
 }
 
 }  // namespace kvq

@@ -149,13 +149,16 @@ def test_mixed_key_value_formats_small(fmt):
     _attn_check(cache, fmt, wl, 0, 1, [0, 1], n, q, out, 4)
 
 
-FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4_1", "q4_1/kvarn4"]
+FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4_1", "q4_1/kvarn4",
+              "q8_0/q4_0", "q4_0/q8_0", "q8_1/q8_1", "kvarn8/q8_1", "q8_0/kvarn3", "q3_0/q3_1",
+              "q3_1/kvarn3", "kvarn3/q3_0", "q2_0/q2_1", "q2_1/kvarn8", "kvarn2/kvarn2", "kvarn8/q2_0"]
 
 
 @pytest.mark.parametrize("fmt", FAST_PAIRS)
 def test_fast_kernel_mixed_pairs_many_pages(fmt):
-    """The 4-bit kernel with different key and value formats: 8 KV heads, 24k tokens (many
-    pages per pair of waves, a partial last page, a 1024-token tail), all heads checked."""
+    """The fast kernel (2-, 3-, 4- and 8-bit codes) with different key and value formats: 8
+    KV heads, 24k tokens (many pages per pair of waves, a partial last page, a 1024-token
+    tail), all heads checked."""
     wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
     n, Tt = 24000, 1024
     cache = T.make_cache(fmt, 1, 8, 32, tail_tokens=Tt, n_seqs=1, max_tokens=n)
