@@ -28,6 +28,8 @@ UNITS = [
     ("kvq_decode_ws_k2.hip", []),
     ("kvq_decode_ws_k3.hip", []),
     ("kvq_decode_ws_k4.hip", []),
+    ("kvq_decode_ws_k5.hip", []),
+    ("kvq_decode_ws_k6.hip", []),
     ("kvq_decode_ws_k8.hip", []),
     ("kvq_merge.hip", []),
     ("kvq_debug.hip", ["-ffp-contract=off"]),

@@ -251,7 +251,7 @@ struct alignas(16) WsLds {
     float wm[kP][kG], wl[kP][kG];
     __device__ float* wacc(int p) { return reinterpret_cast<float*>(&st[p][0]); }   // [kG][kD]
 };
-static_assert(sizeof(WsLds<4>) <= 160 * 1024 && sizeof(WsLds<8>) <= 160 * 1024, "LDS size");
+static_assert(sizeof(WsLds<6>) <= 160 * 1024 && sizeof(WsLds<8>) <= 160 * 1024, "LDS size");
 static_assert(ring_depth<2>() * sizeof(Stage<2>) >= kG * kD * sizeof(float), "wacc fits a ring");
 
 // x * (binary16 half of w), one v_fma_mix_f32 (no separate conversion).
@@ -286,7 +286,7 @@ __device__ __forceinline__ float quad_max(float x)
 // N = 3) and unpacks them to one byte each; kpos<N> gives the byte position of element e
 // (0..15) of the half, which the query operand follows.
 template <int N>
-constexpr int kwin_dwords() { return N == 2 ? 1 : N == 8 ? 4 : 2; }
+constexpr int kwin_dwords() { return N == 2 ? 1 : N == 8 ? 4 : N >= 5 ? 3 : 2; }
 // byte offset of lane half h's window within its block
 template <int N>
 __device__ __forceinline__ int kwin_off(int h) { return (2 * N * h) & ~3; }
@@ -304,6 +304,16 @@ __device__ __forceinline__ int kpos(int e)
         // dwords: low nibbles of bytes 0..3, high nibbles, then the same for bytes 4..7
         return (e < 8 ? 0 : 8) + ((e & 1) ? 4 : 0) + ((e & 7) >> 1);
     }
+    if constexpr (N == 5) {
+        // dwords [e0 e8 e2 e10], [e5 e13 e7 e15], [e1 e3 e4 e6], [e9 e11 e12 e14]
+        constexpr int t[16] = {0, 8, 2, 9, 10, 4, 11, 6, 1, 12, 3, 13, 14, 5, 15, 7};
+        return t[e];
+    }
+    if constexpr (N == 6) {
+        // dwords [e0 e4 e3 e7], [e8 e12 e11 e15], [e1 e2 e5 e6], [e9 e10 e13 e14]
+        constexpr int t[16] = {0, 8, 9, 2, 1, 10, 11, 3, 4, 12, 13, 6, 5, 14, 15, 7};
+        return t[e];
+    }
     return e;
 }
 
@@ -316,13 +326,20 @@ __device__ __forceinline__ KSel ksel3(int h)
     return {two(0, 3), two(1, 4), two(2, 5), 6u + 8u * c, 15u + 8u * c};
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_shr16(uint32_t x, uint32_t s_lo, uint32_t s_hi)
 {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     const u16x2 v = __builtin_bit_cast(u16x2, x);
     const u16x2 sh = {(unsigned short)s_lo, (unsigned short)s_hi};
     return __builtin_bit_cast(uint32_t, v >> sh);
 }
+__device__ __forceinline__ uint32_t pk_shl16(uint32_t x, uint32_t s_lo, uint32_t s_hi)
+{
+    const u16x2 v = __builtin_bit_cast(u16x2, x);
+    const u16x2 sh = {(unsigned short)s_lo, (unsigned short)s_hi};
+    return __builtin_bit_cast(uint32_t, v << sh);
+}
+__device__ __forceinline__ uint32_t bfe5(uint32_t x, uint32_t o) { return __builtin_amdgcn_ubfe(x, o, 5u); }
 
 // The 16 codes of the lane's window as bytes (8-bit codes: u - 128 as a signed byte).
 template <int N>
@@ -346,6 +363,40 @@ __device__ __forceinline__ i32x4 unpack_k(const uint32_t (&w)[kwin_dwords<N>()],
     } else if constexpr (N == 4) {
         const uint32_t m = 0x0F0F0F0Fu;
         return (i32x4){(int)(w[0] & m), (int)((w[0] >> 4) & m), (int)(w[1] & m), (int)((w[1] >> 4) & m)};
+    } else if constexpr (N == 5) {
+        // window data at bit 16 h: move it to bit 0 (x0..x2 = the 80 bits); codes at bit 5e.
+        // Offsets s <= 3 of the pair bytes (k, k + 5) go through the half-word shift; the
+        // eight codes that cross a byte are extracted one by one.
+        const uint32_t sh = ks.y - 6u;                 // 16 h
+        const uint32_t x0 = __builtin_amdgcn_alignbit(w[1], w[0], sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(w[2], w[1], sh);
+        const uint32_t x2 = w[2] >> sh;
+        const uint32_t m = 0x1F1F1F1Fu;
+        const uint32_t d0 = pk_shr16(__builtin_amdgcn_perm(x1, x0, 0x06010500u), 0, 2) & m;
+        const uint32_t z = __builtin_amdgcn_alignbit(x1, x0, 24);
+        const uint32_t d1 = pk_shr16(__builtin_amdgcn_perm(x2, z, 0x05010400u), 1, 3) & m;
+        const uint32_t e1 = bfe5(x0, 5), e3 = bfe5(x0, 15), e4 = bfe5(x0, 20);
+        const uint32_t e6 = __builtin_amdgcn_alignbit(x1, x0, 30) & 31u;
+        const uint32_t e9 = bfe5(x1, 13), e11 = bfe5(x1, 23), e14 = bfe5(x2, 6);
+        const uint32_t e12 = __builtin_amdgcn_alignbit(x2, x1, 28) & 31u;
+        const uint32_t d2 = (e1 | (e3 << 8)) | ((e4 | (e6 << 8)) << 16);
+        const uint32_t d3 = (e9 | (e11 << 8)) | ((e12 | (e14 << 8)) << 16);
+        return (i32x4){(int)d0, (int)d1, (int)d2, (int)d3};
+    } else if constexpr (N == 6) {
+        // codes at bit 6e, the window aligned; offsets 0 and 2 by the half-word shift of the
+        // pair bytes, the codes that cross a byte from 16-bit windows shifted right (to bits
+        // 0..5) or left (to bits 8..13) and merged with one bitfield insert
+        const uint32_t x0 = w[0], x1 = w[1], x2 = w[2];
+        const uint32_t m = 0x3F3F3F3Fu;
+        const uint32_t da = pk_shr16(__builtin_amdgcn_perm(x1, x0, 0x05020300u), 0, 2) & m;
+        const uint32_t db = pk_shr16(__builtin_amdgcn_perm(x2, x1, 0x07040502u), 0, 2) & m;
+        const uint32_t w1 = pk_shr16(__builtin_amdgcn_perm(x1, x0, 0x04030100u), 6, 6);
+        const uint32_t w2 = pk_shl16(__builtin_amdgcn_perm(x1, x0, 0x05040201u), 4, 4);
+        const uint32_t dc = ((w1 & 0x00FF00FFu) | (w2 & 0xFF00FF00u)) & m;
+        const uint32_t w3 = pk_shr16(__builtin_amdgcn_perm(x2, x1, 0x06050302u), 6, 6);
+        const uint32_t w4 = pk_shl16(__builtin_amdgcn_perm(x2, x1, 0x07060403u), 4, 4);
+        const uint32_t dd = ((w3 & 0x00FF00FFu) | (w4 & 0xFF00FF00u)) & m;
+        return (i32x4){(int)da, (int)db, (int)dc, (int)dd};
     } else {
         const uint32_t f = 0x80808080u;
         return (i32x4){(int)(w[0] ^ f), (int)(w[1] ^ f), (int)(w[2] ^ f), (int)(w[3] ^ f)};
@@ -451,8 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
     constexpr int KS = ring_depth<NV>();                            // value ring depth
     constexpr int NI = (NV + 1) / 2;                                // code loads per value stage
     constexpr int kLoads = NI + 1 + (KVARN_V ? 1 : 0);              // V load instructions per stage
-    static_assert((NK == 2 || NK == 3 || NK == 4 || NK == 8) && (NV == 2 || NV == 3 || NV == 4 || NV == 8),
-                  "2-, 3-, 4- and 8-bit formats");
+    static_assert(NK >= 2 && NK <= 8 && NK != 7 && NV >= 2 && NV <= 8 && NV != 7, "2- to 6- and 8-bit formats");
 
     __shared__ WsLds<NV> S;
 
@@ -605,6 +655,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     } else if constexpr (KWD == 2) {
                         const uint2 x = buf_load8(rc, o);
                         L.c[T][bp][0] = x.x; L.c[T][bp][1] = x.y;
+                    } else if constexpr (KWD == 3) {
+                        const auto x = __builtin_amdgcn_raw_buffer_load_b96(rc, o, 0, 0);
+                        L.c[T][bp][0] = x[0]; L.c[T][bp][1] = x[1]; L.c[T][bp][2] = x[2];
                     } else {
                         const uint4 x = buf_load16(rc, o);
                         L.c[T][bp][0] = x.x; L.c[T][bp][1] = x.y; L.c[T][bp][2] = x.z; L.c[T][bp][3] = x.w;
@@ -623,12 +676,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         float ls = 0.0f;                           // sum of p over the lane's tokens
         uint4 cfirst = make_uint4(0u, 0u, 0u, 0u);
         // three register stages, loads issued two steps ahead of their use
+        // KR register stages (two where three would not fit in the registers: wide KVarN keys)
+        constexpr int KR = (KVARN_K && NK >= 5) ? 2 : 3;
         KLoad X, Y, Z;
         if (J > 0) {
             if (KVARN_K) cfirst = chan_load(0);        // first, so that its wait is exact
             kload(0, X);
             kload(1, Y);
-            kload(2, Z);
+            if (KR == 3) kload(2, Z);
         }
         // the lane's 8 query values (head lane >> 4, dims 8 (lane & 15) ..), log2 domain;
         // KVarN: rotated, H q / 128 (spans 1, 2, 4 in the lane, 8 .. 64 across lanes)
@@ -748,17 +803,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             __syncthreads();
         };
         int j = 0;
+        if constexpr (KR == 3) {
 #pragma unroll 1
-        for (; j + 2 < J; j += 3) {
-            kstep(j, X, KS == 3 ? 0 : j & 3);
-            kload(j + 3, X);
-            kstep(j + 1, Y, KS == 3 ? 1 : (j + 1) & 3);
-            kload(j + 4, Y);
-            kstep(j + 2, Z, KS == 3 ? 2 : (j + 2) & 3);
-            kload(j + 5, Z);
+            for (; j + 2 < J; j += 3) {
+                kstep(j, X, KS == 3 ? 0 : j & 3);
+                kload(j + 3, X);
+                kstep(j + 1, Y, KS == 3 ? 1 : (j + 1) & 3);
+                kload(j + 4, Y);
+                kstep(j + 2, Z, KS == 3 ? 2 : (j + 2) & 3);
+                kload(j + 5, Z);
+            }
+            if (j < J) { kstep(j, X, KS == 3 ? 0 : j & 3); ++j; }
+            if (j < J) { kstep(j, Y, KS == 3 ? 1 : j & 3); ++j; }
+        } else {
+#pragma unroll 1
+            for (; j + 1 < J; j += 2) {
+                kstep(j, X, j % KS);
+                kload(j + 2, X);
+                kstep(j + 1, Y, (j + 1) % KS);
+                kload(j + 3, Y);
+            }
+            if (j < J) { kstep(j, X, j % KS); ++j; }
         }
-        if (j < J) { kstep(j, X, KS == 3 ? 0 : j & 3); ++j; }
-        if (j < J) { kstep(j, Y, KS == 3 ? 1 : j & 3); ++j; }
 #pragma unroll 1
         for (; j <= Jmax; ++j) __syncthreads();
         // normalizer of head q4 over its row
@@ -838,7 +904,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         // 2^s (u - o), o = 2^(N-1), also exact.  The factor 2^s of each dim is removed at the end.
         const int tg = lane >> 4, vblk = (lane >> 2) & 3, vj = lane & 3;
         const int lrun = 4 * NV * vblk + NV * vj;          // byte offset of the run in a row
-        struct VRun { uint32_t x[NV == 8 ? 2 : 1]; };
+        struct VRun { uint32_t x[NV == 8 ? 2 : (NV == 5 || NV == 6) ? 3 : 1]; };
         auto vrun = [&](const uint8_t* cb, int row) -> VRun {
             VRun R;
             const int o = row * RV + lrun;
@@ -849,6 +915,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 R.x[0] = *(const uint32_t*)(cb + o);
             } else if constexpr (NV == 2) {
                 R.x[0] = *(const uint32_t*)(cb + (o & ~3)) >> (8 * (lrun & 3));
+            } else if constexpr (NV == 5 || NV == 6) {
+                // 40 or 48 bits: R0 = bytes 0..3, R1 = bytes 4..7, Rm = bytes 3..6 of the run
+                const uint32_t* w = (const uint32_t*)(cb + (o & ~3));
+                const uint32_t d0 = w[0], d1 = w[1], sh = 8 * (lrun & 3);
+                R.x[0] = __builtin_amdgcn_alignbit(d1, d0, sh);
+                R.x[1] = d1 >> sh;
+                R.x[2] = __builtin_amdgcn_alignbit(R.x[1], R.x[0], 24);
             } else {
                 const uint32_t* w = (const uint32_t*)(cb + (o & ~3));
                 R.x[0] = __builtin_amdgcn_alignbit(w[1], w[0], 8 * (lrun & 3));
@@ -866,13 +939,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         uint32_t k6400 = 0x64006400u;
         asm volatile("" : "+v"(k6400));
         // binary16 pair of code r of tokens a (low half) and b (high half), centred and scaled
+        // by 2^s', s' = min(s, 10 - N) (a window whose code sits higher is shifted down first)
         auto vcode = [&](const VRun& ra, const VRun& rb, int r) __attribute__((always_inline)) -> half2_t {
             constexpr int kM = (1 << NV) - 1;
             const int bit = NV * r, k = bit >> 3, s = bit & 7;
-            const _Float16 c = (_Float16)(-(1024.0f + (float)((1 << (NV - 1)) << s)));
+            const int s2 = s < 10 - NV ? s : 10 - NV;
+            const _Float16 c = (_Float16)(-(1024.0f + (float)((1 << (NV - 1)) << s2)));
             const half2_t cc = {c, c};
             uint32_t w;
-            if constexpr (NV == 8) {
+            if constexpr (NV == 5 || NV == 6) {
+                // window (k, k + 1) of the run: bytes of R0 (k <= 2), Rm (k = 3) or R1 (k >= 4)
+                const int src = k <= 2 ? 0 : k == 3 ? 2 : 1;
+                const uint32_t kk = (uint32_t)(k <= 2 ? k : k == 3 ? 0 : k - 4);
+                const uint32_t sel = kk | ((kk + 1) << 8) | ((4 + kk) << 16) | ((5 + kk) << 24);
+                uint32_t x = __builtin_amdgcn_perm(rb.x[src], ra.x[src], sel);
+                if (s > s2) x >>= (s - s2);
+                w = (x & ((uint32_t)(kM << s2) * 0x00010001u)) | k6400;
+            } else if constexpr (NV == 8) {
                 w = __builtin_amdgcn_perm(rb.x[k >> 2], ra.x[k >> 2],
                                           (uint32_t)(k & 3) | 0x0C000C00u | ((uint32_t)(4 + (k & 3)) << 16)) | k6400;
             } else {
@@ -987,7 +1070,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             // page's c_V
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                f32x4 v = D[r] * (1.0f / (float)(1 << ((NV * r) & 7)));
+                const int s = (NV * r) & 7;
+                f32x4 v = D[r] * (1.0f / (float)(1 << (s < 10 - NV ? s : 10 - NV)));
                 if (AFF_V) v += mh4;
                 if (KVARN_V) v *= cvr[r];
 #pragma unroll
@@ -1184,7 +1268,8 @@ int ws_value_switch(int op, int fmt_v, const DecodeArgs* a, int n_wgs, hipStream
     case FV: return op == 0 ? launch_ws_pair<FK, FV>(*a, n_wgs, st) : occ_ws<FK, FV>();
     switch (fmt_v) {
         KVQ_WS_CASE(1) KVQ_WS_CASE(2) KVQ_WS_CASE(3) KVQ_WS_CASE(4) KVQ_WS_CASE(5) KVQ_WS_CASE(6)
-        KVQ_WS_CASE(11) KVQ_WS_CASE(12) KVQ_WS_CASE(13) KVQ_WS_CASE(14) KVQ_WS_CASE(15) KVQ_WS_CASE(18)
+        KVQ_WS_CASE(7) KVQ_WS_CASE(8) KVQ_WS_CASE(9) KVQ_WS_CASE(10) KVQ_WS_CASE(11) KVQ_WS_CASE(12)
+        KVQ_WS_CASE(13) KVQ_WS_CASE(14) KVQ_WS_CASE(15) KVQ_WS_CASE(16) KVQ_WS_CASE(17) KVQ_WS_CASE(18)
     default: return op == 0 ? (int)hipErrorInvalidValue : 0;
     }
 #undef KVQ_WS_CASE

@@ -6,15 +6,16 @@ namespace kvq {
 int decode_fast_w2(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
 int decode_fast_w3(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
 int decode_fast_w4(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+int decode_fast_w5(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
+int decode_fast_w6(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
 int decode_fast_w8(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream);
 
 namespace {
 
-// formats of the fast kernel: qN_0, qN_1 and kvarnN for N = 2, 3, 4, 8
+// formats of the fast kernel: every quantized format (qN_0, qN_1, kvarnN)
 bool fast_format(int f)
 {
-    return f >= 1 && f <= 18 && fkind(f) != KIND_BF16 &&
-           (fbits(f) == 2 || fbits(f) == 3 || fbits(f) == 4 || fbits(f) == 8);
+    return f >= 1 && f <= 18 && fkind(f) != KIND_BF16;
 }
 
 int by_width(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream)
@@ -23,6 +24,8 @@ int by_width(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void*
     case 2: return decode_fast_w2(op, a, fmt_k, fmt_v, n_wgs, stream);
     case 3: return decode_fast_w3(op, a, fmt_k, fmt_v, n_wgs, stream);
     case 4: return decode_fast_w4(op, a, fmt_k, fmt_v, n_wgs, stream);
+    case 5: return decode_fast_w5(op, a, fmt_k, fmt_v, n_wgs, stream);
+    case 6: return decode_fast_w6(op, a, fmt_k, fmt_v, n_wgs, stream);
     case 8: return decode_fast_w8(op, a, fmt_k, fmt_v, n_wgs, stream);
     default: return op == 0 ? (int)hipErrorInvalidValue : 0;
     }

@@ -151,12 +151,14 @@ def test_mixed_key_value_formats_small(fmt):
 
 FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4_1", "q4_1/kvarn4",
               "q8_0/q4_0", "q4_0/q8_0", "q8_1/q8_1", "kvarn8/q8_1", "q8_0/kvarn3", "q3_0/q3_1",
-              "q3_1/kvarn3", "kvarn3/q3_0", "q2_0/q2_1", "q2_1/kvarn8", "kvarn2/kvarn2", "kvarn8/q2_0"]
+              "q3_1/kvarn3", "kvarn3/q3_0", "q2_0/q2_1", "q2_1/kvarn8", "kvarn2/kvarn2", "kvarn8/q2_0",
+              "q5_0/q5_1", "q5_1/kvarn5", "kvarn5/q6_1", "q6_0/q6_0", "q6_1/kvarn6", "kvarn6/q5_0",
+              "q6_0/q4_0", "q4_1/q6_1", "kvarn5/kvarn5"]
 
 
 @pytest.mark.parametrize("fmt", FAST_PAIRS)
 def test_fast_kernel_mixed_pairs_many_pages(fmt):
-    """The fast kernel (2-, 3-, 4- and 8-bit codes) with different key and value formats: 8
+    """The fast kernel (every code width) with different key and value formats: 8
     KV heads, 24k tokens (many pages per pair of waves, a partial last page, a 1024-token
     tail), all heads checked."""
     wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
