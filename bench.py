@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--append-reps", type=int, default=4)
     p.add_argument("--cpu-units", type=int, default=16, help="(layer, kv head) units of the CPU sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--kld", action="store_true",
+                   help="attention-fidelity sweep: median KL over query heads, format x tail x context")
     p.add_argument("--copy-probe", type=int, default=0,
                    help="only run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -175,8 +177,63 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
     }
 
 
+KLD_FMTS = ["q2_0", "q3_0", "q4_0", "q5_0", "q6_0", "q8_0", "kvarn2", "kvarn3", "kvarn4", "kvarn5",
+            "kvarn6", "kvarn8"]
+
+
+def kld_sweep(args):
+    """Median over the 32 query heads of KL(P || Q) (attention over exact BF16 keys vs over the
+    cache's keys) for every format of the pages' KLD table, tails 0 / 1024 / 2048 and contexts
+    4k / 16k / 64k: one layer, 8 KV heads, synthetic keys of the 64k KVarN sweep workload
+    (N(0,1) with four 15x channels), its seeded queries.  Also times the KL kernel."""
+    import numpy as np
+    import torch
+    from mixed_precision_quantized_amd import kvq, synth
+    wl, H, QH = "c3_kvarn_ctx65536", 8, 32
+    ctxs = [4096, 16384, 65536]
+    keys = torch.stack([synth.kv_rows(wl, 0, 0, h, 0, 0, max(ctxs), "cuda") for h in range(H)], 1)
+    vals = torch.stack([synth.kv_rows(wl, 0, 0, h, 1, 0, max(ctxs), "cuda") for h in range(H)], 1)
+    kb, vb = synth.to_bf16_bits(keys).contiguous(), synth.to_bf16_bits(vals).contiguous()
+    q = synth.to_bf16_bits(synth.q_rows(wl, 0, 0, 0, QH, "cuda")).contiguous()
+    stream = torch.cuda.current_stream()
+    table = []
+    for ctx in ctxs:
+        k_ref = kb[:ctx].contiguous()
+        for fmt in KLD_FMTS:
+            for tail in (0, 1024, 2048):
+                cache = kvq.Cache(1, H, QH, fmt, tail_tokens=tail, n_seqs=1, max_tokens=ctx)
+                t = 0
+                while t < ctx:
+                    c = min(16384, ctx - t)
+                    cache.append(0, [0], [c], kb[t:t + c].contiguous(), vb[t:t + c].contiguous())
+                    t += c
+                out = cache.attn_kld(0, 0, q, k_ref)
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                for _ in range(3):
+                    out = cache.attn_kld(0, 0, q, k_ref)
+                a1.record(stream)
+                torch.cuda.synchronize()
+                us = a0.elapsed_time(a1) * 1e3 / 3
+                n, n_q = cache.seq_get(0, 0)
+                byts = H * (n_q * stream_bytes(fmt) + (n - n_q) * 256 + n * 256)
+                kl = out.cpu().numpy().astype(np.float64)
+                table.append({"ctx": ctx, "fmt": fmt, "tail": tail, "kld_median": float(np.median(kl)),
+                              "kld_max": float(kl.max()), "us": round(us, 1),
+                              "gbs": round(byts / (us * 1e-6) / 1e9, 1)})
+                del cache
+        print("  kld ctx %d done" % ctx, file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "attention KL divergence, median over query heads", "unit": "nats",
+                      "data": "synthetic", "config": {"workload": "1 layer x 8 KV heads x 32 q heads x d128, "
+                      "keys N(0,1) with four 15x channels, seeded queries, softmax scale 1/sqrt(128)"},
+                      "table": table}), flush=True)
+
+
 def main():
     args = parse()
+    if args.kld:
+        kld_sweep(args)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)." % args.gpus, file=sys.stderr)

@@ -135,6 +135,24 @@ int kv_decode_attn(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t
                    const void* q, int32_t q_dtype, float softmax_scale, float* out,
                    void* workspace, int64_t ws_bytes, void* stream);
 
+/* Bytes of workspace needed by kv_attn_kld at any length up to max_tokens (partial
+ * results of one call; no initialization needed; calls sharing it must be stream-ordered). */
+int64_t kv_attn_kld_workspace_bytes(const kv_cache* cache);
+
+/* Attention fidelity of the cache for one (sequence, layer): for every query head h,
+ *   kld[h] = KL(P || Q) = sum_t P_t log(P_t / Q_t),
+ *   P_t = softmax_t(softmax_scale * q_h . k_ref_t),  Q_t = softmax_t(softmax_scale * q_h . k_t)
+ * over t < n, where k_ref holds the exact keys of every token and k_t the keys the cache
+ * holds (dequantized rows t < n_q, BF16 ring rows after).  A model-free analogue of the
+ * pages' KL-divergence quality measure ("BeeLLama.cpp v0.4.0: KVarN, KV 정밀도 테일
+ * (precision tail), q2_0-q3_1", KLD table), on attention weights rather than output tokens.
+ * q: [n_q_heads][128] of q_dtype; k_ref: device [n][n_kv_heads][128] BF16 (the canonical
+ * keys the cache was filled from, token-major); kld: device float32 [n_q_heads].  Reads
+ * the cache only.  Errors: KV_EINVAL, KV_EEMPTY (n == 0), KV_ESIZE (workspace). */
+int kv_attn_kld(kv_cache* cache, int32_t layer, int32_t seq_id, const void* q, int32_t q_dtype,
+                float softmax_scale, const void* k_ref, float* kld, void* workspace,
+                int64_t ws_bytes, void* stream);
+
 /* Spill the tail of one sequence: n_q = max(n_q, G*floor(max(0, n - keep_tokens)/G)),
  * encoding the BF16 ring rows that cross the boundary.  layer == -1: all layers.
  * 0 <= keep_tokens <= tail_tokens.  Errors: KV_EINVAL. */

@@ -456,4 +456,213 @@ int device_cu_count()
     return cache[dev];
 }
 
+// ------------------------------------------------------------------------------------------
+// Attention fidelity: per query head h, KL(P || Q) with P_t = softmax_t(s_t), s_t = scale
+// q_h . k_t over the exact BF16 keys, and Q_t the same over the keys the cache holds
+// (dequantized rows below n_q, the BF16 ring above).  With D_t = s_t - s'_t and any
+// constant c,
+//   KL = sum_t P_t (D_t - c) + log sum_t P_t e^{-(D_t - c)}.
+// Two passes over the keys.  The first accumulates m = max s, l = sum e^{s - m} and
+// A = sum e^{s - m} D, which give c = E_P[D] per head (a weighted mean: no cancellation).
+// The second accumulates A = sum e^{s - m} (D - c) and B = sum e^{s - m} (e^{-(D - c)} - 1)
+// with that c, so that KL = A / L + log1p(B / L) adds two small terms: quantization can
+// shift every score by nearly the same amount (a common bias of the keys along q), and
+// measured from any other reference both terms would be large and cancel.  A model-free
+// analogue of the KL-divergence quality measure ("BeeLLama.cpp v0.4.0: KVarN, KV 정밀도
+// 테일", the KLD table; "Экспериментальные методы квантизации KV-кэша в BeeLLama.cpp
+// v0.4.0", the section on measuring quality): the same statistic, on attention weights
+// instead of output tokens.
+namespace {
+
+struct KldState { float m, l, A, B; };
+
+__device__ __forceinline__ void kld_add(KldState& st, float s, float e, bool valid)
+{
+    if (!valid) return;
+    const float mn = fmaxf(st.m, s);
+    const float r = expf(st.m - mn), w = expf(s - mn);
+    st.l = fmaf(st.l, r, w);
+    st.A = fmaf(st.A, r, w * e);
+    // (a token whose cache score exceeds the exact one by more than 60 nats over c counts
+    // as 60: no overflow; such a cache is far off in any case)
+    st.B = fmaf(st.B, r, w * expm1f(fminf(-e, 60.0f)));
+    st.m = mn;
+}
+
+__device__ __forceinline__ void kld_combine(KldState& a, const KldState& b)
+{
+    const float M = fmaxf(a.m, b.m);
+    const float ea = expf(a.m - M), eb = expf(b.m - M);
+    a.l = a.l * ea + b.l * eb;
+    a.A = a.A * ea + b.A * eb;
+    a.B = a.B * ea + b.B * eb;
+    a.m = M;
+}
+
+template <int FK>
+__global__ __launch_bounds__(256) void k_kld(KldArgs a)
+{
+    constexpr int KIND = fkind(FK);
+    __shared__ float qs[kG][kD], qrot[kG][kD];
+    __shared__ KldState ws[4][kG];
+    const int tid = threadIdx.x;
+    const int head = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
+    const CacheGeom& g = a.g;
+    const char* kst = stream_cptr(g, a.seq, a.layer, head, 0);
+    for (int i = tid; i < kG * kD; i += blockDim.x) {
+        const int hh = i / kD, d = i % kD;
+        const int64_t qi = (int64_t)(head * kG + hh) * kD + d;
+        const float qv = (a.q_dtype ? ((const float*)a.q)[qi] : bf16_to_f32(((const uint16_t*)a.q)[qi])) * a.scale;
+        qs[hh][d] = qv;
+        qrot[hh][d] = qv;
+    }
+    __syncthreads();
+    if (KIND == KIND_KVARN) {
+        lds_fwht(qrot);
+        for (int i = tid; i < kG * kD; i += blockDim.x) qrot[i / kD][i % kD] *= (1.0f / 128.0f);
+        __syncthreads();
+    }
+    const int wave = tid >> 6, lane = tid & 63, slot = lane >> 3, part = lane & 7;
+    float qo[kG][16], qc[kG][16];
+#pragma unroll
+    for (int h = 0; h < kG; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            qo[h][j] = qs[h][16 * part + j];
+            qc[h][j] = qrot[h][16 * part + j];
+        }
+    KldState st[kG];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) st[h] = {kNegBig, 0.0f, 0.0f, 0.0f};
+    float cref[kG];                          // pass 2: c = E_P[D] of the head (pass 1: 0)
+#pragma unroll
+    for (int h = 0; h < kG; ++h) cref[h] = a.pass ? a.cref[head * kG + h] : 0.0f;
+    const int64_t t0 = (int64_t)sp * kKldTokens, t1 = min<int64_t>(t0 + kKldTokens, a.n);
+    for (int64_t tb = t0 + 8 * wave; tb < t1; tb += 32) {
+        const int64_t t = tb + slot;
+        const bool valid = t < t1;
+        const int64_t tc = valid ? t : t1 - 1;
+        float k[16], kx[16];
+        const bool quant = tc < a.n_q;
+        if (quant) {
+            float ck[16];
+            if constexpr (KIND == KIND_KVARN) {
+                const uint16_t* cks = (const uint16_t*)(kst + g.k.cscale + (tc / kPage) * 256) + 16 * part;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) ck[j] = fp16_to_f32(cks[j]);
+            }
+            dequant16<FK>(kst, g.k, tc, part, ck, k);
+        } else {
+            ring16(kst, g.k, tc % g.ring_slots, part, k);
+        }
+        {
+            const uint4* pr = (const uint4*)(a.k_ref + (tc * g.n_kv_heads + head) * kD + 16 * part);
+            const uint4 w0 = pr[0], w1 = pr[1];
+            const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kx[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
+                kx[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            float se = 0.0f, sq = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                se = fmaf(qo[h][j], kx[j], se);
+                sq = fmaf((KIND == KIND_KVARN && quant) ? qc[h][j] : qo[h][j], k[j], sq);
+            }
+            se = sum8(se);
+            sq = sum8(sq);
+            kld_add(st[h], se, (se - sq) - cref[h], valid);
+        }
+    }
+    // slots of a wave (lanes 8 apart hold different slots; the 8 lanes of a slot agree)
+#pragma unroll
+    for (int h = 0; h < kG; ++h)
+#pragma unroll
+        for (int o = 8; o < 64; o <<= 1) {
+            KldState b = {__shfl_xor(st[h].m, o), __shfl_xor(st[h].l, o), __shfl_xor(st[h].A, o),
+                          __shfl_xor(st[h].B, o)};
+            kld_combine(st[h], b);
+        }
+    if (lane == 0)
+#pragma unroll
+        for (int h = 0; h < kG; ++h) ws[wave][h] = st[h];
+    __syncthreads();
+    if (tid < kG) {
+        KldState r = ws[0][tid];
+        for (int w = 1; w < 4; ++w) kld_combine(r, ws[w][tid]);
+        float* pp = a.partials + (((int64_t)head * a.splits + sp) * kMaxGroup + tid) * 4;
+        pp[0] = r.m; pp[1] = r.l; pp[2] = r.A; pp[3] = r.B;
+    }
+}
+
+// One thread per query head: merge the splits; pass 1 leaves c = A / L, pass 2 writes
+// KL = A / L + log1p(B / L).
+__global__ __launch_bounds__(64) void k_kld_merge(KldArgs a)
+{
+    const int qh = blockIdx.x * 64 + threadIdx.x;
+    if (qh >= a.g.n_q_heads) return;
+    const int head = qh / kG, h = qh % kG;
+    KldState r = {kNegBig, 0.0f, 0.0f, 0.0f};
+    for (int sp = 0; sp < a.splits; ++sp) {
+        const float* pp = a.partials + (((int64_t)head * a.splits + sp) * kMaxGroup + h) * 4;
+        kld_combine(r, KldState{pp[0], pp[1], pp[2], pp[3]});
+    }
+    if (a.pass == 0) a.cref[qh] = r.A / r.l;
+    else a.out[qh] = r.A / r.l + log1pf(r.B / r.l);
+}
+
+template <int F>
+int launch_kld_fmt(const KldArgs& a, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_kld<F>, dim3(a.g.n_kv_heads * a.splits), dim3(256), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+int launch_kld_pass(const KldArgs& a, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    int rc;
+    switch (a.g.fmt_k) {
+    case 0: rc = launch_kld_fmt<0>(a, st); break;
+    case 1: rc = launch_kld_fmt<1>(a, st); break;
+    case 2: rc = launch_kld_fmt<2>(a, st); break;
+    case 3: rc = launch_kld_fmt<3>(a, st); break;
+    case 4: rc = launch_kld_fmt<4>(a, st); break;
+    case 5: rc = launch_kld_fmt<5>(a, st); break;
+    case 6: rc = launch_kld_fmt<6>(a, st); break;
+    case 7: rc = launch_kld_fmt<7>(a, st); break;
+    case 8: rc = launch_kld_fmt<8>(a, st); break;
+    case 9: rc = launch_kld_fmt<9>(a, st); break;
+    case 10: rc = launch_kld_fmt<10>(a, st); break;
+    case 11: rc = launch_kld_fmt<11>(a, st); break;
+    case 12: rc = launch_kld_fmt<12>(a, st); break;
+    case 13: rc = launch_kld_fmt<13>(a, st); break;
+    case 14: rc = launch_kld_fmt<14>(a, st); break;
+    case 15: rc = launch_kld_fmt<15>(a, st); break;
+    case 16: rc = launch_kld_fmt<16>(a, st); break;
+    case 17: rc = launch_kld_fmt<17>(a, st); break;
+    case 18: rc = launch_kld_fmt<18>(a, st); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_kld_merge, dim3((a.g.n_q_heads + 63) / 64), dim3(64), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_kld(const KldArgs& args, void* stream)
+{
+    KldArgs a = args;
+    for (a.pass = 0; a.pass < 2; ++a.pass) {
+        const int rc = launch_kld_pass(a, stream);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
 }  // namespace kvq

@@ -346,6 +346,45 @@ int64_t kv_decode_workspace_bytes(const kv_cache* c, int32_t n_seqs)
     return align256((int64_t)kMaxDecodeWGs * kPartialFloats * 4);
 }
 
+int64_t kv_attn_kld_workspace_bytes(const kv_cache* c)
+{
+    if (!c) return KV_EINVAL;
+    const int64_t splits = (c->cfg.max_tokens + kKldTokens - 1) / kKldTokens;
+    return align256(splits * c->cfg.n_kv_heads * kMaxGroup * 4 * 4) + align256(c->cfg.n_q_heads * 4);
+}
+
+int kv_attn_kld(kv_cache* c, int32_t layer, int32_t seq_id, const void* q, int32_t q_dtype,
+                float softmax_scale, const void* k_ref, float* kld, void* workspace,
+                int64_t ws_bytes, void* stream)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (seq_id < 0 || seq_id >= c->cfg.n_seqs) return KV_EINVAL;
+    if (!q || !k_ref || !kld || !workspace) return KV_EINVAL;
+    if (q_dtype != KV_IN_BF16 && q_dtype != KV_IN_F32) return KV_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+        return KV_EINVAL;
+    if (ws_bytes < kv_attn_kld_workspace_bytes(c)) return KV_ESIZE;
+    const int64_t n = n_at(c, seq_id, layer);
+    if (n == 0) return KV_EEMPTY;
+    KldArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.g = c->geom;
+    a.layer = layer;
+    a.seq = seq_id;
+    a.n = n;
+    a.n_q = nq_at(c, seq_id, layer);
+    a.q_dtype = q_dtype;
+    a.scale = softmax_scale;
+    a.splits = (int32_t)((n + kKldTokens - 1) / kKldTokens);
+    a.q = q;
+    a.k_ref = (const uint16_t*)k_ref;
+    a.partials = (float*)workspace;
+    const int64_t splits_max = (c->cfg.max_tokens + kKldTokens - 1) / kKldTokens;
+    a.cref = (float*)((char*)workspace + align256(splits_max * c->cfg.n_kv_heads * kMaxGroup * 4 * 4));
+    a.out = kld;
+    return launch_kld(a, stream) ? KV_EDEVICE : KV_OK;
+}
+
 int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                    const void* q, int32_t q_dtype, float softmax_scale, float* out,
                    void* workspace, int64_t ws_bytes, void* stream)

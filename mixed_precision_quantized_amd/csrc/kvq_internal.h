@@ -97,6 +97,25 @@ struct DecodeArgs {
     DecodeSeq seqs[kMaxSeqsPerLaunch];
 };
 
+// Attention fidelity of one (sequence, layer): per query head, the KL divergence of the
+// attention distribution over the cache's keys from the one over exact BF16 keys.
+constexpr int kKldTokens = 2048;   // tokens per split of the KL kernel
+struct KldArgs {
+    CacheGeom g;
+    int32_t layer, seq;
+    int64_t n, n_q;
+    int32_t q_dtype;      // 0 bf16, 1 fp32
+    float scale;          // softmax scale (natural-log domain)
+    int32_t splits;       // ceil(n / kKldTokens)
+    int32_t pass;         // 0: c = E_P[D] per head into cref; 1: KL into out
+    const void* q;        // [n_q_heads][128]
+    const uint16_t* k_ref;   // [n][n_kv_heads][128] bf16
+    float* partials;      // [n_kv_heads][splits][kMaxGroup][4]: m, l, A, B
+    float* cref;          // [n_q_heads]
+    float* out;           // [n_q_heads]
+};
+int launch_kld(const KldArgs& a, void* stream);               // split kernel + merge (kvq_decode.hip)
+
 constexpr int kPartialFloats = kMaxGroup * (kD + 2);   // m, l, acc[128] per query head
 constexpr int kMaxDecodeWGs = 8192;
 

@@ -72,6 +72,10 @@ def lib():
         L.kv_decode_workspace_bytes.restype = _i64
         L.kv_decode_attn.argtypes = [_vp, _i32, _i32, _i32p, _vp, _i32, ctypes.c_float, _vp, _vp, _i64, _vp]
         L.kv_decode_attn.restype = ctypes.c_int
+        L.kv_attn_kld_workspace_bytes.argtypes = [_vp]
+        L.kv_attn_kld_workspace_bytes.restype = _i64
+        L.kv_attn_kld.argtypes = [_vp, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _vp, _i64, _vp]
+        L.kv_attn_kld.restype = ctypes.c_int
         L.kv_spill_tail.argtypes = [_vp, _i32, _i32, _i32, _vp]
         L.kv_spill_tail.restype = ctypes.c_int
         L.kv_seq_get.argtypes = [_vp, _i32, _i32, _i64p, _i64p]
@@ -180,6 +184,25 @@ class Cache:
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.ws.data_ptr()),
                                   self.ws.numel(), _stream(stream))
         _check(rc, "kv_decode_attn")
+        return out
+
+    def attn_kld(self, layer, seq_id, q, k_ref, softmax_scale=None, stream=None):
+        """KL(P || Q) per query head of the attention distributions over the exact keys
+        (P; k_ref: device bfloat16 or int16 bits [n][n_kv_heads][128]) and over the keys the
+        cache holds (Q).  q: device [n_q_heads][128] bfloat16/float32 -> float32 [n_q_heads]."""
+        assert q.is_contiguous() and k_ref.is_contiguous() and k_ref.element_size() == 2
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(128)
+        n_ws = int(lib().kv_attn_kld_workspace_bytes(self.h))
+        _check(n_ws if n_ws < 0 else 0, "kv_attn_kld_workspace_bytes")
+        ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
+        out = torch.empty(self.cfg.n_q_heads, dtype=torch.float32, device=q.device)
+        dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
+        rc = lib().kv_attn_kld(self.h, int(layer), int(seq_id), ctypes.c_void_p(q.data_ptr()), dt,
+                               float(softmax_scale), ctypes.c_void_p(k_ref.data_ptr()),
+                               ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                               ws.numel(), _stream(stream))
+        _check(rc, "kv_attn_kld")
         return out
 
     def spill(self, layer, seq_id, keep_tokens, stream=None):

@@ -79,6 +79,9 @@ def lib():
                                     _u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p,
                                     ctypes.c_int, _f64p, ctypes.c_double, _f64p]
         L.kvo_attention.restype = ctypes.c_int
+        L.kvo_attention_kld.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _u8p, _u16p, _u16p,
+                                        _u16p, ctypes.c_int, _f64p, ctypes.c_double, _f64p]
+        L.kvo_attention_kld.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -287,4 +290,23 @@ def attention(n, n_q, fmt_k, fmt_v, kq, vq, k_tail, v_tail, q, sigma):
                              _p(out, _f64p))
     if rc != 0:
         raise ValueError("attention rc=%d" % rc)
+    return out
+
+
+def attention_kld(n, n_q, fmt_k, kq, k_exact, q, sigma):
+    """KL(P || Q) per query head: P over the exact bf16 keys k_exact ([n][128] bits, every
+    token), Q over the cache's keys (kq = (codes, scales, cscale) of rows [0, n_q), the
+    exact rows after).  q: [g][128] values.  Returns [g] float64."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    g = q.shape[0]
+    out = np.zeros(g, np.float64)
+    c, s, cs = kq if kq is not None else (None, None, None)
+    c = np.ascontiguousarray(c, dtype=np.uint8) if c is not None and c.size else None
+    s = np.ascontiguousarray(s, dtype=np.uint16) if s is not None and s.size else None
+    cs = np.ascontiguousarray(cs, dtype=np.uint16) if cs is not None and cs.size else None
+    ke = np.ascontiguousarray(k_exact, dtype=np.uint16)
+    rc = lib().kvo_attention_kld(int(n), int(n_q), fmt_k, _p(c, _u8p), _p(s, _u16p), _p(cs, _u16p),
+                                 _p(ke, _u16p), g, _p(q, _f64p), float(sigma), _p(out, _f64p))
+    if rc != 0:
+        raise ValueError("attention_kld rc=%d" % rc)
     return out

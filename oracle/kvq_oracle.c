@@ -547,3 +547,58 @@ int kvo_attention(int64_t n, int64_t n_q, int fmt_k, int fmt_v,
     free(s);
     return 0;
 }
+
+/* ======================================================================== */
+/* Attention fidelity (KL divergence of attention distributions)           */
+/* ======================================================================== */
+
+int kvo_attention_kld(int64_t n, int64_t n_q, int fmt_k, const uint8_t* kq_codes,
+                      const uint16_t* kq_scales, const uint16_t* kq_cscale,
+                      const uint16_t* k_exact, int g, const double* q, double sigma, double* kld)
+{
+    int N, kind, cb, sb, pb;
+    if (kvo_format_info(fmt_k, &N, &kind, &cb, &sb, &pb) != 0) return -1;
+    if (n == 0) return -4;
+    if (n < 0 || n_q < 0 || n_q > n || g <= 0 || !k_exact || !q || !kld) return -1;
+    double* K = (double*)malloc(sizeof(double) * (size_t)n * 128);
+    double* se = (double*)malloc(sizeof(double) * (size_t)n);
+    double* sq = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!K || !se || !sq) { free(K); free(se); free(sq); return -1; }
+    /* the cache's keys: dequantized below n_q, the exact bf16 rows above */
+    if (n_q > 0) kvo_dequant_stream(fmt_k, n_q, kq_codes, kq_scales, kq_cscale, K);
+    for (int64_t t = n_q; t < n; ++t)
+        for (int i = 0; i < 128; ++i) K[t * 128 + i] = (double)kvo_f32_from_bf16(k_exact[t * 128 + i]);
+    for (int h = 0; h < g; ++h) {
+        const double* qh = q + h * 128;
+        double Me = -INFINITY, Mq = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            double a = 0.0, b = 0.0;
+            for (int i = 0; i < 128; ++i) {
+                a += qh[i] * (double)kvo_f32_from_bf16(k_exact[t * 128 + i]);
+                b += qh[i] * K[t * 128 + i];
+            }
+            se[t] = sigma * a;
+            sq[t] = sigma * b;
+            if (se[t] > Me) Me = se[t];
+            if (sq[t] > Mq) Mq = sq[t];
+        }
+        /* log-normalizers of both distributions */
+        double Le = 0.0, Lq = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            Le += exp(se[t] - Me);
+            Lq += exp(sq[t] - Mq);
+        }
+        const double lse_e = Me + log(Le), lse_q = Mq + log(Lq);
+        /* sum_t P_t (log P_t - log Q_t) */
+        double acc = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            const double lp = se[t] - lse_e, lq = sq[t] - lse_q;
+            acc += exp(lp) * (lp - lq);
+        }
+        kld[h] = acc;
+    }
+    free(K);
+    free(se);
+    free(sq);
+    return 0;
+}

@@ -146,6 +146,18 @@ int kvo_attention(int64_t n, int64_t n_q, int fmt_k, int fmt_v,
                   const uint16_t* k_tail, const uint16_t* v_tail,
                   int g, const double* q, double sigma, double* out);
 
+/* ---- attention fidelity --------------------------------------------------------------- */
+/* Kullback-Leibler divergence of the attention distribution over the cache's keys from the
+ * one over the exact keys, per query head (a model-free analogue of the KLD quality
+ * measure of "BeeLLama.cpp v0.4.0: KVarN, KV 정밀도 테일 (precision tail), q2_0-q3_1", KLD
+ * table):  P_t = softmax_t(sigma q_h . x_t) over the exact bf16 keys x (k_exact, all n
+ * tokens, [n][128]),  Q_t = softmax_t(sigma q_h . k_t) over the dequantized rows t < n_q
+ * and the exact rows after (the bf16 tail),  kld[h] = sum_t P_t (log P_t - log Q_t), in
+ * binary64.  Returns 0, -1 on bad arguments, -4 when n == 0. */
+int kvo_attention_kld(int64_t n, int64_t n_q, int fmt_k, const uint8_t* kq_codes,
+                      const uint16_t* kq_scales, const uint16_t* kq_cscale,
+                      const uint16_t* k_exact, int g, const double* q, double sigma, double* kld);
+
 /* Convenience for tests: dequantize rows [0, n_q) of one stream to binary64
  * (out: [n_q][128]). */
 int kvo_dequant_stream(int fmt, int64_t n_q, const uint8_t* codes, const uint16_t* scales,

@@ -1,0 +1,71 @@
+"""GPU parity of the attention-fidelity entry point (kv_attn_kld) against the oracle's
+binary64 KL divergence, through the C ABI.
+
+Every format family, with a tail of 0 and 300 tokens, 5000 tokens and ragged appends; one
+65,536-token layer of 8 KV heads (kvarn4, tail 1024) at full size.  The kernel computes the
+scores in binary32, so the divergence D_t = s_t - s'_t of each token carries an absolute
+error of a few ulps of the scores (~1e-6); KL ~ Var_P(D) / 2 then has a relative error
+of about 2e-6 / std_P(D), which is below 1e-3 for every format here (std_P(D) >= 1e-2 at
+8 bits with the 15x outlier channels).  The bound in the test is 1e-2 relative, plus 1e-9
+absolute for the exact (zero) cases.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_quantized_amd import kvq
+
+import kvq_testlib as T
+
+pytestmark = pytest.mark.gpu
+SIGMA = 1.0 / math.sqrt(128)
+RTOL, ATOL = 1e-2, 1e-9
+
+
+def _check(cache, fmt, wl, n, H, q_heads):
+    rows = [T.canon_rows(wl, 0, 0, h, 0, 0, n) for h in range(H)]
+    k_ref = torch.from_numpy(np.ascontiguousarray(np.stack(rows, 1)).view(np.int16)).cuda()
+    q = T.query(wl, 0, 0, 0, q_heads, "cuda")
+    got = cache.attn_kld(0, 0, q, k_ref).cpu().numpy().astype(np.float64)
+    _, n_q = cache.seq_get(0, 0)
+    qv = T.query_values(q)
+    f = O.FORMAT_NAMES.index(fmt)
+    g = q_heads // H
+    for h in range(H):
+        kq = O.encode_stream(f, n_q, rows[h]) if n_q else None
+        ref = O.attention_kld(n, n_q, f, kq, rows[h], qv[g * h:g * (h + 1)], SIGMA)
+        err = np.abs(got[g * h:g * (h + 1)] - ref)
+        assert np.all(err <= RTOL * ref + ATOL), "%s head %d: gpu %s oracle %s" % (fmt, h, got[g * h:g * (h + 1)], ref)
+    return got
+
+
+@pytest.mark.parametrize("tail", [0, 300])
+@pytest.mark.parametrize("fmt", ["q2_0", "q3_1", "q4_0", "q5_1", "q6_0", "q8_0", "kvarn2", "kvarn4",
+                                 "kvarn6", "bf16"])
+def test_kld_matches_oracle(fmt, tail):
+    wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
+    n, H = 5000, 2
+    cache = kvq.Cache(1, H, 8, fmt, tail_tokens=tail, n_seqs=1, max_tokens=n)
+    T.fill(cache, wl, 0, [0], H, n, T.chunk_list(n, [1777, 1, 999]))
+    got = _check(cache, fmt, wl, n, H, 8)
+    if fmt == "bf16":
+        assert np.all(got == 0.0)
+
+
+def test_kld_full_size_layer():
+    wl = "c3_kvarn_ctx65536"
+    n, H = 65536, 8
+    cache = kvq.Cache(1, H, 32, "kvarn4", tail_tokens=1024, n_seqs=1, max_tokens=n)
+    T.fill(cache, wl, 0, [0], H, n, [16384] * 4)
+    _check(cache, "kvarn4", wl, n, H, 32)
+
+
+def test_kld_errors():
+    cache = kvq.Cache(1, 1, 4, "q4_0", tail_tokens=0, n_seqs=1, max_tokens=256)
+    q = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")
+    k_ref = torch.zeros(1, 1, 128, dtype=torch.int16, device="cuda")
+    with pytest.raises(kvq.KVError):
+        cache.attn_kld(0, 0, q, k_ref)                      # empty sequence
