@@ -79,6 +79,10 @@ def lib():
                                     _u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p,
                                     ctypes.c_int, _f64p, ctypes.c_double, _f64p]
         L.kvo_attention.restype = ctypes.c_int
+        L.kvo_prefill_attention.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_int, _u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p,
+                                            _u16p, ctypes.c_int, _f64p, ctypes.c_double, _f64p]
+        L.kvo_prefill_attention.restype = ctypes.c_int
         L.kvo_attention_kld.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _u8p, _u16p, _u16p,
                                         _u16p, ctypes.c_int, _f64p, ctypes.c_double, _f64p]
         L.kvo_attention_kld.restype = ctypes.c_int
@@ -309,4 +313,31 @@ def attention_kld(n, n_q, fmt_k, kq, k_exact, q, sigma):
                                  _p(ke, _u16p), g, _p(q, _f64p), float(sigma), _p(out, _f64p))
     if rc != 0:
         raise ValueError("attention_kld rc=%d" % rc)
+    return out
+
+
+def prefill_attention(n, n_q, n_new, fmt_k, fmt_v, kq, vq, k_tail, v_tail, q, sigma):
+    """Causal attention of the last n_new tokens: q [n_new][g][128] values; kq/vq as in
+    attention(); k_tail/v_tail: bf16 rows of tokens [n_q, n).  Returns [n_new][g][128]."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    n_new_, g = q.shape[0], q.shape[1]
+    assert n_new_ == n_new
+    out = np.zeros((n_new, g, 128), np.float64)
+
+    def parts(t):
+        if t is None:
+            return None, None, None
+        c, s, cs = t
+        c = np.ascontiguousarray(c, dtype=np.uint8) if c is not None and c.size else None
+        s = np.ascontiguousarray(s, dtype=np.uint16) if s is not None and s.size else None
+        cs = np.ascontiguousarray(cs, dtype=np.uint16) if cs is not None and cs.size else None
+        return _p(c, _u8p), _p(s, _u16p), _p(cs, _u16p)
+
+    kt = np.ascontiguousarray(k_tail, dtype=np.uint16) if n > n_q else None
+    vt = np.ascontiguousarray(v_tail, dtype=np.uint16) if n > n_q else None
+    rc = lib().kvo_prefill_attention(int(n), int(n_q), int(n_new), fmt_k, fmt_v, *parts(kq), *parts(vq),
+                                     _p(kt, _u16p), _p(vt, _u16p), g, _p(q, _f64p), float(sigma),
+                                     _p(out, _f64p))
+    if rc != 0:
+        raise ValueError("prefill_attention rc=%d" % rc)
     return out

@@ -602,3 +602,60 @@ int kvo_attention_kld(int64_t n, int64_t n_q, int fmt_k, const uint8_t* kq_codes
     free(sq);
     return 0;
 }
+
+/* ======================================================================== */
+/* Chunked prefill attention (causal, over the mixed cache)                 */
+/* ======================================================================== */
+
+int kvo_prefill_attention(int64_t n, int64_t n_q, int64_t n_new, int fmt_k, int fmt_v,
+                          const uint8_t* kq_codes, const uint16_t* kq_scales, const uint16_t* kq_cscale,
+                          const uint8_t* vq_codes, const uint16_t* vq_scales, const uint16_t* vq_cscale,
+                          const uint16_t* k_tail, const uint16_t* v_tail,
+                          int g, const double* q, double sigma, double* out)
+{
+    int Nk, kk, cbk, sbk, pbk, Nv, kv, cbv, sbv, pbv;
+    if (kvo_format_info(fmt_k, &Nk, &kk, &cbk, &sbk, &pbk) != 0) return -1;
+    if (kvo_format_info(fmt_v, &Nv, &kv, &cbv, &sbv, &pbv) != 0) return -1;
+    if (n_new == 0) return -4;
+    if (n < 0 || n_q < 0 || n_q > n || n_new < 0 || n_new > n || g <= 0) return -1;
+    /* every token of the sequence as the cache holds it */
+    double* K = (double*)malloc(sizeof(double) * (size_t)n * 128);
+    double* V = (double*)malloc(sizeof(double) * (size_t)n * 128);
+    double* s = (double*)malloc(sizeof(double) * (size_t)n);
+    if (!K || !V || !s) { free(K); free(V); free(s); return -1; }
+    if (n_q > 0) {
+        kvo_dequant_stream(fmt_k, n_q, kq_codes, kq_scales, kq_cscale, K);
+        kvo_dequant_stream(fmt_v, n_q, vq_codes, vq_scales, vq_cscale, V);
+    }
+    for (int64_t t = n_q; t < n; ++t) {
+        for (int i = 0; i < 128; ++i) {
+            K[t * 128 + i] = (double)kvo_f32_from_bf16(k_tail[(t - n_q) * 128 + i]);
+            V[t * 128 + i] = (double)kvo_f32_from_bf16(v_tail[(t - n_q) * 128 + i]);
+        }
+    }
+    for (int64_t qi = 0; qi < n_new; ++qi) {
+        const int64_t ctx = n - n_new + qi + 1;          /* tokens 0 .. p_i */
+        for (int h = 0; h < g; ++h) {
+            const double* qh = q + (qi * g + h) * 128;
+            double M = -INFINITY;
+            for (int64_t t = 0; t < ctx; ++t) {
+                double acc = 0.0;
+                for (int i = 0; i < 128; ++i) acc += qh[i] * K[t * 128 + i];
+                s[t] = sigma * acc;
+                if (s[t] > M) M = s[t];
+            }
+            double l = 0.0, o[128];
+            for (int i = 0; i < 128; ++i) o[i] = 0.0;
+            for (int64_t t = 0; t < ctx; ++t) {
+                const double p = exp(s[t] - M);
+                l += p;
+                for (int i = 0; i < 128; ++i) o[i] += p * V[t * 128 + i];
+            }
+            for (int i = 0; i < 128; ++i) out[(qi * g + h) * 128 + i] = o[i] / l;
+        }
+    }
+    free(K);
+    free(V);
+    free(s);
+    return 0;
+}

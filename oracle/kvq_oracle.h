@@ -146,6 +146,19 @@ int kvo_attention(int64_t n, int64_t n_q, int fmt_k, int fmt_v,
                   const uint16_t* k_tail, const uint16_t* v_tail,
                   int g, const double* q, double sigma, double* out);
 
+/* ---- chunked prefill attention -------------------------------------------------------- */
+/* Causal attention of the last n_new tokens of a sequence over the cache that holds them:
+ * query i (0 <= i < n_new) sits at position p_i = n - n_new + i and attends to the tokens
+ * t <= p_i, each as the cache holds it (dequantized rows t < n_q from the encoding of the
+ * whole quantized region, bf16 rows k_tail/v_tail for n_q <= t < n, given in token order).
+ * q: [n_new][g][128] values; out: [n_new][g][128]; binary64, same formula as
+ * kvo_attention per query.  Returns 0, -1 on bad arguments, -4 when n_new == 0. */
+int kvo_prefill_attention(int64_t n, int64_t n_q, int64_t n_new, int fmt_k, int fmt_v,
+                          const uint8_t* kq_codes, const uint16_t* kq_scales, const uint16_t* kq_cscale,
+                          const uint8_t* vq_codes, const uint16_t* vq_scales, const uint16_t* vq_cscale,
+                          const uint16_t* k_tail, const uint16_t* v_tail,
+                          int g, const double* q, double sigma, double* out);
+
 /* ---- attention fidelity --------------------------------------------------------------- */
 /* Kullback-Leibler divergence of the attention distribution over the cache's keys from the
  * one over the exact keys, per query head (a model-free analogue of the KLD quality
