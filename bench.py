@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--append-reps", type=int, default=4)
     p.add_argument("--cpu-units", type=int, default=16, help="(layer, kv head) units of the CPU sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
+                   help="chunked-prefill attention: time a CHUNK-token chunk at the end of --ctx tokens")
     p.add_argument("--kld", action="store_true",
                    help="attention-fidelity sweep: median KL over query heads, format x tail x context")
     p.add_argument("--copy-probe", type=int, default=0,
@@ -229,10 +231,61 @@ def kld_sweep(args):
                       "table": table}), flush=True)
 
 
+def prefill_bench(args):
+    """Causal attention of a chunk of args.prefill tokens at the end of args.ctx tokens (one
+    layer of the decode workload's shape: 8 KV heads, 32 query heads, the chosen format and
+    tail), timed per call with HIP events.  Algorithmic work: for every query head and query
+    i, 2 x 128 multiply-adds per visible key for q.k and as many for p.v."""
+    import torch
+    from mixed_precision_quantized_amd import kvq, synth
+    wl, H, QH = "c4_ctx240000_64l", 8, 32
+    n, c = args.ctx, args.prefill
+    fk, fv = split_fmt(args.fmt)
+    cache = kvq.Cache(1, H, QH, fmt_k=fk, fmt_v=fv, tail_tokens=args.tail, n_seqs=1, max_tokens=n)
+    spans, t = [], 0
+    while t < n - c:                       # the context, then the chunk as one append
+        spans.append((t, min(t + 16384, n - c)))
+        t = spans[-1][1]
+    spans.append((n - c, n))
+    for t0, t1 in spans:
+        k = torch.stack([synth.kv_rows(wl, 0, 0, h, 0, t0, t1, "cuda") for h in range(H)], 1)
+        v = torch.stack([synth.kv_rows(wl, 0, 0, h, 1, t0, t1, "cuda") for h in range(H)], 1)
+        cache.append(0, [0], [t1 - t0], synth.to_bf16_bits(k).contiguous(), synth.to_bf16_bits(v).contiguous())
+    q = torch.stack([synth.to_bf16_bits(synth.q_rows(wl, 0, 0, i, QH, "cuda")) for i in range(c)], 0).contiguous()
+    n_ws = int(kvq.lib().kv_prefill_workspace_bytes(cache.h, c))
+    ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((c, QH, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        cache.prefill(0, 0, q, out=out, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a0, a1 in evs:
+        a0.record(stream)
+        cache.prefill(0, 0, q, out=out, ws=ws)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a0.elapsed_time(a1) for a0, a1 in evs) / args.steps
+    visible = sum(n - c + i + 1 for i in range(c))
+    flops = 4.0 * 128 * QH * visible
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "chunked-prefill attention, chunk tokens/s per layer", "value": round(c / (ms * 1e-3), 1),
+                      "unit": "tokens/s", "ms_per_call": round(ms, 4), "higher_is_better": True, "data": "synthetic",
+                      "dtype": "f16 MFMA operands (exact codes, two-term query), f32 accumulate",
+                      "config": {"workload": "1 layer x 8 KV heads x 32 q heads x d128, chunk %d at the end of %d "
+                                             "tokens, %s, tail %d" % (c, n, args.fmt, args.tail)},
+                      "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                                   "frac": round(tf / 2500.0, 4), "traffic": None,
+                                   "kernel": "k_prefill + k_prefill_merge", "flops_per_call": flops}}), flush=True)
+
+
 def main():
     args = parse()
     if args.kld:
         kld_sweep(args)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -135,6 +135,25 @@ int kv_decode_attn(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t
                    const void* q, int32_t q_dtype, float softmax_scale, float* out,
                    void* workspace, int64_t ws_bytes, void* stream);
 
+/* Bytes of workspace needed by kv_prefill_attn for a chunk of n_new tokens at any length
+ * up to max_tokens (per-split partial results; no initialization needed; calls sharing it
+ * must be stream-ordered). */
+int64_t kv_prefill_workspace_bytes(const kv_cache* cache, int32_t n_new);
+
+/* Chunked-prefill attention for `layer` of one sequence: the chunk is the sequence's last
+ * n_new tokens, already appended (kv_append).  Query i of the chunk (q: [n_new][n_q_heads]
+ * [128] of q_dtype) sits at position p = n - n_new + i and attends causally to the tokens
+ * t <= p as the cache holds them (dequantized rows t < n_q, BF16 ring rows after):
+ *   out[i][h] = sum_{t<=p} exp(s_t - max) v_t / sum_{t<=p} exp(s_t - max),
+ *   s_t = softmax_scale * q_ih . k_t,  KV head h / g;
+ * out: float32 [n_new][n_q_heads][128].  The step on the other side of append: prefill and
+ * decode are measured separately ("Форк beellama и KV-кванты kvarn на длинном контексте",
+ * the section on how to compare builds).  Reads the cache only.  Errors: KV_EINVAL
+ * (n_new < 1 or n_new > n), KV_EEMPTY (n == 0), KV_ESIZE (workspace). */
+int kv_prefill_attn(kv_cache* cache, int32_t layer, int32_t seq_id, int32_t n_new, const void* q,
+                    int32_t q_dtype, float softmax_scale, float* out, void* workspace,
+                    int64_t ws_bytes, void* stream);
+
 /* Bytes of workspace needed by kv_attn_kld at any length up to max_tokens (partial
  * results of one call; no initialization needed; calls sharing it must be stream-ordered). */
 int64_t kv_attn_kld_workspace_bytes(const kv_cache* cache);

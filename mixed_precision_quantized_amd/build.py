@@ -32,6 +32,7 @@ UNITS = [
     ("kvq_decode_ws_k6.hip", []),
     ("kvq_decode_ws_k8.hip", []),
     ("kvq_merge.hip", []),
+    ("kvq_prefill.hip", []),
     ("kvq_debug.hip", ["-ffp-contract=off"]),
 ]
 

@@ -346,6 +346,68 @@ int64_t kv_decode_workspace_bytes(const kv_cache* c, int32_t n_seqs)
     return align256((int64_t)kMaxDecodeWGs * kPartialFloats * 4);
 }
 
+namespace {
+// Split plan of one prefill call: workgroups = KV heads x query tiles x key splits, about
+// two per CU; quantized and ring blocks never share a split.
+struct PfPlan { int32_t tiles, splits_q, splits_t, bps, splits_max; };
+PfPlan prefill_plan(const kv_cache* c, int64_t n, int64_t n_q, int32_t n_new)
+{
+    PfPlan p;
+    p.tiles = (n_new + kPfQ - 1) / kPfQ;
+    const int64_t nbq = (n_q + kPfKB - 1) / kPfKB, nbt = (n - n_q + kPfKB - 1) / kPfKB;
+    const int64_t target = 2 * (int64_t)std::max(1, device_cu_count());
+    const int64_t per = (int64_t)c->cfg.n_kv_heads * p.tiles;
+    const int64_t splits = std::max<int64_t>(1, (target + per - 1) / per);
+    p.bps = (int32_t)std::max<int64_t>(1, (nbq + nbt + splits - 1) / splits);
+    p.splits_q = (int32_t)((nbq + p.bps - 1) / p.bps);
+    p.splits_t = (int32_t)((nbt + p.bps - 1) / p.bps);
+    p.splits_max = (int32_t)(splits + 2);
+    return p;
+}
+}  // namespace
+
+int64_t kv_prefill_workspace_bytes(const kv_cache* c, int32_t n_new)
+{
+    if (!c || n_new < 1) return KV_EINVAL;
+    const PfPlan p = prefill_plan(c, c->cfg.max_tokens, 0, n_new);
+    return align256((int64_t)c->cfg.n_kv_heads * p.tiles * p.splits_max * 4 * kPfQ * (kD + 2) * 4);
+}
+
+int kv_prefill_attn(kv_cache* c, int32_t layer, int32_t seq_id, int32_t n_new, const void* q,
+                    int32_t q_dtype, float softmax_scale, float* out, void* workspace,
+                    int64_t ws_bytes, void* stream)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers) return KV_EINVAL;
+    if (seq_id < 0 || seq_id >= c->cfg.n_seqs) return KV_EINVAL;
+    if (!q || !out || !workspace) return KV_EINVAL;
+    if (q_dtype != KV_IN_BF16 && q_dtype != KV_IN_F32) return KV_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+        return KV_EINVAL;
+    const int64_t n = n_at(c, seq_id, layer);
+    if (n == 0) return KV_EEMPTY;
+    if (n_new < 1 || n_new > n) return KV_EINVAL;
+    if (ws_bytes < kv_prefill_workspace_bytes(c, n_new)) return KV_ESIZE;
+    PrefillArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.g = c->geom;
+    a.layer = layer;
+    a.seq = seq_id;
+    a.n = n;
+    a.n_q = nq_at(c, seq_id, layer);
+    a.n_new = n_new;
+    a.q_dtype = q_dtype;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    const PfPlan p = prefill_plan(c, a.n, a.n_q, n_new);
+    a.tiles = p.tiles;
+    a.splits_q = p.splits_q;
+    a.splits_t = p.splits_t;
+    a.bps = p.bps;
+    a.q = q;
+    a.out = out;
+    a.partials = (float*)workspace;
+    return launch_prefill(a, stream) ? KV_EDEVICE : KV_OK;
+}
+
 int64_t kv_attn_kld_workspace_bytes(const kv_cache* c)
 {
     if (!c) return KV_EINVAL;

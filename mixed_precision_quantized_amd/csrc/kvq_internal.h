@@ -116,6 +116,25 @@ struct KldArgs {
 };
 int launch_kld(const KldArgs& a, void* stream);               // split kernel + merge (kvq_decode.hip)
 
+// Causal attention of a sequence's last n_new tokens over the cache that holds them.
+constexpr int kPfQ = 32;           // query positions per prefill workgroup
+constexpr int kPfKB = 32;          // keys per prefill block
+struct PrefillArgs {
+    CacheGeom g;
+    int32_t layer, seq;
+    int64_t n, n_q;       // tokens of the sequence (the chunk is the last n_new), quantized boundary
+    int32_t n_new, q_dtype;
+    float scale_log2;     // softmax_scale * log2(e)
+    int32_t tiles;        // ceil(n_new / kPfQ)
+    int32_t splits_q, splits_t;   // key splits over the quantized blocks / the ring blocks
+    int32_t bps;          // kPfKB-token blocks per split
+    int32_t pad_;
+    const void* q;        // [n_new][n_q_heads][128]
+    float* out;           // [n_new][n_q_heads][128]
+    float* partials;      // [n_kv_heads][tiles][splits][4][kPfQ][kD + 2]: m, l, acc
+};
+int launch_prefill(const PrefillArgs& a, void* stream);          // kvq_prefill.hip
+
 constexpr int kPartialFloats = kMaxGroup * (kD + 2);   // m, l, acc[128] per query head
 constexpr int kMaxDecodeWGs = 8192;
 

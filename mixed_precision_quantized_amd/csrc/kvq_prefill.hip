@@ -1,0 +1,601 @@
+// kvq_prefill.hip -- causal chunked-prefill attention over the mixed-precision cache, gfx950.
+//
+// After a chunk of n_new tokens has been appended, query i of the chunk (position
+// p = n - n_new + i) attends to the tokens t <= p as the cache holds them: dequantized rows
+// below n_q, BF16 ring rows above.  Prefill is measured on its own, apart from decode ("Форк
+// beellama и KV-кванты kvarn на длинном контексте", the section on how to compare builds);
+// unlike single-token decode it is a dense contraction (every key meets every query of the
+// chunk), so it runs on the matrix cores:
+//
+//   workgroup = (KV head, 32 query positions, key split): four waves, one per query head of
+//   the KV head's group, each owning 32 queries; the raw bytes of each 32-key block are
+//   loaded straight to LDS two blocks ahead and unpacked to binary16 one block ahead;
+//   per 32-key block each wave computes
+//   S^T = K Q^T (32 keys x 32 queries, v_mfma_f32_32x32x16_f16: a lane holds one query and
+//   16 of the keys, so the softmax of a query is a reduction over registers and one lane
+//   pair), the online softmax, and O^T += V^T P^T (128 dims x 32 queries, four 32x32 tiles).
+//
+// Precision.  Keys enter as their exact centred codes (u - o, or u for affine codes: small
+// integers, exact in binary16); the block scale d of each (token, block) is applied to the
+// binary32 product of that block's 32 dims, and the affine minimum m as m * sum(q) of the
+// block, so the keys are used exactly.  (Rounding dequantized keys to binary16 would not do:
+// keys with 15x outlier channels reach |k| ~ 800, where binary16 keeps 0.25 absolute.)  The
+// query (times the page's channel scales for KVarN keys) enters as two binary16 terms,
+// q = hi + lo, one MFMA each: one rounding of q alone cost up to 1.9e-3 of the output on the
+// 64k block-format workload.  Values are dequantized to binary16 (|v| is small) and the
+// probabilities are rounded to binary16 before the P V product.
+//
+// KVarN, as in decode: keys are scored in the rotated domain with q'' = (H q / 128) * c_K
+// of the page; values accumulate in the rotated domain and are rotated back once in the
+// merge (quantized and ring blocks never share a split, so each split is in one domain).
+#include "kvq_device.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kG = 4;
+constexpr float kNeg = -1.0e30f;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct alignas(16) PfLds {
+    _Float16 kc[kPfKB][kD + 8];     // key codes (or exact values), token-major; +8: bank spread
+    _Float16 vt[kD][kPfKB + 8];     // dequantized values, dim-major
+    float dk[4][kPfKB];             // key block scales [block][token] (1 for exact rows)
+    float mk[4][kPfKB];             // key block minima (affine codes)
+    float ck[kD];                   // KVarN key channel scales of the block's page
+};
+
+__device__ __forceinline__ const char* pf_stream(const CacheGeom& g, int seq, int layer, int head, int isv)
+{
+    const int64_t unit = ((int64_t)seq * g.n_layers + layer) * g.n_kv_heads + head;
+    return g.base + unit * g.unit_bytes + (isv ? g.v_offset : 0);
+}
+
+// Staging of one 32-token block.  Its raw bytes (codes, scales, channel scales, or BF16
+// rows) are loaded straight to LDS by buffer loads two blocks ahead of use (no registers,
+// the latency overlaps the compute of two blocks); one block ahead, the waves unpack them
+// into the binary16 operand buffers.
+struct alignas(16) PfRawL {
+    uint8_t k[8192];       // key codes (32 rows of 16 N bytes) or BF16 rows (32 x 256 B)
+    uint8_t v[8192];
+    uint8_t ks[512];       // block-scale rows (8 or 16 B per token)
+    uint8_t vs[512];
+    uint16_t kch[128];     // KVarN channel scales of the block's page
+    uint16_t vch[128];
+};
+
+typedef __amdgpu_buffer_rsrc_t pf_rsrc_t;
+__device__ __forceinline__ pf_rsrc_t pf_rsrc(const void* p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+// lane l copies 16 bytes from the resource at voff to lds + 16 l (reads past the resource's
+// size return zero); the wait is explicit (pf_wait_vm0).  M0 is set in the same block.
+__device__ __forceinline__ void pf_dma16(pf_rsrc_t r, int voff, const void* lds)
+{
+    const uint32_t la = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_nop 0"
+                 :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void pf_wait_vm0()
+{
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0) only
+}
+
+// Loop-invariant buffer resources of one stream over the split's region (rows past its
+// end read as zero) and the issue of one block's loads into R (every wave: 2 x 64 chunks
+// per stream; chunk c of a block = bytes 16 c of its rows).
+struct PfStream {
+    pf_rsrc_t rows, scales, chan;
+    int rb, sb;             // code (or BF16) bytes per row, scale bytes per row
+    bool ring;
+};
+__device__ __forceinline__ PfStream pf_stream_rsrc(const PrefillArgs& a, const char* st, const StreamLayout& Ls,
+                                                   int fmt, bool quant)
+{
+    PfStream S;
+    const bool exact = fkind(fmt) == KIND_BF16;
+    S.ring = !quant;
+    S.rb = quant && !exact ? 16 * fbits(fmt) : 256;
+    S.sb = fkind(fmt) == KIND_Q1 ? 16 : 8;
+    if (quant) {
+        S.rows = pf_rsrc(st + Ls.codes, (int)(a.n_q * S.rb));
+        S.scales = pf_rsrc(st + Ls.scales, exact ? 0 : (int)(a.n_q * S.sb));
+        S.chan = pf_rsrc(st + (Ls.cscale >= 0 ? Ls.cscale : 0), fkind(fmt) == KIND_KVARN ? (int)((a.n_q + kPage - 1) / kPage * 256) : 0);
+    } else {
+        S.rows = pf_rsrc(st + Ls.ring, a.g.ring_slots * 256);
+        S.scales = S.chan = S.rows;
+    }
+    return S;
+}
+
+template <int KK, int KV>
+__device__ __forceinline__ void pf_dma(PfRawL& R, const PrefillArgs& a, const PfStream& SK, const PfStream& SV,
+                                       int64_t tb, int nt, int wave, int lane)
+{
+    auto stream = [&](const PfStream& S, bool coded, bool kvarn, uint8_t* dst, uint8_t* sdst, uint16_t* cdst,
+                      int swave, int cwave) {
+        if (!S.ring) {
+            const int base = (int)tb * S.rb;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c0 = 64 * (wave + 4 * i);
+                pf_dma16(S.rows, base + 16 * (c0 + lane), dst + 16 * c0);
+            }
+            if (coded && wave == swave && lane < 32) pf_dma16(S.scales, (int)tb * S.sb + 16 * lane, sdst);
+            if (kvarn && wave == cwave && lane < 16) pf_dma16(S.chan, (int)(tb / kPage) * 256 + 16 * lane, cdst);
+        } else {
+            // ring rows: slot (t mod R); rows past nt read past the resource (zero)
+            const int R = a.g.ring_slots;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c0 = 64 * (wave + 4 * i), c = c0 + lane, r = c >> 4;
+                const int voff = r < nt ? (int)((tb + r) % R) * 256 + 16 * (c & 15) : R * 256;
+                pf_dma16(S.rows, voff, dst + 16 * c0);
+            }
+        }
+    };
+    stream(SK, KK != KIND_BF16, KK == KIND_KVARN, R.k, R.ks, R.kch, 0, 2);
+    stream(SV, KV != KIND_BF16, KV == KIND_KVARN, R.v, R.vs, R.vch, 1, 3);
+}
+
+// 16 N-bit codes of part `part` of a row held at lds row (dword aligned)
+template <int N>
+__device__ __forceinline__ void unpack16(const uint8_t* row, int part, uint32_t (&u)[16])
+{
+    const int b0 = 2 * N * part, fd = b0 >> 2, sh0 = 8 * (b0 & 3);
+    const uint32_t* p = (const uint32_t*)row + fd;
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = (32 * i < sh0 + 16 * N) ? p[i] : 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int bit = sh0 + N * e, wi = bit >> 5, sh = bit & 31;
+        uint32_t v = w[wi] >> sh;
+        if (sh + N > 32) v |= w[wi + 1] << (32 - sh);
+        u[e] = v & ((1u << N) - 1u);
+    }
+}
+__device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part, uint32_t (&u)[16])
+{
+    switch (N) {
+    case 2: unpack16<2>(row, part, u); break;
+    case 3: unpack16<3>(row, part, u); break;
+    case 4: unpack16<4>(row, part, u); break;
+    case 5: unpack16<5>(row, part, u); break;
+    case 6: unpack16<6>(row, part, u); break;
+    default: unpack16<8>(row, part, u); break;
+    }
+}
+
+// Unpack a raw block into the operand buffers.  Thread tid: token r = tid >> 3, dims
+// 16 (tid & 7) .. of both streams.
+template <int KK, int KV>
+__device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const PrefillArgs& a, int nt, bool quant, int tid)
+{
+    const CacheGeom& g = a.g;
+    const int r = tid >> 3, pp = tid & 7, b = pp >> 1;
+    const bool valid = r < nt;
+    float kx[16], vx[16];
+    float d = 1.0f, m = 0.0f;
+    if (quant && KK != KIND_BF16) {
+        const int N = fbits(g.fmt_k);
+        uint32_t u[16];
+        unpack16_rt(N, R.k + r * 16 * N, pp, u);
+        const float off = KK == KIND_Q1 ? 0.0f : (float)(1 << (N - 1));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) kx[e] = (float)u[e] - off;
+        if (KK == KIND_Q1) {
+            const uint32_t dm = *(const uint32_t*)(R.ks + r * 16 + 4 * b);
+            d = fp16_to_f32(dm & 0xFFFFu);
+            m = fp16_to_f32(dm >> 16);
+        } else {
+            d = fp16_to_f32(*(const uint16_t*)(R.ks + r * 8 + 2 * b));
+        }
+    } else {
+        const uint4* q = (const uint4*)(R.k + r * 256 + 32 * pp);
+        const uint4 x0 = q[0], x1 = q[1];
+        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kx[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            kx[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+    if (quant && KV != KIND_BF16) {
+        const int N = fbits(g.fmt_v);
+        uint32_t u[16];
+        unpack16_rt(N, R.v + r * 16 * N, pp, u);
+        if (KV == KIND_Q1) {
+            const uint32_t dm = *(const uint32_t*)(R.vs + r * 16 + 4 * b);
+            const float dv = fp16_to_f32(dm & 0xFFFFu), mv = fp16_to_f32(dm >> 16);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) vx[e] = fmaf(dv, (float)u[e], mv);
+        } else {
+            const float dv = fp16_to_f32(*(const uint16_t*)(R.vs + r * 8 + 2 * b));
+            const float off = (float)(1 << (N - 1));
+#pragma unroll
+            for (int e = 0; e < 16; ++e) vx[e] = ((float)u[e] - off) * dv;
+            if (KV == KIND_KVARN) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) vx[e] *= fp16_to_f32(R.vch[16 * pp + e]);
+            }
+        }
+    } else {
+        const uint4* q = (const uint4*)(R.v + r * 256 + 32 * pp);
+        const uint4 x0 = q[0], x1 = q[1];
+        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            vx[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            vx[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+    if (!valid) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
+    }
+    {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const h2 v = {(_Float16)kx[2 * i], (_Float16)kx[2 * i + 1]};
+            w[i] = __builtin_bit_cast(uint32_t, v);
+        }
+        uint4* dst = (uint4*)&L.kc[r][16 * pp];
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) L.vt[16 * pp + e][r] = (_Float16)vx[e];
+    if ((pp & 1) == 0) {
+        L.dk[b][r] = d;
+        L.mk[b][r] = m;
+    }
+    if (KK == KIND_KVARN && quant && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
+}
+
+template <int KK, int KV>
+__global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
+{
+    // Wave h computes query head h of the group (32 queries) and, with the others, stages
+    // the blocks: block i + 2 is loaded to raw LDS and block i + 1 unpacked while block i is
+    // computed; one barrier per block.
+    __shared__ PfLds L[2];
+    __shared__ PfRawL RW[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int S = a.splits_q + a.splits_t;
+    const int sp = blockIdx.x % S;
+    const int tile = (blockIdx.x / S) % a.tiles;
+    const int head = blockIdx.x / (S * a.tiles);
+    const bool quant = sp < a.splits_q;
+    const CacheGeom& g = a.g;
+    const char* kst = pf_stream(g, a.seq, a.layer, head, 0);
+    const char* vst = pf_stream(g, a.seq, a.layer, head, 1);
+    const int64_t pos_max = a.n - a.n_new + min(kPfQ * tile + kPfQ, a.n_new) - 1;
+
+    // ---- key range of the split (32-token blocks of the quantized or the ring region) ------
+    const int64_t r0 = quant ? 0 : a.n_q, r1 = quant ? a.n_q : a.n;
+    const int blk0 = (quant ? sp : sp - a.splits_q) * a.bps;
+    const int nblk = (int)((r1 - r0 + kPfKB - 1) / kPfKB);
+    const int blk1 = min(blk0 + a.bps, nblk);
+    // causal: no key after the tile's last query is seen
+    const int blk_end = pos_max < r0 ? blk0 : (int)min<int64_t>(blk1, (pos_max - r0) / kPfKB + 1);
+    const int nb = max(0, blk_end - blk0);
+    auto tb_of = [&](int i) { return r0 + (int64_t)(blk0 + i) * kPfKB; };
+    auto nt_of = [&](int i) { return (int)min<int64_t>(kPfKB, r1 - tb_of(i)); };
+
+    // ================================ compute waves ================================
+    const int h = wave;                                              // query head of the group
+    const int j = lane & 31, hh = lane >> 5;
+    const int qi = kPfQ * tile + j;                                  // query index in the chunk
+    const bool qvalid = qi < a.n_new;
+    const int64_t pos = a.n - a.n_new + (qvalid ? qi : a.n_new - 1);
+    const int64_t pos_min = a.n - a.n_new + kPfQ * tile;             // the tile's first query
+    const bool kv_k = KK == KIND_KVARN && quant;
+
+    // ---- query: the lane's 64 dims {16 idx + 8 hh + c}, log2 domain, as hi + lo binary16 ----
+    h8 qb[8], ql[8];                 // the operand of the current page: query = qb + ql
+    h8 rb[8], rl[8];                 // KVarN: the rotated query H q / 128 (before c_K)
+    {
+        float qf[8][8];
+        const int64_t base = ((int64_t)(qvalid ? qi : 0) * g.n_q_heads + head * kG + h) * kD;
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int64_t e = base + 16 * idx + 8 * hh + c;
+                const float v = a.q_dtype ? ((const float*)a.q)[e] : bf16_to_f32(((const uint16_t*)a.q)[e]);
+                qf[idx][c] = qvalid ? v * a.scale_log2 : 0.0f;
+            }
+        if (kv_k) {
+            // H q / 128: spans 1, 2, 4 (c) and 16, 32, 64 (idx) in the lane, 8 across the pair
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+                for (int sp2 = 1; sp2 < 8; sp2 <<= 1)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        if ((c & sp2) == 0) {
+                            const float x = qf[idx][c], y = qf[idx][c + sp2];
+                            qf[idx][c] = x + y;
+                            qf[idx][c + sp2] = x - y;
+                        }
+#pragma unroll
+            for (int s2 = 1; s2 < 8; s2 <<= 1)
+#pragma unroll
+                for (int idx = 0; idx < 8; ++idx)
+                    if ((idx & s2) == 0)
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const float x = qf[idx][c], y = qf[idx + s2][c];
+                            qf[idx][c] = x + y;
+                            qf[idx + s2][c] = x - y;
+                        }
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float y = __shfl_xor(qf[idx][c], 32);
+                    qf[idx][c] = (hh ? y - qf[idx][c] : qf[idx][c] + y) * (1.0f / 128.0f);
+                }
+        }
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const _Float16 hi = (_Float16)qf[idx][c];
+                qb[idx][c] = hi;
+                ql[idx][c] = (_Float16)(qf[idx][c] - (float)hi);
+            }
+        if (kv_k) {
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx) { rb[idx] = qb[idx]; rl[idx] = ql[idx]; }
+        }
+    }
+    float qsum[4];
+    auto make_qsum = [&]() {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                s += ((float)qb[2 * b][c] + (float)ql[2 * b][c]) + ((float)qb[2 * b + 1][c] + (float)ql[2 * b + 1][c]);
+            qsum[b] = s + __shfl_xor(s, 32);
+        }
+    };
+    if (KK == KIND_Q1) make_qsum();
+    // KVarN keys: q'' = (H q / 128) * c_K of the page, again as hi + lo
+    auto page_operand = [&](const PfLds& B) {
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float v = ((float)rb[idx][c] + (float)rl[idx][c]) * B.ck[16 * idx + 8 * hh + c];
+                const _Float16 hi = (_Float16)v;
+                qb[idx][c] = hi;
+                ql[idx][c] = (_Float16)(v - (float)hi);
+            }
+    };
+
+    float mrun = kNeg, lrun = 0.0f;
+    f32x16 O[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[b][r] = 0.0f;
+    int64_t page = -1;
+    // key rows of this lane in the 32x32 accumulators: i(r) = 8 (r / 4) + 4 hh + r % 4
+    auto compute = [&](const PfLds& B, int64_t tb, int nt) __attribute__((always_inline)) {
+        if (kv_k && tb / kPage != page) {
+            page = tb / kPage;
+            page_operand(B);
+        }
+        // S^T: keys x queries
+        f32x16 Sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Sacc[r] = 0.0f;
+        const bool scaled = quant && KK != KIND_BF16;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x16 T;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) T[r] = 0.0f;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int idx = 2 * b + k2;
+                const h8 A = *(const h8*)&B.kc[j][16 * idx + 8 * hh];
+                T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qb[idx], T, 0, 0, 0);
+                T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, ql[idx], T, 0, 0, 0);
+            }
+            if (scaled) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 dd = *(const float4*)&B.dk[b][8 * r4 + 4 * hh];
+                    const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(dv[c], T[4 * r4 + c], Sacc[4 * r4 + c]);
+                    if (KK == KIND_Q1) {
+                        const float4 mm = *(const float4*)&B.mk[b][8 * r4 + 4 * hh];
+                        const float mv[4] = {mm.x, mm.y, mm.z, mm.w};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(mv[c], qsum[b], Sacc[4 * r4 + c]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Sacc[r] += T[r];
+            }
+        }
+        // mask: rows past the block's end, and keys later than the query (only blocks that
+        // reach the tile's first query or end early need it; unused query slots are never
+        // read back)
+        if (nt < kPfKB || tb + kPfKB - 1 > pos_min) {
+            const int lim = (int)min<int64_t>(nt - 1, pos - tb);      // last visible row
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (i > lim) Sacc[r] = kNeg;
+            }
+        }
+        float mx = kNeg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sacc[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(mrun, mx);
+        const float al = __builtin_amdgcn_exp2f(mrun - mn);
+        float ps = 0.0f;
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = Sacc[r] > 0.5f * kNeg ? __builtin_amdgcn_exp2f(Sacc[r] - mn) : 0.0f;
+            ps += p[r];
+        }
+        ps += __shfl_xor(ps, 32);
+        lrun = fmaf(lrun, al, ps);
+        mrun = mn;
+        if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) O[b][r] *= al;
+        }
+        // O^T += V^T P^T: K slot 8 hh + c of MFMA k2 is key 16 k2 + 8 (c / 4) + 4 hh + c % 4,
+        // which is accumulator register 8 k2 + c of this lane
+        h8 pb[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) pb[k2][c] = (_Float16)p[8 * k2 + c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const _Float16* row = &B.vt[32 * b + j][0];
+                const uint2 lo = *(const uint2*)(row + 16 * k2 + 4 * hh);
+                const uint2 hi = *(const uint2*)(row + 16 * k2 + 8 + 4 * hh);
+                const h8 A = __builtin_bit_cast(h8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                O[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, pb[k2], O[b], 0, 0, 0);
+            }
+    };
+    const PfStream SK = pf_stream_rsrc(a, kst, g.k, g.fmt_k, quant), SV = pf_stream_rsrc(a, vst, g.v, g.fmt_v, quant);
+    if (nb > 0) pf_dma<KK, KV>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
+    if (nb > 1) pf_dma<KK, KV>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
+    pf_wait_vm0();
+    __syncthreads();
+    if (nb > 0) pf_unpack<KK, KV>(L[0], RW[0], a, nt_of(0), quant, tid);
+    // iteration i: L[i & 1] holds block i, RW[(i + 1) & 1] raw block i + 1 (loaded during
+    // block i - 1); RW[i & 1] is free for block i + 2
+    auto step = [&](int i, PfLds& Lc, PfLds& Ln, PfRawL& Rn, PfRawL& Rf) __attribute__((always_inline)) {
+        pf_wait_vm0();
+        __syncthreads();
+        if (i + 1 < nb) pf_unpack<KK, KV>(Ln, Rn, a, nt_of(i + 1), quant, tid);
+        if (i + 2 < nb) pf_dma<KK, KV>(Rf, a, SK, SV, tb_of(i + 2), nt_of(i + 2), wave, lane);
+        compute(Lc, tb_of(i), nt_of(i));
+    };
+    for (int i = 0; i < nb; i += 2) {
+        step(i, L[0], L[1], RW[1], RW[0]);
+        if (i + 1 < nb) step(i + 1, L[1], L[0], RW[0], RW[1]);
+    }
+    pf_wait_vm0();
+    // ---- partial result of the split: m, l and acc[128] per query (dims 32 b + i(r)) --------
+    float* pp = a.partials + (((((int64_t)head * a.tiles + tile) * S + sp) * kG + h) * kPfQ + j) * (kD + 2);
+    if (hh == 0) {
+        pp[0] = mrun;
+        pp[1] = lrun;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pp[2 + 32 * b + 8 * (r >> 2) + 4 * hh + (r & 3)] = O[b][r];
+}
+
+// One workgroup of 128 threads per (query, query head): merge the splits; the quantized
+// splits' value sum is rotated back for KVarN values.
+template <bool KVARN_V>
+__global__ __launch_bounds__(128) void k_prefill_merge(PrefillArgs a)
+{
+    __shared__ float vq[kD];
+    __shared__ float ML[2];
+    const int d = threadIdx.x;
+    const int qi = blockIdx.x / a.g.n_q_heads, qh = blockIdx.x % a.g.n_q_heads;
+    const int head = qh / kG, h = qh % kG, tile = qi / kPfQ, j = qi % kPfQ;
+    const int S = a.splits_q + a.splits_t;
+    const float* base = a.partials + ((((int64_t)head * a.tiles + tile) * S) * kG + h) * kPfQ * (kD + 2) + (int64_t)j * (kD + 2);
+    const int64_t sstride = (int64_t)kG * kPfQ * (kD + 2);
+    float M = kNeg;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, base[s * sstride]);
+    float L = 0.0f, aq = 0.0f, at = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float* p = base + s * sstride;
+        const float w = p[1] > 0.0f ? __builtin_amdgcn_exp2f(p[0] - M) : 0.0f;
+        L = fmaf(p[1], w, L);
+        if (s < a.splits_q) aq = fmaf(p[2 + d], w, aq);
+        else at = fmaf(p[2 + d], w, at);
+    }
+    vq[d] = aq;
+    if (KVARN_V) {
+        for (int span = 1; span < kD; span <<= 1) {
+            __syncthreads();
+            if (d < kD / 2) {
+                const int lo = d & (span - 1);
+                const int i = ((d - lo) << 1) | lo;
+                const float x = vq[i], y = vq[i + span];
+                vq[i] = x + y;
+                vq[i + span] = x - y;
+            }
+        }
+    }
+    __syncthreads();
+    if (d == 0) ML[1] = L;
+    __syncthreads();
+    const float q = KVARN_V ? vq[d] * (1.0f / 128.0f) : vq[d];
+    a.out[((int64_t)qi * a.g.n_q_heads + qh) * kD + d] = (q + at) / ML[1];
+}
+
+template <int KK, int KV>
+int launch_pf(const PrefillArgs& a, hipStream_t st)
+{
+    const int n = a.g.n_kv_heads * a.tiles * (a.splits_q + a.splits_t);
+    hipLaunchKernelGGL((k_prefill<KK, KV>), dim3(n), dim3(256), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+template <int KK>
+int launch_pf_v(const PrefillArgs& a, hipStream_t st)
+{
+    switch (fkind(a.g.fmt_v)) {
+    case KIND_BF16: return launch_pf<KK, KIND_BF16>(a, st);
+    case KIND_Q0: return launch_pf<KK, KIND_Q0>(a, st);
+    case KIND_Q1: return launch_pf<KK, KIND_Q1>(a, st);
+    default: return launch_pf<KK, KIND_KVARN>(a, st);
+    }
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs& a, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    int rc;
+    switch (fkind(a.g.fmt_k)) {
+    case KIND_BF16: rc = launch_pf_v<KIND_BF16>(a, st); break;
+    case KIND_Q0: rc = launch_pf_v<KIND_Q0>(a, st); break;
+    case KIND_Q1: rc = launch_pf_v<KIND_Q1>(a, st); break;
+    default: rc = launch_pf_v<KIND_KVARN>(a, st); break;
+    }
+    if (rc) return rc;
+    const int n = a.n_new * a.g.n_q_heads;
+    if (fkind(a.g.fmt_v) == KIND_KVARN)
+        hipLaunchKernelGGL(k_prefill_merge<true>, dim3(n), dim3(128), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_prefill_merge<false>, dim3(n), dim3(128), 0, st, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace kvq

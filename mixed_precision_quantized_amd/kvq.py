@@ -72,6 +72,10 @@ def lib():
         L.kv_decode_workspace_bytes.restype = _i64
         L.kv_decode_attn.argtypes = [_vp, _i32, _i32, _i32p, _vp, _i32, ctypes.c_float, _vp, _vp, _i64, _vp]
         L.kv_decode_attn.restype = ctypes.c_int
+        L.kv_prefill_workspace_bytes.argtypes = [_vp, _i32]
+        L.kv_prefill_workspace_bytes.restype = _i64
+        L.kv_prefill_attn.argtypes = [_vp, _i32, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _i64, _vp]
+        L.kv_prefill_attn.restype = ctypes.c_int
         L.kv_attn_kld_workspace_bytes.argtypes = [_vp]
         L.kv_attn_kld_workspace_bytes.restype = _i64
         L.kv_attn_kld.argtypes = [_vp, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _vp, _i64, _vp]
@@ -184,6 +188,26 @@ class Cache:
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.ws.data_ptr()),
                                   self.ws.numel(), _stream(stream))
         _check(rc, "kv_decode_attn")
+        return out
+
+    def prefill(self, layer, seq_id, q, softmax_scale=None, out=None, ws=None, stream=None):
+        """Causal attention of the sequence's last n_new tokens (already appended); q: device
+        [n_new][n_q_heads][128] bfloat16/float32 -> float32 [n_new][n_q_heads][128]."""
+        assert q.is_contiguous()
+        n_new = q.shape[0]
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(128)
+        if ws is None:
+            n_ws = int(lib().kv_prefill_workspace_bytes(self.h, n_new))
+            _check(n_ws if n_ws < 0 else 0, "kv_prefill_workspace_bytes")
+            ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty((n_new, self.cfg.n_q_heads, 128), dtype=torch.float32, device=q.device)
+        dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
+        rc = lib().kv_prefill_attn(self.h, int(layer), int(seq_id), n_new, ctypes.c_void_p(q.data_ptr()), dt,
+                                   float(softmax_scale), ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+        _check(rc, "kv_prefill_attn")
         return out
 
     def attn_kld(self, layer, seq_id, q, k_ref, softmax_scale=None, stream=None):
