@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--ctx", type=int, default=240000)
     p.add_argument("--layers", type=int, default=64)
     p.add_argument("--tail", type=int, default=2048)
+    p.add_argument("--tail-dtype", default="bf16", choices=["bf16", "f16"],
+                   help="16-bit type of the precision tail (and of the values quantized from it)")
     p.add_argument("--append-chunk", type=int, default=512)
     p.add_argument("--append-reps", type=int, default=4)
     p.add_argument("--cpu-units", type=int, default=16, help="(layer, kv head) units of the CPU sample")
@@ -304,7 +306,8 @@ def main():
     print("bench: %s, %d layers, ctx %d, tail %d, %s" % (args.fmt, L, args.ctx, args.tail,
           torch.cuda.get_device_name(0)), file=sys.stderr, flush=True)
     fk, fv = split_fmt(args.fmt)
-    cache = kvq.Cache(L, H, QH, fmt_k=fk, fmt_v=fv, tail_tokens=args.tail, n_seqs=1, max_tokens=args.ctx + extra)
+    cache = kvq.Cache(L, H, QH, fmt_k=fk, fmt_v=fv, tail_tokens=args.tail, n_seqs=1, max_tokens=args.ctx + extra,
+                      tail_dtype=args.tail_dtype)
     t0 = time.time()
     fill_cache(cache, wl, L, H, args.ctx)
     torch.cuda.synchronize()

@@ -85,10 +85,19 @@ typedef struct {
     int32_t n_q_heads;     /* multiple of n_kv_heads; n_q_heads / n_kv_heads <= 8 */
     int32_t head_dim;      /* must be 128 */
     int32_t fmt_k, fmt_v;  /* kv_format of the key and value caches (may differ) */
-    int32_t tail_tokens;   /* T: newest tokens kept in BF16 (0 = quantize everything) */
+    int32_t tail_tokens;   /* T: newest tokens kept at 16 bits (0 = quantize everything) */
     int32_t n_seqs;        /* sequences (batch slots) held by the cache */
     int64_t max_tokens;    /* capacity per sequence, in tokens */
+    int32_t tail_dtype;    /* KV_TAIL_BF16 (0, default) or KV_TAIL_F16: the 16-bit type of the
+                            * tail ring, and the canonical value every quantized row is encoded
+                            * from ("Экспериментальные методы квантизации KV-кэша в BeeLLama.cpp
+                            * v0.4.0", section "KV Cache Precision Tail": BF16 or F16).  An F16
+                            * value is the binary16 nearest the input (ties to even), saturated
+                            * to +-65504, zero as +0.  KV_TAIL_F16 excludes the bf16 format. */
+    int32_t reserved;      /* 0 */
 } kv_config;
+
+enum { KV_TAIL_BF16 = 0, KV_TAIL_F16 = 1 };
 
 typedef struct kv_cache kv_cache;   /* opaque host handle */
 

@@ -10,10 +10,11 @@
 //    normalized values ("Практическое руководство: запуск Bonsai-Ternary-27B на 120k
 //    токенах с менее чем 10 ГБ VRAM", sections "Решение: KVarN ..." and "Как
 //    преобразование Уолша-Адамара и Sinkhorn спасают качество при 4-битном сжатии").
-//  * k_ring_write: canonical bf16 rows of the newest tokens into the precision-tail ring.
+//  * k_ring_write: canonical 16-bit rows of the newest tokens into the precision-tail ring.
 //
-// Every value is the canonical bf16 of the input (fp32 inputs rounded to nearest even),
-// so codes depend only on a token's (or its page's) values, never on when it is spilled.
+// Every value is the canonical 16-bit form of the input, bf16 or (F16 tail) binary16, both
+// rounded to nearest even, so codes depend only on a token's (or its page's) values, never
+// on when it is spilled.
 #pragma clang fp contract(off)
 
 #include <float.h>
@@ -39,33 +40,39 @@ __device__ __forceinline__ const char* input_row(const AppendArgs& a, int lrel, 
 }
 
 // Load NV consecutive canonical values (as floats) starting at element e0 of a row that is
-// either bf16 (ring rows, bf16 inputs) or fp32 (rounded to bf16 first).
+// a ring row (canonical already), an fp32 input row or a bf16 input row (both rounded to
+// the canonical type first; a bf16 input is its own canonical value for a BF16 tail).
 template <int NV>
-__device__ __forceinline__ void load_canon(const char* row, bool f32, int e0, float (&x)[NV])
+__device__ __forceinline__ void load_canon(const char* row, bool f32, bool ring, bool f16, int e0, float (&x)[NV])
 {
     if (f32) {
         const float4* p = (const float4*)(row + 4 * e0);
 #pragma unroll
         for (int i = 0; i < NV / 4; ++i) {
             float4 w = p[i];
-            x[4 * i + 0] = bf16_to_f32(bf16_rne(w.x));
-            x[4 * i + 1] = bf16_to_f32(bf16_rne(w.y));
-            x[4 * i + 2] = bf16_to_f32(bf16_rne(w.z));
-            x[4 * i + 3] = bf16_to_f32(bf16_rne(w.w));
+            x[4 * i + 0] = canon_to_f32(canon_bits(w.x, f16), f16);
+            x[4 * i + 1] = canon_to_f32(canon_bits(w.y, f16), f16);
+            x[4 * i + 2] = canon_to_f32(canon_bits(w.z, f16), f16);
+            x[4 * i + 3] = canon_to_f32(canon_bits(w.w, f16), f16);
         }
     } else {
         const uint4* p = (const uint4*)(row + 2 * e0);
+        // ring rows hold the canonical type; bf16 input rows are rounded to binary16 for F16
+        const bool conv = f16 && !ring;
+        auto val = [&](uint32_t h) {
+            return conv ? canon_to_f32(canon_bits(bf16_to_f32(h), true), true) : canon_to_f32(h, f16 && ring);
+        };
 #pragma unroll
         for (int i = 0; i < NV / 8; ++i) {
             uint4 w = p[i];
-            x[8 * i + 0] = bf16_to_f32(w.x & 0xFFFFu);
-            x[8 * i + 1] = bf16_to_f32(w.x >> 16);
-            x[8 * i + 2] = bf16_to_f32(w.y & 0xFFFFu);
-            x[8 * i + 3] = bf16_to_f32(w.y >> 16);
-            x[8 * i + 4] = bf16_to_f32(w.z & 0xFFFFu);
-            x[8 * i + 5] = bf16_to_f32(w.z >> 16);
-            x[8 * i + 6] = bf16_to_f32(w.w & 0xFFFFu);
-            x[8 * i + 7] = bf16_to_f32(w.w >> 16);
+            x[8 * i + 0] = val(w.x & 0xFFFFu);
+            x[8 * i + 1] = val(w.x >> 16);
+            x[8 * i + 2] = val(w.y & 0xFFFFu);
+            x[8 * i + 3] = val(w.y >> 16);
+            x[8 * i + 4] = val(w.z & 0xFFFFu);
+            x[8 * i + 5] = val(w.z >> 16);
+            x[8 * i + 6] = val(w.w & 0xFFFFu);
+            x[8 * i + 7] = val(w.w >> 16);
         }
     }
 }
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(256) void k_encode_q(AppendArgs a, int64_t tokens, 
             *(uint4*)(codes + 64 * b + 16 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
     } else {
         float x[32];
-        load_canon<32>(src, f32, 32 * b, x);
+        load_canon<32>(src, f32, from_ring, a.g.tail_f16 != 0, 32 * b, x);
         uint32_t u[32];
         uint32_t packed[N];
         char* scales = st + L.scales + p * (fscale_halves(FMT) * 2);
@@ -289,15 +296,27 @@ __global__ __launch_bounds__(256) void k_ring_write(AppendArgs a, int64_t tokens
     const StreamLayout& L = sv ? a.g.v : a.g.k;
     const char* src = input_row(a, lrel, s.in_row0 + (p - s.n_old), head, sv);
     char* dst = st + L.ring + (p % a.g.ring_slots) * 256 + 32 * part;
+    const bool f16 = a.g.tail_f16 != 0;
     if (a.in_dtype == 1) {
         const float4* q = (const float4*)(src + 64 * part);
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float4 v = q[i];
-            o[2 * i] = bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16);
-            o[2 * i + 1] = bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16);
+            o[2 * i] = canon_bits(v.x, f16) | (canon_bits(v.y, f16) << 16);
+            o[2 * i + 1] = canon_bits(v.z, f16) | (canon_bits(v.w, f16) << 16);
         }
+        *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
+        *(uint4*)(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+    } else if (f16) {
+        // bf16 input, binary16 ring
+        const uint4* q = (const uint4*)(src + 32 * part);
+        const uint4 w0 = q[0], w1 = q[1];
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] = canon_bits(bf16_to_f32(w[i] & 0xFFFFu), true) | (canon_bits(bf16_to_f32(w[i] >> 16), true) << 16);
         *(uint4*)dst = make_uint4(o[0], o[1], o[2], o[3]);
         *(uint4*)(dst + 16) = make_uint4(o[4], o[5], o[6], o[7]);
     } else {
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages,
     const char* src = from_ring ? st + L.ring + (p % a.g.ring_slots) * 256
                                 : input_row(a, lrel, s.in_row0 + (p - s.n_old), head, sv);
     float y[64];
-    load_canon<64>(src, !from_ring && a.in_dtype == 1, 64 * half, y);
+    load_canon<64>(src, !from_ring && a.in_dtype == 1, from_ring, a.g.tail_f16 != 0, 64 * half, y);
 #pragma unroll
     for (int h = 1; h < 64; h <<= 1) {
 #pragma unroll

@@ -116,15 +116,16 @@ __device__ __forceinline__ void dequant16(const char* st, const StreamLayout& L,
     }
 }
 
-__device__ __forceinline__ void ring16(const char* st, const StreamLayout& L, int64_t slot, int part, float (&x)[16])
+__device__ __forceinline__ void ring16(const char* st, const StreamLayout& L, int64_t slot, int part, bool f16,
+                                      float (&x)[16])
 {
     const uint4* p = (const uint4*)(st + L.ring + slot * 256 + 32 * part);
     uint4 a = p[0], b = p[1];
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-        x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        x[2 * i] = canon_to_f32(w[i] & 0xFFFFu, f16);
+        x[2 * i + 1] = canon_to_f32(w[i] >> 16, f16);
     }
 }
 
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
                 const int64_t tc = valid ? t : t1 - 1;
                 const int64_t rs = tc % g.ring_slots;
                 float k[16], v[16];
-                ring16(kst, g.k, rs, part, k);
-                ring16(vst, g.v, rs, part, v);
+                ring16(kst, g.k, rs, part, g.tail_f16 != 0, k);
+                ring16(vst, g.v, rs, part, g.tail_f16 != 0, v);
                 online_step(o, qr, k, v, valid);
             }
         }
@@ -553,7 +554,7 @@ __global__ __launch_bounds__(256) void k_kld(KldArgs a)
             }
             dequant16<FK>(kst, g.k, tc, part, ck, k);
         } else {
-            ring16(kst, g.k, tc % g.ring_slots, part, k);
+            ring16(kst, g.k, tc % g.ring_slots, part, g.tail_f16 != 0, k);
         }
         {
             const uint4* pr = (const uint4*)(a.k_ref + (tc * g.n_kv_heads + head) * kD + 16 * part);
@@ -561,8 +562,8 @@ __global__ __launch_bounds__(256) void k_kld(KldArgs a)
             const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                kx[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                kx[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
+                kx[2 * i] = canon_to_f32(ww[i] & 0xFFFFu, g.tail_f16 != 0);
+                kx[2 * i + 1] = canon_to_f32(ww[i] >> 16, g.tail_f16 != 0);
             }
         }
 #pragma unroll

@@ -1119,8 +1119,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                         float kx[16];
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
-                            kx[2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                            kx[2 * i + 1] = bf16_to_f32(ww[i] >> 16);
+                            kx[2 * i] = canon_to_f32(ww[i] & 0xFFFFu, g.tail_f16 != 0);
+                            kx[2 * i + 1] = canon_to_f32(ww[i] >> 16, g.tail_f16 != 0);
                         }
 #pragma unroll
                         for (int h = 0; h < kG; ++h) {
@@ -1201,8 +1201,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                         const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
-                            vx[t][2 * i] = bf16_to_f32(ww[i] & 0xFFFFu);
-                            vx[t][2 * i + 1] = bf16_to_f32(ww[i] >> 16);
+                            vx[t][2 * i] = canon_to_f32(ww[i] & 0xFFFFu, g.tail_f16 != 0);
+                            vx[t][2 * i + 1] = canon_to_f32(ww[i] >> 16, g.tail_f16 != 0);
                         }
                     }
                     float pp[4][2];

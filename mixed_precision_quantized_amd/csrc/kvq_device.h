@@ -80,6 +80,18 @@ __device__ __forceinline__ float fp16_to_f32(uint32_t h)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
+// A canonical 16-bit value (ring rows): bf16, or binary16 for an F16 tail.
+__device__ __forceinline__ float canon_to_f32(uint32_t h, bool f16)
+{
+    return f16 ? fp16_to_f32(h & 0xFFFFu) : bf16_to_f32(h & 0xFFFFu);
+}
+// The canonical 16 bits of an input value: bf16 by RNE, or binary16 by RNE, saturated to
+// +-65504 with zero as +0 (the same conversion as the block scales).
+__device__ __forceinline__ uint32_t canon_bits(float x, bool f16)
+{
+    return f16 ? (uint32_t)fp16s_rne(x) : (uint32_t)bf16_rne(x);
+}
+
 // ------------------------------------------------------------------ packed codes
 // Extract code i (0-based within a group) of N bits from a little-endian bit stream held
 // in 32-bit words w[] (word 0 holds stream bits 0..31).

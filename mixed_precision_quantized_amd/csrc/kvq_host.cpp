@@ -98,6 +98,8 @@ int plan_config(const kv_config* cfg, CacheGeom* geom, int64_t* total, int64_t* 
         cfg->max_tokens < 1 || cfg->tail_tokens < 0)
         return KV_EINVAL;
     if (cfg->n_q_heads % cfg->n_kv_heads) return KV_EINVAL;
+    if (cfg->tail_dtype != KV_TAIL_BF16 && cfg->tail_dtype != KV_TAIL_F16) return KV_EINVAL;
+    if (cfg->tail_dtype == KV_TAIL_F16 && (cfg->fmt_k == KV_BF16 || cfg->fmt_v == KV_BF16)) return KV_EUNSUPPORTED;
     FormatDesc fk, fv;
     if (!format_desc(cfg->fmt_k, &fk) || !format_desc(cfg->fmt_v, &fv)) return KV_EINVAL;
     if (cfg->head_dim != kD) return KV_EUNSUPPORTED;
@@ -124,6 +126,7 @@ int plan_config(const kv_config* cfg, CacheGeom* geom, int64_t* total, int64_t* 
     gm.n_q_heads = cfg->n_q_heads;
     gm.group = group;
     gm.ring_slots = (int32_t)r;
+    gm.tail_f16 = cfg->tail_dtype == KV_TAIL_F16 ? 1 : 0;
     double units = (double)cfg->n_seqs * cfg->n_layers * cfg->n_kv_heads;
     if (units * (double)gm.unit_bytes > 9.0e18) return KV_EINVAL;
     if (geom) *geom = gm;

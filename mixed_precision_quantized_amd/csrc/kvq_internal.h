@@ -43,7 +43,7 @@ struct CacheGeom {
     int32_t fmt_k, fmt_v;
     int32_t n_layers, n_kv_heads, n_q_heads, group;
     int32_t ring_slots;   // R
-    int32_t pad_;
+    int32_t tail_f16;     // 16-bit type of the ring and of canonical values: 0 bf16, 1 binary16
 };
 
 // Per-sequence entry of an append launch.

@@ -201,8 +201,8 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            kx[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-            kx[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+            kx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
+            kx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
     }
     if (quant && KV != KIND_BF16) {
@@ -230,8 +230,8 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            vx[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-            vx[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+            vx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
+            vx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
     }
     if (!valid) {

@@ -41,7 +41,8 @@ class KVConfig(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("fmt_k", ctypes.c_int32), ("fmt_v", ctypes.c_int32),
                 ("tail_tokens", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int64)]
+                ("max_tokens", ctypes.c_int64), ("tail_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -125,10 +126,13 @@ def format_info(fmt):
     return tuple(v.value for v in vals)
 
 
+TAIL_DTYPES = {"bf16": 0, "f16": 1}
+
+
 def make_config(n_layers, n_kv_heads, n_q_heads, fmt_k, fmt_v, tail_tokens, n_seqs, max_tokens,
-                head_dim=128) -> KVConfig:
+                head_dim=128, tail_dtype="bf16") -> KVConfig:
     return KVConfig(n_layers, n_kv_heads, n_q_heads, head_dim, fmt_id(fmt_k), fmt_id(fmt_v),
-                    tail_tokens, n_seqs, max_tokens)
+                    tail_tokens, n_seqs, max_tokens, TAIL_DTYPES[tail_dtype], 0)
 
 
 def cache_bytes(cfg: KVConfig) -> int:
@@ -139,10 +143,11 @@ class Cache:
     """A cache over one caller-owned device buffer (a torch uint8 tensor)."""
 
     def __init__(self, n_layers, n_kv_heads, n_q_heads, fmt=None, tail_tokens=0, n_seqs=1,
-                 max_tokens=4096, fmt_k=None, fmt_v=None, device="cuda"):
+                 max_tokens=4096, fmt_k=None, fmt_v=None, device="cuda", tail_dtype="bf16"):
         fk = fmt_k if fmt_k is not None else fmt
         fv = fmt_v if fmt_v is not None else fmt
-        self.cfg = make_config(n_layers, n_kv_heads, n_q_heads, fk, fv, tail_tokens, n_seqs, max_tokens)
+        self.cfg = make_config(n_layers, n_kv_heads, n_q_heads, fk, fv, tail_tokens, n_seqs, max_tokens,
+                               tail_dtype=tail_dtype)
         nbytes = cache_bytes(self.cfg)
         if nbytes < 0:
             raise KVError(nbytes, "kv_cache_bytes")

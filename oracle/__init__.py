@@ -79,6 +79,10 @@ def lib():
                                     _u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p, _u16p,
                                     ctypes.c_int, _f64p, ctypes.c_double, _f64p]
         L.kvo_attention.restype = ctypes.c_int
+        L.kvo_set_canonical_f16.argtypes = [ctypes.c_int]
+        L.kvo_set_canonical_f16.restype = None
+        L.kvo_canonical_f16.argtypes = []
+        L.kvo_canonical_f16.restype = ctypes.c_int
         L.kvo_prefill_attention.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                             ctypes.c_int, _u8p, _u16p, _u16p, _u8p, _u16p, _u16p, _u16p,
                                             _u16p, ctypes.c_int, _f64p, ctypes.c_double, _f64p]
@@ -112,6 +116,50 @@ def fp16s_from_f32(x: float) -> int:
 
 def f64_from_fp16(h: int) -> float:
     return float(lib().kvo_f64_from_fp16(int(h)))
+
+
+def set_canonical_f16(on: bool) -> None:
+    """Canonical 16-bit type of the values the oracle encodes and attends over: bf16
+    (default) or binary16 (an F16 tail).  Process-wide; see canonical()."""
+    lib().kvo_set_canonical_f16(1 if on else 0)
+
+
+def canonical_f16() -> bool:
+    return bool(lib().kvo_canonical_f16())
+
+
+class canonical:
+    """with canonical("f16"): ... -- the oracle's canonical type inside the block."""
+
+    def __init__(self, dtype: str):
+        assert dtype in ("bf16", "f16")
+        self.on = dtype == "f16"
+
+    def __enter__(self):
+        self.prev = canonical_f16()
+        set_canonical_f16(self.on)
+        return self
+
+    def __exit__(self, *exc):
+        set_canonical_f16(self.prev)
+        return False
+
+
+def canon_f16(x: np.ndarray) -> np.ndarray:
+    """Canonical binary16 bits of token values: float32 values, or bf16 bits (uint16), to
+    the nearest binary16 (ties to even), saturated to +-65504, zero as +0 -- the oracle's
+    scalar kvo_fp16s_from_f32, vectorized (numpy's float16 cast rounds to nearest even)."""
+    if x.dtype == np.uint16:
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.clip(x, -65504.0, 65504.0).astype(np.float16)
+    y[y == 0] = 0.0
+    return y.view(np.uint16)
+
+
+def canon(x: np.ndarray) -> np.ndarray:
+    """Canonical 16-bit bits of token values in the current canonical type."""
+    return canon_f16(x) if canonical_f16() else canon_bf16(x)
 
 
 def canon_bf16(x: np.ndarray) -> np.ndarray:

@@ -28,6 +28,15 @@ float kvo_f32_from_bf16(uint16_t b)
     return f32_from_bits((uint32_t)b << 16);
 }
 
+/* The canonical 16-bit type of the cache's values: bf16 (default) or binary16 (an F16
+ * tail, "Экспериментальные методы квантизации KV-кэша в BeeLLama.cpp v0.4.0", section
+ * "KV Cache Precision Tail": the tail is BF16 or F16).  Every function below that takes
+ * canonical 16-bit values reads them in this type. */
+static int g_canon_f16 = 0;
+void kvo_set_canonical_f16(int on) { g_canon_f16 = on ? 1 : 0; }
+int kvo_canonical_f16(void) { return g_canon_f16; }
+static double f64_from_canon(uint16_t b);
+
 /* Round x (finite) to the nearest multiple of 'quantum' (a power of two), ties to an
  * even multiple.  x/quantum is exact in binary64 because x has at most 24 significant
  * bits; rint() in the default rounding mode is round-half-to-even. */
@@ -121,6 +130,8 @@ uint16_t kvo_fp16s_from_f32(float xf)
 }
 
 static float f32_from_fp16(uint16_t h) { return (float)kvo_f64_from_fp16(h); }
+static double f64_from_canon(uint16_t b) { return g_canon_f16 ? kvo_f64_from_fp16(b) : (double)kvo_f32_from_bf16(b); }
+static float f32_from_canon(uint16_t b) { return (float)f64_from_canon(b); }
 
 /* ======================================================================== */
 /* Format table                                                              */
@@ -321,7 +332,7 @@ void kvo_encode_page_kvarn(int N, const uint16_t* X, uint8_t* codes, uint16_t* s
     /* 1. rotation of every token vector */
     for (int t = 0; t < 128; ++t) {
         float* y = Y + t * 128;
-        for (int i = 0; i < 128; ++i) y[i] = kvo_f32_from_bf16(X[t * 128 + i]);
+        for (int i = 0; i < 128; ++i) y[i] = f32_from_canon(X[t * 128 + i]);
         kvo_fwht128_f32(y);
     }
     /* 2. squares */
@@ -364,7 +375,7 @@ int kvo_encode_token(int fmt, const uint16_t* x, uint8_t* codes, uint16_t* scale
     if (kind == KVO_KIND_KVARN) return -1;      /* pages only */
     float xf[128];
     uint8_t u[128];
-    for (int i = 0; i < 128; ++i) xf[i] = kvo_f32_from_bf16(x[i]);
+    for (int i = 0; i < 128; ++i) xf[i] = f32_from_canon(x[i]);
     for (int b = 0; b < 4; ++b) {
         if (kind == KVO_KIND_Q0) {
             kvo_encode_block_q0(N, xf + 32 * b, &scales[b], u + 32 * b);
@@ -519,8 +530,8 @@ int kvo_attention(int64_t n, int64_t n_q, int fmt_k, int fmt_v,
     kvo_dequant_stream(fmt_v, n_q, vq_codes, vq_scales, vq_cscale, V);
     for (int64_t t = n_q; t < n; ++t) {
         for (int i = 0; i < 128; ++i) {
-            K[t * 128 + i] = (double)kvo_f32_from_bf16(k_tail[(t - n_q) * 128 + i]);
-            V[t * 128 + i] = (double)kvo_f32_from_bf16(v_tail[(t - n_q) * 128 + i]);
+            K[t * 128 + i] = f64_from_canon(k_tail[(t - n_q) * 128 + i]);
+            V[t * 128 + i] = f64_from_canon(v_tail[(t - n_q) * 128 + i]);
         }
     }
     for (int h = 0; h < g; ++h) {
@@ -567,14 +578,14 @@ int kvo_attention_kld(int64_t n, int64_t n_q, int fmt_k, const uint8_t* kq_codes
     /* the cache's keys: dequantized below n_q, the exact bf16 rows above */
     if (n_q > 0) kvo_dequant_stream(fmt_k, n_q, kq_codes, kq_scales, kq_cscale, K);
     for (int64_t t = n_q; t < n; ++t)
-        for (int i = 0; i < 128; ++i) K[t * 128 + i] = (double)kvo_f32_from_bf16(k_exact[t * 128 + i]);
+        for (int i = 0; i < 128; ++i) K[t * 128 + i] = f64_from_canon(k_exact[t * 128 + i]);
     for (int h = 0; h < g; ++h) {
         const double* qh = q + h * 128;
         double Me = -INFINITY, Mq = -INFINITY;
         for (int64_t t = 0; t < n; ++t) {
             double a = 0.0, b = 0.0;
             for (int i = 0; i < 128; ++i) {
-                a += qh[i] * (double)kvo_f32_from_bf16(k_exact[t * 128 + i]);
+                a += qh[i] * f64_from_canon(k_exact[t * 128 + i]);
                 b += qh[i] * K[t * 128 + i];
             }
             se[t] = sigma * a;
@@ -629,8 +640,8 @@ int kvo_prefill_attention(int64_t n, int64_t n_q, int64_t n_new, int fmt_k, int 
     }
     for (int64_t t = n_q; t < n; ++t) {
         for (int i = 0; i < 128; ++i) {
-            K[t * 128 + i] = (double)kvo_f32_from_bf16(k_tail[(t - n_q) * 128 + i]);
-            V[t * 128 + i] = (double)kvo_f32_from_bf16(v_tail[(t - n_q) * 128 + i]);
+            K[t * 128 + i] = f64_from_canon(k_tail[(t - n_q) * 128 + i]);
+            V[t * 128 + i] = f64_from_canon(v_tail[(t - n_q) * 128 + i]);
         }
     }
     for (int64_t qi = 0; qi < n_new; ++qi) {

@@ -64,6 +64,11 @@ enum { KVO_KIND_BF16 = 0, KVO_KIND_Q0 = 1, KVO_KIND_Q1 = 2, KVO_KIND_KVARN = 3 }
 /* bf16(x): round-to-nearest-even to an 8-bit significand.  Precondition: x finite. */
 uint16_t kvo_bf16_from_f32(float x);
 float    kvo_f32_from_bf16(uint16_t b);
+
+/* The canonical 16-bit type of values passed to the encoders, the ring image and the
+ * attention references: bf16 (0, the default) or binary16 (1, an F16 tail).  Process-wide. */
+void kvo_set_canonical_f16(int on);
+int  kvo_canonical_f16(void);
 /* fp16s(x): round-to-nearest-even to binary16, then +-inf -> +-65504 (saturate);
  * a zero result is always stored as +0 (0x0000).  Precondition: x finite. */
 uint16_t kvo_fp16s_from_f32(float x);

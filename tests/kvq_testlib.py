@@ -57,11 +57,13 @@ def chunk_list(n, pattern):
 
 
 def canon_rows(wl, seq, layer, head, is_v, t0, t1) -> np.ndarray:
-    """Canonical bf16 bits of a stream as the oracle defines them (CPU generation)."""
+    """Canonical 16-bit bits of a stream as the oracle defines them (CPU generation), in the
+    oracle's current canonical type (bf16, or binary16 inside O.canonical("f16"))."""
     x = synth.kv_rows(wl, seq, layer, head, is_v, t0, t1, "cpu")
     if workload_dtype(wl) == torch.bfloat16:
-        return synth.bf16_as_u16(synth.to_bf16_bits(x))
-    return O.canon_bf16(x.numpy())
+        b = synth.bf16_as_u16(synth.to_bf16_bits(x))
+        return O.canon_f16(b) if O.canonical_f16() else b
+    return O.canon(x.numpy())
 
 
 def split_fmt(fmt: str):

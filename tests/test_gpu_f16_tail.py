@@ -1,0 +1,75 @@
+"""GPU parity of the F16-tail option (tail_dtype = KV_TAIL_F16) against the oracle in its
+binary16 canonical mode, through the C ABI: codes, scales, channel scales and ring rows
+byte-identical, decode attention within 2e-3 normwise per head; fp32 and bf16 inputs
+(the bf16 ones are rounded to binary16 on append); one prefill and one KL check; the bf16
+format is refused with an F16 tail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_quantized_amd import kvq
+
+import kvq_testlib as T
+
+pytestmark = pytest.mark.gpu
+SIGMA = 1.0 / math.sqrt(128)
+TOL = 2e-3
+
+
+@pytest.mark.parametrize("wl", ["c1_q4_0_ctx4096", "c3_kvarn_ctx65536"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q3_1", "kvarn4", "q8_0/q4_1", "kvarn2/q6_0"])
+def test_f16_tail_streams_and_decode(fmt, wl):
+    n, tail, H = 1500, 300, 2
+    with O.canonical("f16"):
+        cache = T.make_cache(fmt, 2, H, 4 * H, tail_tokens=tail, n_seqs=1, max_tokens=n, tail_dtype="f16")
+        T.fill(cache, wl, 0, [0, 1], H, n, T.chunk_list(n, [555, 1, 321]))
+        torch.cuda.synchronize()
+        for layer in (0, 1):
+            for h in range(H):
+                for is_v in (0, 1):
+                    T.compare_stream(cache, fmt, T.canon_rows(wl, 0, layer, h, is_v, 0, n), 0, layer, h, is_v)
+        q = T.query(wl, 0, 1, 0, 4 * H, "cuda").unsqueeze(0)
+        out = cache.decode(1, [0], q)[0].cpu().numpy()
+        _, n_q = cache.seq_get(0, 1)
+        qv = T.query_values(q)[0]
+        for h in range(H):
+            k, v = T.canon_rows(wl, 0, 1, h, 0, 0, n), T.canon_rows(wl, 0, 1, h, 1, 0, n)
+            ref = T.oracle_attention(fmt, k, v, n, n_q, qv[4 * h:4 * h + 4], SIGMA)
+            e = T.rel_err(out[4 * h:4 * h + 4], ref)
+            assert e <= TOL, "%s head %d: rel err %.3g" % (fmt, h, e)
+
+
+def test_f16_tail_prefill_and_kld():
+    wl, fmt, n, n_new, tail, H = "c3_kvarn_ctx65536", "kvarn4", 1200, 100, 256, 2
+    with O.canonical("f16"):
+        cache = kvq.Cache(1, H, 4 * H, fmt, tail_tokens=tail, n_seqs=1, max_tokens=n, tail_dtype="f16")
+        T.fill(cache, wl, 0, [0], H, n, [n - n_new, n_new])
+        qs = torch.stack([T.query(wl, 0, 0, i, 4 * H, "cuda") for i in range(n_new)], 0).contiguous()
+        out = cache.prefill(0, 0, qs).cpu().numpy()
+        _, n_q = cache.seq_get(0, 0)
+        qv = T.query_values(qs)
+        rows = [T.canon_rows(wl, 0, 0, h, 0, 0, n) for h in range(H)]
+        f = O.FORMAT_NAMES.index(fmt)
+        for h in range(H):
+            v = T.canon_rows(wl, 0, 0, h, 1, 0, n)
+            kq, vq = O.encode_stream(f, n_q, rows[h]), O.encode_stream(f, n_q, v)
+            ref = O.prefill_attention(n, n_q, n_new, f, f, kq, vq, rows[h][n_q:], v[n_q:], qv[:, 4 * h:4 * h + 4], SIGMA)
+            g = out[:, 4 * h:4 * h + 4].reshape(-1, 128).astype(np.float64)
+            r = ref.reshape(-1, 128)
+            assert np.max(np.abs(g - r).max(axis=1) / np.abs(r).max(axis=1)) <= TOL
+        k_ref = torch.from_numpy(np.ascontiguousarray(np.stack(rows, 1)).view(np.int16)).cuda()
+        q1 = T.query(wl, 0, 0, 0, 4 * H, "cuda")
+        got = cache.attn_kld(0, 0, q1, k_ref).cpu().numpy().astype(np.float64)
+        q1v = T.query_values(q1)
+        for h in range(H):
+            ref = O.attention_kld(n, n_q, f, O.encode_stream(f, n_q, rows[h]), rows[h], q1v[4 * h:4 * h + 4], SIGMA)
+            assert np.all(np.abs(got[4 * h:4 * h + 4] - ref) <= 1e-2 * ref + 1e-9)
+
+
+def test_f16_tail_refuses_bf16_format():
+    with pytest.raises(kvq.KVError):
+        kvq.Cache(1, 1, 4, "bf16", tail_tokens=64, max_tokens=256, tail_dtype="f16")
