@@ -40,6 +40,7 @@
 #pragma once
 
 #include <float.h>
+#include <type_traits>
 
 #include "kvq_device.h"
 
@@ -1081,149 +1082,155 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
     } else {
-        // ========================= BF16 ring chunks (binary32) =========================
-        // units of 32 tokens; a step is two halves of 16 tokens (8 lanes per token pair)
-        const int R = g.ring_slots;
-        load_query();
-        if (kwave) {
-            float mh = kNeg;                           // running max of the lane's head kb
-            float lsum = 0.0f;                         // sum of p of the lane's head
-            float qr[kG][16];
+        // ========================= 16-bit ring chunks (binary32) =========================
+        // compiled once per ring type (BF16 or binary16), chosen once per workgroup
+        auto ring_role = [&](auto f16_tag) __attribute__((always_inline)) {
+            constexpr bool F16 = decltype(f16_tag)::value;
+            // units of 32 tokens; a step is two halves of 16 tokens (8 lanes per token pair)
+            const int R = g.ring_slots;
+            load_query();
+            if (kwave) {
+                float mh = kNeg;                           // running max of the lane's head kb
+                float lsum = 0.0f;                         // sum of p of the lane's head
+                float qr[kG][16];
 #pragma unroll
-            for (int h = 0; h < kG; ++h)
+                for (int h = 0; h < kG; ++h)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) qr[h][j] = S.qs[h][16 * vp + j];
-            int j = 0;
+                    for (int j = 0; j < 16; ++j) qr[h][j] = S.qs[h][16 * vp + j];
+                int j = 0;
 #pragma unroll 1
-            for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
-                const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
-                const uint32_t tbm = (uint32_t)(tb % R);
-                float sc[2][kG][2];
+                for (; j < J; ++j) {
+                    const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
+                    const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
+                    const uint32_t tbm = (uint32_t)(tb % R);
+                    float sc[2][kG][2];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int off = 16 * half + 2 * vg;
-                    uint4 w[2][2];
+                    for (int half = 0; half < 2; ++half) {
+                        const int off = 16 * half + 2 * vg;
+                        uint4 w[2][2];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int o = min<int64_t>(off + t, te - tb - 1);
-                        const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
-                        const uint4* pk = (const uint4*)(kst + g.k.ring + (int64_t)rs * 256 + 32 * vp);
-                        w[t][0] = pk[0];
-                        w[t][1] = pk[1];
-                    }
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const uint32_t ww[8] = {w[t][0].x, w[t][0].y, w[t][0].z, w[t][0].w,
-                                                w[t][1].x, w[t][1].y, w[t][1].z, w[t][1].w};
-                        float kx[16];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            kx[2 * i] = canon_to_f32(ww[i] & 0xFFFFu, g.tail_f16 != 0);
-                            kx[2 * i + 1] = canon_to_f32(ww[i] >> 16, g.tail_f16 != 0);
+                        for (int t = 0; t < 2; ++t) {
+                            const int o = min<int64_t>(off + t, te - tb - 1);
+                            const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
+                            const uint4* pk = (const uint4*)(kst + g.k.ring + (int64_t)rs * 256 + 32 * vp);
+                            w[t][0] = pk[0];
+                            w[t][1] = pk[1];
                         }
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const uint32_t ww[8] = {w[t][0].x, w[t][0].y, w[t][0].z, w[t][0].w,
+                                                    w[t][1].x, w[t][1].y, w[t][1].z, w[t][1].w};
+                            float kx[16];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                kx[2 * i] = canon_to_f32(ww[i] & 0xFFFFu, F16);
+                                kx[2 * i + 1] = canon_to_f32(ww[i] >> 16, F16);
+                            }
+#pragma unroll
+                            for (int h = 0; h < kG; ++h) {
+                                float x = 0.0f;
+#pragma unroll
+                                for (int jj = 0; jj < 16; ++jj) x = fmaf(qr[h][jj], kx[jj], x);
+                                x += dpp<QP_XOR1>(x);
+                                x += dpp<QP_XOR2>(x);
+                                x += dpp<ROW_HMIRROR>(x);
+                                sc[half][h][t] = (tb + off + t < te) ? x : kNeg;
+                            }
+                        }
+                    }
+                    // each lane keeps the scores of head vp & 3; lanes with equal vp share a head
+                    const int hv = vp & 3;
+                    float x[2][2];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const f32x4 v = {sc[half][0][t], sc[half][1][t], sc[half][2][t], sc[half][3][t]};
+                            x[half][t] = v[hv];
+                        }
+                    const float nm = fmaxf(mh, wave_max8(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[1][0], x[1][1]))));
+                    const float al = __builtin_amdgcn_exp2f(mh - nm);    // exactly 1 if unchanged
+                    mh = nm;
+                    lsum *= al;
+                    PBuf& P = S.pb[pr][j & 1];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int off = 16 * half + 2 * vg;
+                        const float p0 = (tb + off < te) ? __builtin_amdgcn_exp2f(x[half][0] - mh) : 0.0f;
+                        const float p1 = (tb + off + 1 < te) ? __builtin_amdgcn_exp2f(x[half][1] - mh) : 0.0f;
+                        if (vp < kG) {
+                            *(float2*)&P.p[vp][16 * half + 2 * vg] = make_float2(p0, p1);
+                            lsum += p0 + p1;
+                        }
+                    }
+                    if (lane < kG) P.alpha[lane] = al;
+                    __syncthreads();
+                }
+#pragma unroll 1
+                for (; j <= Jmax; ++j) __syncthreads();
+                finish_k(mh, lsum);
+            } else {
+                float acc[kG][16];
+#pragma unroll
+                for (int h = 0; h < kG; ++h)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
+                __syncthreads();
+                int j = 0;
+#pragma unroll 1
+                for (; j < J; ++j) {
+                    const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
+                    const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
+                    const uint32_t tbm = (uint32_t)(tb % R);
+                    const PBuf& P = S.pb[pr][j & 1];
+                    const float4 al = *(const float4*)P.alpha;
+                    if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
+                        const float alv[kG] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+                        for (int h = 0; h < kG; ++h)
+#pragma unroll
+                            for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
+                    }
+#pragma unroll 1
+                    for (int half = 0; half < 2; ++half) {
+                        const int slot = vg + 8 * half;
+                        const int off = 2 * slot;
+                        float vx[2][16];
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const int o = min<int64_t>(off + t, te - tb - 1);
+                            const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
+                            const uint4* pv = (const uint4*)(vst + g.v.ring + (int64_t)rs * 256 + 32 * vp);
+                            const uint4 w0 = pv[0], w1 = pv[1];
+                            const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                vx[t][2 * i] = canon_to_f32(ww[i] & 0xFFFFu, F16);
+                                vx[t][2 * i + 1] = canon_to_f32(ww[i] >> 16, F16);
+                            }
+                        }
+                        float pp[4][2];
 #pragma unroll
                         for (int h = 0; h < kG; ++h) {
-                            float x = 0.0f;
-#pragma unroll
-                            for (int jj = 0; jj < 16; ++jj) x = fmaf(qr[h][jj], kx[jj], x);
-                            x += dpp<QP_XOR1>(x);
-                            x += dpp<QP_XOR2>(x);
-                            x += dpp<ROW_HMIRROR>(x);
-                            sc[half][h][t] = (tb + off + t < te) ? x : kNeg;
+                            const float2 w = *(const float2*)&P.p[h][2 * slot];
+                            pp[h][0] = w.x;
+                            pp[h][1] = w.y;
                         }
+#pragma unroll
+                        for (int h = 0; h < kG; ++h)
+#pragma unroll
+                            for (int jj = 0; jj < 16; ++jj)
+                                acc[h][jj] = fmaf(pp[h][0], vx[0][jj], fmaf(pp[h][1], vx[1][jj], acc[h][jj]));
                     }
+                    __syncthreads();
                 }
-                // each lane keeps the scores of head vp & 3; lanes with equal vp share a head
-                const int hv = vp & 3;
-                float x[2][2];
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const f32x4 v = {sc[half][0][t], sc[half][1][t], sc[half][2][t], sc[half][3][t]};
-                        x[half][t] = v[hv];
-                    }
-                const float nm = fmaxf(mh, wave_max8(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[1][0], x[1][1]))));
-                const float al = __builtin_amdgcn_exp2f(mh - nm);    // exactly 1 if unchanged
-                mh = nm;
-                lsum *= al;
-                PBuf& P = S.pb[pr][j & 1];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int off = 16 * half + 2 * vg;
-                    const float p0 = (tb + off < te) ? __builtin_amdgcn_exp2f(x[half][0] - mh) : 0.0f;
-                    const float p1 = (tb + off + 1 < te) ? __builtin_amdgcn_exp2f(x[half][1] - mh) : 0.0f;
-                    if (vp < kG) {
-                        *(float2*)&P.p[vp][16 * half + 2 * vg] = make_float2(p0, p1);
-                        lsum += p0 + p1;
-                    }
-                }
-                if (lane < kG) P.alpha[lane] = al;
-                __syncthreads();
+#pragma unroll 1
+                for (++j; j <= Jmax; ++j) __syncthreads();
+                finish_v(acc);
             }
-#pragma unroll 1
-            for (; j <= Jmax; ++j) __syncthreads();
-            finish_k(mh, lsum);
-        } else {
-            float acc[kG][16];
-#pragma unroll
-            for (int h = 0; h < kG; ++h)
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) acc[h][jj] = 0.0f;
-            __syncthreads();
-            int j = 0;
-#pragma unroll 1
-            for (; j < J; ++j) {
-                const int64_t tb = sq.n_q + (int64_t)(u_first + kP * j) * kTailUnit;
-                const int64_t te = min<int64_t>(tb + kTailUnit, sq.n);
-                const uint32_t tbm = (uint32_t)(tb % R);
-                const PBuf& P = S.pb[pr][j & 1];
-                const float4 al = *(const float4*)P.alpha;
-                if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
-                    const float alv[kG] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-                    for (int h = 0; h < kG; ++h)
-#pragma unroll
-                        for (int jj = 0; jj < 16; ++jj) acc[h][jj] *= alv[h];
-                }
-#pragma unroll 1
-                for (int half = 0; half < 2; ++half) {
-                    const int slot = vg + 8 * half;
-                    const int off = 2 * slot;
-                    float vx[2][16];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int o = min<int64_t>(off + t, te - tb - 1);
-                        const uint32_t rs = (tbm + (uint32_t)o) % (uint32_t)R;
-                        const uint4* pv = (const uint4*)(vst + g.v.ring + (int64_t)rs * 256 + 32 * vp);
-                        const uint4 w0 = pv[0], w1 = pv[1];
-                        const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            vx[t][2 * i] = canon_to_f32(ww[i] & 0xFFFFu, g.tail_f16 != 0);
-                            vx[t][2 * i + 1] = canon_to_f32(ww[i] >> 16, g.tail_f16 != 0);
-                        }
-                    }
-                    float pp[4][2];
-#pragma unroll
-                    for (int h = 0; h < kG; ++h) {
-                        const float2 w = *(const float2*)&P.p[h][2 * slot];
-                        pp[h][0] = w.x;
-                        pp[h][1] = w.y;
-                    }
-#pragma unroll
-                    for (int h = 0; h < kG; ++h)
-#pragma unroll
-                        for (int jj = 0; jj < 16; ++jj)
-                            acc[h][jj] = fmaf(pp[h][0], vx[0][jj], fmaf(pp[h][1], vx[1][jj], acc[h][jj]));
-                }
-                __syncthreads();
-            }
-#pragma unroll 1
-            for (++j; j <= Jmax; ++j) __syncthreads();
-            finish_v(acc);
-        }
+        };
+        if (g.tail_f16) ring_role(std::true_type{});
+        else ring_role(std::false_type{});
     }
 
     __syncthreads();
