@@ -42,8 +42,8 @@ __device__ __forceinline__ const char* input_row(const AppendArgs& a, int lrel, 
 // Load NV consecutive canonical values (as floats) starting at element e0 of a row that is
 // a ring row (canonical already), an fp32 input row or a bf16 input row (both rounded to
 // the canonical type first; a bf16 input is its own canonical value for a BF16 tail).
-template <int NV>
-__device__ __forceinline__ void load_canon(const char* row, bool f32, bool ring, bool f16, int e0, float (&x)[NV])
+template <int NV, bool f16>
+__device__ __forceinline__ void load_canon_t(const char* row, bool f32, bool ring, int e0, float (&x)[NV])
 {
     if (f32) {
         const float4* p = (const float4*)(row + 4 * e0);
@@ -75,6 +75,13 @@ __device__ __forceinline__ void load_canon(const char* row, bool f32, bool ring,
             x[8 * i + 7] = val(w.w >> 16);
         }
     }
+}
+// the canonical type chosen once per call (a uniform branch), not per value
+template <int NV>
+__device__ __forceinline__ void load_canon(const char* row, bool f32, bool ring, bool f16, int e0, float (&x)[NV])
+{
+    if (f16) load_canon_t<NV, true>(row, f32, ring, e0, x);
+    else load_canon_t<NV, false>(row, f32, ring, e0, x);
 }
 
 // clamp(rint(t) + off, 0, top) in binary32, rint = round half to even.
