@@ -15,11 +15,13 @@ _LIB = None
 
 # Format numbering (an interface value shared with the library header, same integers).
 BF16, Q2_0, Q2_1, Q3_0, Q3_1, Q4_0, Q4_1, Q5_0, Q5_1, Q6_0, Q6_1, Q8_0, Q8_1, \
-    KVARN2, KVARN3, KVARN4, KVARN5, KVARN6, KVARN8 = range(19)
+    KVARN2, KVARN3, KVARN4, KVARN5, KVARN6, KVARN8, \
+    KVARN2_1, KVARN3_1, KVARN4_1, KVARN5_1, KVARN6_1, KVARN8_1 = range(25)
 FORMAT_NAMES = ["bf16", "q2_0", "q2_1", "q3_0", "q3_1", "q4_0", "q4_1", "q5_0", "q5_1",
                 "q6_0", "q6_1", "q8_0", "q8_1", "kvarn2", "kvarn3", "kvarn4", "kvarn5",
-                "kvarn6", "kvarn8"]
-KIND_BF16, KIND_Q0, KIND_Q1, KIND_KVARN = range(4)
+                "kvarn6", "kvarn8", "kvarn2_1", "kvarn3_1", "kvarn4_1", "kvarn5_1", "kvarn6_1",
+                "kvarn8_1"]
+KIND_BF16, KIND_Q0, KIND_Q1, KIND_KVARN, KIND_KVARN1 = range(5)
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -59,6 +61,8 @@ def lib():
         L.kvo_sinkhorn128.restype = None
         L.kvo_encode_page_kvarn.argtypes = [ctypes.c_int, _u16p, _u8p, _u16p, _u16p]
         L.kvo_encode_page_kvarn.restype = None
+        L.kvo_encode_page_kvarn_q1.argtypes = [ctypes.c_int, _u16p, _u8p, _u16p, _u16p]
+        L.kvo_encode_page_kvarn_q1.restype = None
         L.kvo_encode_token.argtypes = [ctypes.c_int, _u16p, _u8p, _u16p]
         L.kvo_encode_token.restype = ctypes.c_int
         L.kvo_encode_stream.argtypes = [ctypes.c_int, ctypes.c_int64, _u16p, _u8p, _u16p, _u16p]
@@ -237,14 +241,15 @@ def sinkhorn128(A, iters: int = 8):
     return r2, c2
 
 
-def encode_page_kvarn(N: int, X_bf16):
+def encode_page_kvarn(N: int, X_bf16, affine: bool = False):
+    """One KVarN page; affine: the qN_1 inner quantizer (scales [128][4][2] {d, m})."""
     X = np.ascontiguousarray(X_bf16, dtype=np.uint16)
     assert X.shape == (128, 128)
     codes = np.zeros((128, 16 * N), np.uint8)
-    scales = np.zeros((128, 4), np.uint16)
+    scales = np.zeros((128, 8) if affine else (128, 4), np.uint16)
     cscale = np.zeros(128, np.uint16)
-    lib().kvo_encode_page_kvarn(N, _p(X, _u16p), _p(codes, _u8p), _p(scales, _u16p),
-                                _p(cscale, _u16p))
+    f = lib().kvo_encode_page_kvarn_q1 if affine else lib().kvo_encode_page_kvarn
+    f(N, _p(X, _u16p), _p(codes, _u8p), _p(scales, _u16p), _p(cscale, _u16p))
     return codes, scales, cscale
 
 
@@ -270,7 +275,7 @@ def encode_stream(fmt: int, n_q: int, x_bf16):
                                  _p(cscale, _u16p))
     if rc != 0:
         raise ValueError("encode_stream rc=%d" % rc)
-    return codes, scales[:, : sb // 2], cscale[: n_q // 128] if kind == KIND_KVARN else None
+    return codes, scales[:, : sb // 2], cscale[: n_q // 128] if kind in (KIND_KVARN, KIND_KVARN1) else None
 
 
 def dequant_token(fmt: int, codes, scales=None, cscale_row=None) -> np.ndarray:

@@ -161,13 +161,19 @@ int kvo_format_info(int fmt, int* bits, int* kind, int* code_bytes, int* scale_b
     case KVO_KVARN5: N = 5; K = KVO_KIND_KVARN; break;
     case KVO_KVARN6: N = 6; K = KVO_KIND_KVARN; break;
     case KVO_KVARN8: N = 8; K = KVO_KIND_KVARN; break;
+    case KVO_KVARN2_1: N = 2; K = KVO_KIND_KVARN1; break;
+    case KVO_KVARN3_1: N = 3; K = KVO_KIND_KVARN1; break;
+    case KVO_KVARN4_1: N = 4; K = KVO_KIND_KVARN1; break;
+    case KVO_KVARN5_1: N = 5; K = KVO_KIND_KVARN1; break;
+    case KVO_KVARN6_1: N = 6; K = KVO_KIND_KVARN1; break;
+    case KVO_KVARN8_1: N = 8; K = KVO_KIND_KVARN1; break;
     default: return -1;
     }
     if (bits) *bits = N;
     if (kind) *kind = K;
     if (code_bytes) *code_bytes = (K == KVO_KIND_BF16) ? 256 : 16 * N;
-    if (scale_bytes) *scale_bytes = (K == KVO_KIND_BF16) ? 0 : (K == KVO_KIND_Q1 ? 16 : 8);
-    if (page_bytes) *page_bytes = (K == KVO_KIND_KVARN) ? 256 : 0;
+    if (scale_bytes) *scale_bytes = (K == KVO_KIND_BF16) ? 0 : ((K == KVO_KIND_Q1 || K == KVO_KIND_KVARN1) ? 16 : 8);
+    if (page_bytes) *page_bytes = (K == KVO_KIND_KVARN || K == KVO_KIND_KVARN1) ? 256 : 0;
     return 0;
 }
 
@@ -323,8 +329,23 @@ void kvo_sinkhorn128(const float* A, int iters, float r2[128], float c2[128])
 
 #define KVARN_ITERS 8
 
+static void encode_page_kvarn_impl(int N, int affine, const uint16_t* X, uint8_t* codes,
+                                   uint16_t* scales, uint16_t* cscale);
+
 void kvo_encode_page_kvarn(int N, const uint16_t* X, uint8_t* codes, uint16_t* scales,
                            uint16_t* cscale)
+{
+    encode_page_kvarn_impl(N, 0, X, codes, scales, cscale);
+}
+
+void kvo_encode_page_kvarn_q1(int N, const uint16_t* X, uint8_t* codes, uint16_t* scales,
+                              uint16_t* cscale)
+{
+    encode_page_kvarn_impl(N, 1, X, codes, scales, cscale);
+}
+
+static void encode_page_kvarn_impl(int N, int affine, const uint16_t* X, uint8_t* codes,
+                                   uint16_t* scales, uint16_t* cscale)
 {
     float* Y = (float*)malloc(sizeof(float) * 128 * 128);
     float* A = (float*)malloc(sizeof(float) * 128 * 128);
@@ -346,14 +367,19 @@ void kvo_encode_page_kvarn(int N, const uint16_t* X, uint8_t* codes, uint16_t* s
         cscale[j] = c;
         ic16[j] = 1.0f / f32_from_fp16(c);
     }
-    /* 5./6. normalize each channel, then symmetric block quantization and packing */
+    /* 5./6. normalize each channel, then block quantization (symmetric, or affine for
+     * an _1 base) and packing */
     const int cb = 16 * N;
     for (int t = 0; t < 128; ++t) {
         float w[128];
         uint8_t u[128];
         for (int j = 0; j < 128; ++j) w[j] = Y[t * 128 + j] * ic16[j];
-        for (int b = 0; b < 4; ++b)
-            kvo_encode_block_q0(N, w + 32 * b, &scales[t * 4 + b], u + 32 * b);
+        for (int b = 0; b < 4; ++b) {
+            if (affine)
+                kvo_encode_block_q1(N, w + 32 * b, &scales[t * 8 + 2 * b], &scales[t * 8 + 2 * b + 1], u + 32 * b);
+            else
+                kvo_encode_block_q0(N, w + 32 * b, &scales[t * 4 + b], u + 32 * b);
+        }
         kvo_pack_codes(N, u, codes + (size_t)t * cb);
     }
     free(Y);
@@ -372,7 +398,7 @@ int kvo_encode_token(int fmt, const uint16_t* x, uint8_t* codes, uint16_t* scale
         memcpy(codes, x, 256);                  /* identity: the bf16 row itself */
         return 0;
     }
-    if (kind == KVO_KIND_KVARN) return -1;      /* pages only */
+    if (kind == KVO_KIND_KVARN || kind == KVO_KIND_KVARN1) return -1;      /* pages only */
     float xf[128];
     uint8_t u[128];
     for (int i = 0; i < 128; ++i) xf[i] = f32_from_canon(x[i]);
@@ -392,11 +418,11 @@ int kvo_encode_stream(int fmt, int64_t n_q, const uint16_t* x, uint8_t* codes,
 {
     int N, kind, cb, sb, pb;
     if (kvo_format_info(fmt, &N, &kind, &cb, &sb, &pb) != 0 || n_q < 0) return -1;
-    if (kind == KVO_KIND_KVARN) {
+    if (kind == KVO_KIND_KVARN || kind == KVO_KIND_KVARN1) {
         if (n_q % KVO_PAGE) return -1;
         for (int64_t p = 0; p < n_q / KVO_PAGE; ++p) {
-            kvo_encode_page_kvarn(N, x + p * 128 * 128, codes + p * 128 * cb,
-                                  scales + p * 128 * 4, cscale + p * 128);
+            encode_page_kvarn_impl(N, kind == KVO_KIND_KVARN1, x + p * 128 * 128, codes + p * 128 * cb,
+                                   scales + p * 128 * (sb / 2), cscale + p * 128);
         }
         return 0;
     }
@@ -440,11 +466,15 @@ int kvo_dequant_token(int fmt, const uint8_t* codes, const uint16_t* scales,
         }
         return 0;
     }
-    /* kvarn: Yhat in the rotated, channel-normalized domain, then x = H Yhat / 128 */
+    /* kvarn: Yhat = c * (the block-quantized value) in the rotated domain, then
+     * x = H Yhat / 128 */
     double yh[128];
-    for (int j = 0; j < 128; ++j)
-        yh[j] = kvo_f64_from_fp16(cscale_row[j]) * kvo_f64_from_fp16(scales[j / 32]) *
-                (double)(u[j] - off);
+    for (int j = 0; j < 128; ++j) {
+        const double w = kind == KVO_KIND_KVARN1
+            ? kvo_f64_from_fp16(scales[2 * (j / 32) + 1]) + (double)u[j] * kvo_f64_from_fp16(scales[2 * (j / 32)])
+            : kvo_f64_from_fp16(scales[j / 32]) * (double)(u[j] - off);
+        yh[j] = kvo_f64_from_fp16(cscale_row[j]) * w;
+    }
     for (int i = 0; i < 128; ++i) {
         double s = 0.0;
         for (int j = 0; j < 128; ++j) {
@@ -462,7 +492,7 @@ int kvo_dequant_stream(int fmt, int64_t n_q, const uint8_t* codes, const uint16_
     int N, kind, cb, sb, pb;
     if (kvo_format_info(fmt, &N, &kind, &cb, &sb, &pb) != 0 || n_q < 0) return -1;
     for (int64_t t = 0; t < n_q; ++t) {
-        const uint16_t* crow = (kind == KVO_KIND_KVARN) ? cscale + (t / KVO_PAGE) * 128 : NULL;
+        const uint16_t* crow = (kind == KVO_KIND_KVARN || kind == KVO_KIND_KVARN1) ? cscale + (t / KVO_PAGE) * 128 : NULL;
         kvo_dequant_token(fmt, codes + t * cb, scales ? scales + t * (sb / 2) : NULL, crow,
                           out + t * 128);
     }
@@ -478,7 +508,8 @@ int64_t kvo_granule(int fmt_k, int fmt_v)
     int kk = -1, kv = -1;
     kvo_format_info(fmt_k, NULL, &kk, NULL, NULL, NULL);
     kvo_format_info(fmt_v, NULL, &kv, NULL, NULL, NULL);
-    return (kk == KVO_KIND_KVARN || kv == KVO_KIND_KVARN) ? KVO_PAGE : 1;
+    return (kk == KVO_KIND_KVARN || kv == KVO_KIND_KVARN || kk == KVO_KIND_KVARN1 || kv == KVO_KIND_KVARN1)
+               ? KVO_PAGE : 1;
 }
 
 int64_t kvo_ring_capacity(int64_t T, int64_t G)

@@ -52,9 +52,11 @@ enum {
     KVO_Q2_0, KVO_Q2_1, KVO_Q3_0, KVO_Q3_1, KVO_Q4_0, KVO_Q4_1, KVO_Q5_0, KVO_Q5_1,
     KVO_Q6_0, KVO_Q6_1, KVO_Q8_0, KVO_Q8_1,
     KVO_KVARN2, KVO_KVARN3, KVO_KVARN4, KVO_KVARN5, KVO_KVARN6, KVO_KVARN8,
+    /* var-norm over the affine bases: KVarN with qN_1 as the inner quantizer */
+    KVO_KVARN2_1, KVO_KVARN3_1, KVO_KVARN4_1, KVO_KVARN5_1, KVO_KVARN6_1, KVO_KVARN8_1,
     KVO_NUM_FORMATS
 };
-enum { KVO_KIND_BF16 = 0, KVO_KIND_Q0 = 1, KVO_KIND_Q1 = 2, KVO_KIND_KVARN = 3 };
+enum { KVO_KIND_BF16 = 0, KVO_KIND_Q0 = 1, KVO_KIND_Q1 = 2, KVO_KIND_KVARN = 3, KVO_KIND_KVARN1 = 4 };
 
 #define KVO_D 128        /* head_dim; the only supported value */
 #define KVO_BLOCK 32     /* block of consecutive dims sharing one scale (READING) */
@@ -106,6 +108,12 @@ void kvo_fwht128_f32(float y[128]);
 void kvo_sinkhorn128(const float* A, int iters, float r2[128], float c2[128]);
 /* Encode one 128-token page of one stream with kvarnN.  X: [128][128] bf16 bits,
  * token-major.  Outputs codes [128][16N], scales [128][4] fp16 d, cscale[128] fp16. */
+/* The same page encoding with qN_1 (affine: fp16 step and minimum per block, scales
+ * [128][4][2] {d, m}) as the inner quantizer: var-norm over an _1 base ("Экспериментальные
+ * методы квантизации KV-кэша в BeeLLama.cpp v0.4.0": var-norm as a switch over a cache
+ * type, e.g. q2_1 with --cache-var-norm). */
+void kvo_encode_page_kvarn_q1(int N, const uint16_t* X, uint8_t* codes, uint16_t* scales,
+                              uint16_t* cscale);
 void kvo_encode_page_kvarn(int N, const uint16_t* X, uint8_t* codes, uint16_t* scales,
                            uint16_t* cscale);
 
