@@ -63,6 +63,7 @@ typedef enum {
     KV_Q2_0, KV_Q2_1, KV_Q3_0, KV_Q3_1, KV_Q4_0, KV_Q4_1, KV_Q5_0, KV_Q5_1,
     KV_Q6_0, KV_Q6_1, KV_Q8_0, KV_Q8_1,
     KV_KVARN2, KV_KVARN3, KV_KVARN4, KV_KVARN5, KV_KVARN6, KV_KVARN8,
+    KV_KVARN2_1, KV_KVARN3_1, KV_KVARN4_1, KV_KVARN5_1, KV_KVARN6_1, KV_KVARN8_1,
     KV_NUM_FORMATS
 } kv_format;
 

@@ -6,8 +6,8 @@
 //    (max-min)/(2^N-1) and an fp16 min.  Codes are a little-endian N-bit stream per token.
 //  * k_kvarn_page<N>: KVarN for one 128-token page of one stream per workgroup: unnormalized
 //    Walsh-Hadamard rotation of every token vector, 8 Sinkhorn iterations balancing
-//    per-token and per-channel mean squares, fp16 channel scales, then qN_0 of the
-//    normalized values ("Практическое руководство: запуск Bonsai-Ternary-27B на 120k
+//    per-token and per-channel mean squares, fp16 channel scales, then qN_0 (kvarnN) or
+//    qN_1 (kvarnN_1, AFF) of the normalized values ("Практическое руководство: запуск Bonsai-Ternary-27B на 120k
 //    токенах с менее чем 10 ГБ VRAM", sections "Решение: KVarN ..." and "Как
 //    преобразование Уолша-Адамара и Sinkhorn спасают качество при 4-битном сжатии").
 //  * k_ring_write: canonical 16-bit rows of the newest tokens into the precision-tail ring.
@@ -353,7 +353,7 @@ __device__ __forceinline__ float swap_pair(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
-template <int N>
+template <int N, bool AFF>
 __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages, int streams_mask)
 {
     __shared__ float As[kPage * kLdsStride];   // squares A[t][j]
@@ -445,21 +445,21 @@ __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages,
         ((uint16_t*)(st + L.cscale + page * 256))[tid] = (uint16_t)c;
     }
     __syncthreads();
-    // ---- 5./6. normalize, symmetric block quantization, pack -----------------------------
+    // ---- 5./6. normalize, block quantization (symmetric or affine), pack ------------------
     char* codes = st + L.codes + p * (16 * N);
-    uint16_t* scl = (uint16_t*)(st + L.scales + p * 8);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
         float x[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) x[i] = y[32 * bb + i] * ic16_s[64 * half + 32 * bb + i];
         uint32_t u[32];
-        uint32_t d = encode_block_q0<N>(x, u);
+        const uint32_t d = AFF ? encode_block_q1<N>(x, u) : encode_block_q0<N>(x, u);
         uint32_t packed[N];
         pack32<N>(u, packed);
         const int blk = 2 * half + bb;
         store_words<N>(codes + 4 * N * blk, packed);
-        scl[blk] = (uint16_t)d;
+        if (AFF) ((uint32_t*)(st + L.scales + p * 16))[blk] = d;   // step | minimum << 16
+        else ((uint16_t*)(st + L.scales + p * 8))[blk] = (uint16_t)d;
     }
 }
 
@@ -508,11 +508,11 @@ int launch_enc_fmt(int fmt, const AppendArgs& a, int64_t tokens, int sv_sel, hip
     }
 }
 
-template <int N>
+template <int N, bool AFF>
 int launch_kv(const AppendArgs& a, int64_t pages, int mask, hipStream_t st)
 {
     int64_t blocks = pages * 2 * a.g.n_kv_heads * (int64_t)a.layers_in;
-    hipLaunchKernelGGL(k_kvarn_page<N>, dim3((unsigned)blocks), dim3(256), 0, st, a, pages, mask);
+    hipLaunchKernelGGL((k_kvarn_page<N, AFF>), dim3((unsigned)blocks), dim3(256), 0, st, a, pages, mask);
     return (int)hipGetLastError();
 }
 
@@ -524,7 +524,7 @@ int launch_append_encode(const AppendArgs& a, void* stream)
     if (tokens <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
     // token-wise formats only; a KVarN stream is encoded page-wise (launch_append_kvarn)
-    const bool kq = fkind(a.g.fmt_k) != KIND_KVARN, vq = fkind(a.g.fmt_v) != KIND_KVARN;
+    const bool kq = !kind_paged(fkind(a.g.fmt_k)), vq = !kind_paged(fkind(a.g.fmt_v));
     if (kq && vq && a.g.fmt_k == a.g.fmt_v) return launch_enc_fmt(a.g.fmt_k, a, tokens, 2, st);
     int rc = 0;
     if (kq) rc = launch_enc_fmt(a.g.fmt_k, a, tokens, 0, st);
@@ -537,19 +537,20 @@ int launch_append_kvarn(const AppendArgs& a, void* stream)
     int64_t pages = total_of(a, 2);
     if (pages <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
-    // one launch per code width: mask bit 0 = K stream, bit 1 = V stream
+    // one launch per format: mask bit 0 = K stream, bit 1 = V stream
     auto launch_n = [&](int fmt, int mask) -> int {
+        const bool aff = fkind(fmt) == KIND_KVARN1;
         switch (fbits(fmt)) {
-        case 2: return launch_kv<2>(a, pages, mask, st);
-        case 3: return launch_kv<3>(a, pages, mask, st);
-        case 4: return launch_kv<4>(a, pages, mask, st);
-        case 5: return launch_kv<5>(a, pages, mask, st);
-        case 6: return launch_kv<6>(a, pages, mask, st);
-        case 8: return launch_kv<8>(a, pages, mask, st);
+        case 2: return aff ? launch_kv<2, true>(a, pages, mask, st) : launch_kv<2, false>(a, pages, mask, st);
+        case 3: return aff ? launch_kv<3, true>(a, pages, mask, st) : launch_kv<3, false>(a, pages, mask, st);
+        case 4: return aff ? launch_kv<4, true>(a, pages, mask, st) : launch_kv<4, false>(a, pages, mask, st);
+        case 5: return aff ? launch_kv<5, true>(a, pages, mask, st) : launch_kv<5, false>(a, pages, mask, st);
+        case 6: return aff ? launch_kv<6, true>(a, pages, mask, st) : launch_kv<6, false>(a, pages, mask, st);
+        case 8: return aff ? launch_kv<8, true>(a, pages, mask, st) : launch_kv<8, false>(a, pages, mask, st);
         default: return (int)hipErrorInvalidValue;
         }
     };
-    const bool kk = fkind(a.g.fmt_k) == KIND_KVARN, vk = fkind(a.g.fmt_v) == KIND_KVARN;
+    const bool kk = kind_paged(fkind(a.g.fmt_k)), vk = kind_paged(fkind(a.g.fmt_v));
     if (kk && vk && a.g.fmt_k == a.g.fmt_v) return launch_n(a.g.fmt_k, 3);
     int rc = 0;
     if (kk) rc = launch_n(a.g.fmt_k, 1);

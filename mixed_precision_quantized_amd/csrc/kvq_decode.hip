@@ -98,18 +98,22 @@ __device__ __forceinline__ void dequant16(const char* st, const StreamLayout& L,
         uint32_t w[(N + 1) / 2];
         load_codes16<N>(st + L.codes + t * (16 * N), part, w);
         const int b = part >> 1;
-        if constexpr (KIND == KIND_Q1) {
+        if constexpr (kind_affine(KIND)) {
             uint32_t dm = *(const uint32_t*)(st + L.scales + t * 16 + 4 * b);
             float d = fp16_to_f32(dm & 0xFFFFu), m = fp16_to_f32(dm >> 16);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) x[j] = m + d * (float)code_at<N>(w, j);
+            for (int j = 0; j < 16; ++j) {
+                float c = m + d * (float)code_at<N>(w, j);
+                if constexpr (KIND == KIND_KVARN1) c *= crow[j];
+                x[j] = c;
+            }
         } else {
             float d = fp16_to_f32(*(const uint16_t*)(st + L.scales + t * 8 + 2 * b));
             const float off = (float)(1 << (N - 1));
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 float c = ((float)code_at<N>(w, j) - off) * d;
-                if constexpr (KIND == KIND_KVARN) c *= crow[j];
+                if constexpr (kind_paged(KIND)) c *= crow[j];
                 x[j] = c;
             }
         }
@@ -152,7 +156,13 @@ __device__ __forceinline__ void dequant16_rt(int fmt, const char* st, const Stre
     case 15: dequant16<15>(st, L, t, part, crow, x); break;
     case 16: dequant16<16>(st, L, t, part, crow, x); break;
     case 17: dequant16<17>(st, L, t, part, crow, x); break;
-    default: dequant16<18>(st, L, t, part, crow, x); break;
+    case 18: dequant16<18>(st, L, t, part, crow, x); break;
+    case 19: dequant16<19>(st, L, t, part, crow, x); break;
+    case 20: dequant16<20>(st, L, t, part, crow, x); break;
+    case 21: dequant16<21>(st, L, t, part, crow, x); break;
+    case 22: dequant16<22>(st, L, t, part, crow, x); break;
+    case 23: dequant16<23>(st, L, t, part, crow, x); break;
+    default: dequant16<24>(st, L, t, part, crow, x); break;
     }
 }
 
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
 {
     constexpr int KIND = fkind(FK);
     const int fv = FV >= 0 ? FV : a.g.fmt_v;
-    const bool v_kvarn = fkind(fv) == KIND_KVARN;
+    const bool v_kvarn = kind_paged(fkind(fv));
     __shared__ float qs[kG][kD];
     __shared__ float wm[4][kG], wl[4][kG];
     __shared__ float wacc[4][kG][kD];
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
         qs[hh][d] = qv * a.scale_log2;
     }
     __syncthreads();
-    if (KIND == KIND_KVARN && quant) {
+    if (kind_paged(KIND) && quant) {
         lds_fwht(qs);
         for (int i = tid; i < kG * kD; i += blockDim.x) qs[i / kD][i % kD] *= (1.0f / 128.0f);
         __syncthreads();
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
             const int64_t t0 = (int64_t)u * kPage;
             const int64_t t1 = min<int64_t>(t0 + kPage, sq.n_q);
             float ck[16], cv[16];
-            if constexpr (KIND == KIND_KVARN) {
+            if constexpr (kind_paged(KIND)) {
                 const uint16_t* cks = (const uint16_t*)(kst + g.k.cscale + (int64_t)u * 256) + 16 * part;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) ck[j] = fp16_to_f32(cks[j]);
@@ -404,6 +414,12 @@ int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)
     case 16: return launch_fmt<16>(a, n_wgs, st);
     case 17: return launch_fmt<17>(a, n_wgs, st);
     case 18: return launch_fmt<18>(a, n_wgs, st);
+    case 19: return launch_fmt<19>(a, n_wgs, st);
+    case 20: return launch_fmt<20>(a, n_wgs, st);
+    case 21: return launch_fmt<21>(a, n_wgs, st);
+    case 22: return launch_fmt<22>(a, n_wgs, st);
+    case 23: return launch_fmt<23>(a, n_wgs, st);
+    case 24: return launch_fmt<24>(a, n_wgs, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
@@ -412,8 +428,8 @@ int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
 {
     (void)group;
     if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k, fmt_v);
-    static int cache[19][2] = {{0}};
-    if (fmt_k < 0 || fmt_k >= 19 || fmt_v < 0 || fmt_v >= 19) return 0;
+    static int cache[kNumFormats][2] = {{0}};
+    if (fmt_k < 0 || fmt_k >= kNumFormats || fmt_v < 0 || fmt_v >= kNumFormats) return 0;
     const int mx = fmt_v != fmt_k ? 1 : 0;
     if (cache[fmt_k][mx]) return cache[fmt_k][mx];
     int n = 0;
@@ -437,6 +453,12 @@ int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
     case 16: n = occ_fmt<16>(mx); break;
     case 17: n = occ_fmt<17>(mx); break;
     case 18: n = occ_fmt<18>(mx); break;
+    case 19: n = occ_fmt<19>(mx); break;
+    case 20: n = occ_fmt<20>(mx); break;
+    case 21: n = occ_fmt<21>(mx); break;
+    case 22: n = occ_fmt<22>(mx); break;
+    case 23: n = occ_fmt<23>(mx); break;
+    case 24: n = occ_fmt<24>(mx); break;
     default: break;
     }
     cache[fmt_k][mx] = n;
@@ -518,7 +540,7 @@ __global__ __launch_bounds__(256) void k_kld(KldArgs a)
         qrot[hh][d] = qv;
     }
     __syncthreads();
-    if (KIND == KIND_KVARN) {
+    if (kind_paged(KIND)) {
         lds_fwht(qrot);
         for (int i = tid; i < kG * kD; i += blockDim.x) qrot[i / kD][i % kD] *= (1.0f / 128.0f);
         __syncthreads();
@@ -547,7 +569,7 @@ __global__ __launch_bounds__(256) void k_kld(KldArgs a)
         const bool quant = tc < a.n_q;
         if (quant) {
             float ck[16];
-            if constexpr (KIND == KIND_KVARN) {
+            if constexpr (kind_paged(KIND)) {
                 const uint16_t* cks = (const uint16_t*)(kst + g.k.cscale + (tc / kPage) * 256) + 16 * part;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) ck[j] = fp16_to_f32(cks[j]);
@@ -572,7 +594,7 @@ __global__ __launch_bounds__(256) void k_kld(KldArgs a)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 se = fmaf(qo[h][j], kx[j], se);
-                sq = fmaf((KIND == KIND_KVARN && quant) ? qc[h][j] : qo[h][j], k[j], sq);
+                sq = fmaf((kind_paged(KIND) && quant) ? qc[h][j] : qo[h][j], k[j], sq);
             }
             se = sum8(se);
             sq = sum8(sq);
@@ -647,6 +669,12 @@ int launch_kld_pass(const KldArgs& a, void* stream)
     case 16: rc = launch_kld_fmt<16>(a, st); break;
     case 17: rc = launch_kld_fmt<17>(a, st); break;
     case 18: rc = launch_kld_fmt<18>(a, st); break;
+    case 19: rc = launch_kld_fmt<19>(a, st); break;
+    case 20: rc = launch_kld_fmt<20>(a, st); break;
+    case 21: rc = launch_kld_fmt<21>(a, st); break;
+    case 22: rc = launch_kld_fmt<22>(a, st); break;
+    case 23: rc = launch_kld_fmt<23>(a, st); break;
+    case 24: rc = launch_kld_fmt<24>(a, st); break;
     default: return (int)hipErrorInvalidValue;
     }
     if (rc) return rc;

@@ -12,10 +12,10 @@ int decode_fast_w8(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs,
 
 namespace {
 
-// formats of the fast kernel: every quantized format (qN_0, qN_1, kvarnN)
+// formats of the fast kernel: qN_0, qN_1 and kvarnN (kvarnN_1 and bf16 take the generic kernel)
 bool fast_format(int f)
 {
-    return f >= 1 && f <= 18 && fkind(f) != KIND_BF16;
+    return f >= 1 && f < kNumFormats && (fkind(f) == KIND_Q0 || fkind(f) == KIND_Q1 || fkind(f) == KIND_KVARN);
 }
 
 int by_width(int op, const DecodeArgs* a, int fmt_k, int fmt_v, int n_wgs, void* stream)
@@ -46,7 +46,7 @@ int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream)
 
 int decode_fast_wgs_per_cu(int fmt_k, int fmt_v)
 {
-    static int cache[19][19] = {{0}};
+    static int cache[kNumFormats][kNumFormats] = {{0}};
     if (!decode_fast_supported(fmt_k, fmt_v)) return 0;
     if (!cache[fmt_k][fmt_v]) cache[fmt_k][fmt_v] = by_width(1, nullptr, fmt_k, fmt_v, 0, nullptr);
     return cache[fmt_k][fmt_v];

@@ -20,16 +20,18 @@ __host__ __device__ constexpr int fbits(int f)
 {
     return f == 0 ? 16 : f == 1 ? 2 : f == 2 ? 2 : f == 3 ? 3 : f == 4 ? 3 : f == 5 ? 4 : f == 6 ? 4
          : f == 7 ? 5 : f == 8 ? 5 : f == 9 ? 6 : f == 10 ? 6 : f == 11 ? 8 : f == 12 ? 8
-         : f == 13 ? 2 : f == 14 ? 3 : f == 15 ? 4 : f == 16 ? 5 : f == 17 ? 6 : f == 18 ? 8 : 0;
+         : f == 13 ? 2 : f == 14 ? 3 : f == 15 ? 4 : f == 16 ? 5 : f == 17 ? 6 : f == 18 ? 8
+         : f == 19 ? 2 : f == 20 ? 3 : f == 21 ? 4 : f == 22 ? 5 : f == 23 ? 6 : f == 24 ? 8 : 0;
 }
 __host__ __device__ constexpr int fkind(int f)
 {
-    return f == 0 ? KIND_BF16 : f >= 13 ? KIND_KVARN : ((f - 1) % 2 == 0 ? KIND_Q0 : KIND_Q1);
+    return f == 0 ? KIND_BF16 : f >= 19 ? KIND_KVARN1 : f >= 13 ? KIND_KVARN
+         : ((f - 1) % 2 == 0 ? KIND_Q0 : KIND_Q1);
 }
 __host__ __device__ constexpr int fcode_bytes(int f) { return f == 0 ? 256 : 16 * fbits(f); }
 __host__ __device__ constexpr int fscale_halves(int f)
 {
-    return fkind(f) == KIND_BF16 ? 0 : (fkind(f) == KIND_Q1 ? 8 : 4);
+    return fkind(f) == KIND_BF16 ? 0 : (kind_affine(fkind(f)) ? 8 : 4);
 }
 
 // ------------------------------------------------------------------ conversions

@@ -33,20 +33,24 @@ struct kv_cache {
     std::vector<int64_t> nq;
 };
 
+static_assert(KV_NUM_FORMATS == kNumFormats, "format count of the C ABI and the kernels");
+
 namespace {
 
 bool format_desc(int32_t fmt, FormatDesc* d)
 {
-    static const int8_t bits[KV_NUM_FORMATS] = {16, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6, 8, 8, 2, 3, 4, 5, 6, 8};
+    static const int8_t bits[KV_NUM_FORMATS] = {16, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6, 8, 8,
+                                                      2, 3, 4, 5, 6, 8, 2, 3, 4, 5, 6, 8};
     if (fmt < 0 || fmt >= KV_NUM_FORMATS) return false;
     FormatDesc r;
     r.bits = bits[fmt];
     if (fmt == KV_BF16) r.kind = KIND_BF16;
+    else if (fmt >= KV_KVARN2_1) r.kind = KIND_KVARN1;
     else if (fmt >= KV_KVARN2) r.kind = KIND_KVARN;
     else r.kind = ((fmt - KV_Q2_0) % 2 == 0) ? KIND_Q0 : KIND_Q1;
     r.code_bytes = (r.kind == KIND_BF16) ? 256 : 16 * r.bits;
-    r.scale_bytes = (r.kind == KIND_BF16) ? 0 : (r.kind == KIND_Q1 ? 16 : 8);
-    r.page_bytes = (r.kind == KIND_KVARN) ? 256 : 0;
+    r.scale_bytes = (r.kind == KIND_BF16) ? 0 : (kind_affine(r.kind) ? 16 : 8);
+    r.page_bytes = kind_paged(r.kind) ? 256 : 0;
     *d = r;
     return true;
 }
@@ -61,7 +65,7 @@ StreamLayout stream_layout(const FormatDesc& f, int64_t tokens_pad, int64_t ring
     off = align256(off + tokens_pad * f.code_bytes);
     s.scales = off;
     off = align256(off + tokens_pad * f.scale_bytes);
-    if (f.kind == KIND_KVARN) {
+    if (kind_paged(f.kind)) {
         s.cscale = off;
         off = align256(off + (tokens_pad / kPage) * 256);
     } else {
@@ -78,7 +82,7 @@ int64_t granule_of(int32_t fk, int32_t fv)
     FormatDesc a, b;
     format_desc(fk, &a);
     format_desc(fv, &b);
-    return (a.kind == KIND_KVARN || b.kind == KIND_KVARN) ? kPage : 1;
+    return (kind_paged(a.kind) || kind_paged(b.kind)) ? kPage : 1;
 }
 
 int64_t ring_capacity(int64_t T, int64_t G) { return G * ((T + G - 1 + G - 1) / G); }
@@ -165,11 +169,11 @@ int launch_group(kv_cache* c, AppendArgs& a, void* stream)
     }
     int rc = 0;
     if (any_enc) {
-        if (fk.kind != KIND_KVARN || fv.kind != KIND_KVARN) {
+        if (!kind_paged(fk.kind) || !kind_paged(fv.kind)) {
             rc = launch_append_encode(a, stream);
             if (rc) return rc;
         }
-        if (fk.kind == KIND_KVARN || fv.kind == KIND_KVARN) {
+        if (kind_paged(fk.kind) || kind_paged(fv.kind)) {
             rc = launch_append_kvarn(a, stream);
             if (rc) return rc;
         }

@@ -13,15 +13,24 @@ constexpr int kPage = 128;       // tokens per KVarN page (channel-scale row)
 constexpr int kTailUnit = 32;    // tokens of the BF16 ring per decode work unit
 constexpr int kMaxSeqsPerLaunch = 32;
 constexpr int kMaxGroup = 8;     // query heads per KV head
+constexpr int kNumFormats = 25;  // format ids 0..24 (the C ABI's kv_format)
 
-enum Kind : int32_t { KIND_BF16 = 0, KIND_Q0 = 1, KIND_Q1 = 2, KIND_KVARN = 3 };
+// KIND_KVARN: rotated, Sinkhorn-normalized pages over a symmetric block quantizer;
+// KIND_KVARN1: the same over an affine (step and minimum) block quantizer.
+enum Kind : int32_t { KIND_BF16 = 0, KIND_Q0 = 1, KIND_Q1 = 2, KIND_KVARN = 3, KIND_KVARN1 = 4 };
+
+// Page formats: values stored rotated with a per-page channel-scale row.  (constexpr
+// functions are callable from device code as well.)
+constexpr bool kind_paged(int k) { return k == KIND_KVARN || k == KIND_KVARN1; }
+// Formats whose blocks carry a step and a minimum (16 scale bytes per token).
+constexpr bool kind_affine(int k) { return k == KIND_Q1 || k == KIND_KVARN1; }
 
 struct FormatDesc {
     int32_t bits;         // N (16 for bf16)
     int32_t kind;         // Kind
     int32_t code_bytes;   // per token: 16N, or 256 for bf16
-    int32_t scale_bytes;  // per token: 8 (qN_0, kvarn), 16 (qN_1), 0 (bf16)
-    int32_t page_bytes;   // per 128-token page: 256 (kvarn), else 0
+    int32_t scale_bytes;  // per token: 8 (qN_0, kvarnN), 16 (qN_1, kvarnN_1), 0 (bf16)
+    int32_t page_bytes;   // per 128-token page: 256 (kvarnN, kvarnN_1), else 0
 };
 
 // Byte layout of one stream (the K or V history of one (seq, layer, kv_head)).

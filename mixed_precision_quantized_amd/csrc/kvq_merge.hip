@@ -10,7 +10,7 @@
 // release fence in every workgroup, and each such fence writes back the whole L2 of its
 // XCD while the other workgroups are still streaming the cache.
 //
-// KVarN: the quantized splits accumulate rotated values (Yhat, with x = H Yhat / 128 and H
+// KVarN (both inner quantizers): the quantized splits accumulate rotated values (Yhat, with x = H Yhat / 128 and H
 // the unnormalized Sylvester Hadamard matrix), the BF16 ring splits original values; the
 // quantized sum is rotated back here once, before the two are added.
 #include "kvq_device.h"
@@ -132,7 +132,7 @@ int launch_merge(const DecodeArgs& a, void* stream)
 {
     hipStream_t st = (hipStream_t)stream;
     const int n = a.n_seqs * a.g.n_kv_heads * kG;
-    if (fkind(a.g.fmt_v) == KIND_KVARN)      // values accumulated in the rotated domain
+    if (kind_paged(fkind(a.g.fmt_v)))        // values accumulated in the rotated domain
         hipLaunchKernelGGL(k_merge<true>, dim3(n), dim3(kThreads), 0, st, a);
     else
         hipLaunchKernelGGL(k_merge<false>, dim3(n), dim3(kThreads), 0, st, a);

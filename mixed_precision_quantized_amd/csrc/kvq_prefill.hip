@@ -25,7 +25,7 @@
 // 64k block-format workload.  Values are dequantized to binary16 (|v| is small) and the
 // probabilities are rounded to binary16 before the P V product.
 //
-// KVarN, as in decode: keys are scored in the rotated domain with q'' = (H q / 128) * c_K
+// KVarN (either inner quantizer), as in decode: keys are scored in the rotated domain with q'' = (H q / 128) * c_K
 // of the page; values accumulate in the rotated domain and are rotated back once in the
 // merge (quantized and ring blocks never share a split, so each split is in one domain).
 #include "kvq_device.h"
@@ -100,11 +100,11 @@ __device__ __forceinline__ PfStream pf_stream_rsrc(const PrefillArgs& a, const c
     const bool exact = fkind(fmt) == KIND_BF16;
     S.ring = !quant;
     S.rb = quant && !exact ? 16 * fbits(fmt) : 256;
-    S.sb = fkind(fmt) == KIND_Q1 ? 16 : 8;
+    S.sb = kind_affine(fkind(fmt)) ? 16 : 8;
     if (quant) {
         S.rows = pf_rsrc(st + Ls.codes, (int)(a.n_q * S.rb));
         S.scales = pf_rsrc(st + Ls.scales, exact ? 0 : (int)(a.n_q * S.sb));
-        S.chan = pf_rsrc(st + (Ls.cscale >= 0 ? Ls.cscale : 0), fkind(fmt) == KIND_KVARN ? (int)((a.n_q + kPage - 1) / kPage * 256) : 0);
+        S.chan = pf_rsrc(st + (Ls.cscale >= 0 ? Ls.cscale : 0), kind_paged(fkind(fmt)) ? (int)((a.n_q + kPage - 1) / kPage * 256) : 0);
     } else {
         S.rows = pf_rsrc(st + Ls.ring, a.g.ring_slots * 256);
         S.scales = S.chan = S.rows;
@@ -138,8 +138,8 @@ __device__ __forceinline__ void pf_dma(PfRawL& R, const PrefillArgs& a, const Pf
             }
         }
     };
-    stream(SK, KK != KIND_BF16, KK == KIND_KVARN, R.k, R.ks, R.kch, 0, 2);
-    stream(SV, KV != KIND_BF16, KV == KIND_KVARN, R.v, R.vs, R.vch, 1, 3);
+    stream(SK, KK != KIND_BF16, kind_paged(KK), R.k, R.ks, R.kch, 0, 2);
+    stream(SV, KV != KIND_BF16, kind_paged(KV), R.v, R.vs, R.vch, 1, 3);
 }
 
 // 16 N-bit codes of part `part` of a row held at lds row (dword aligned)
@@ -185,10 +185,10 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         const int N = fbits(g.fmt_k);
         uint32_t u[16];
         unpack16_rt(N, R.k + r * 16 * N, pp, u);
-        const float off = KK == KIND_Q1 ? 0.0f : (float)(1 << (N - 1));
+        const float off = kind_affine(KK) ? 0.0f : (float)(1 << (N - 1));
 #pragma unroll
         for (int e = 0; e < 16; ++e) kx[e] = (float)u[e] - off;
-        if (KK == KIND_Q1) {
+        if (kind_affine(KK)) {
             const uint32_t dm = *(const uint32_t*)(R.ks + r * 16 + 4 * b);
             d = fp16_to_f32(dm & 0xFFFFu);
             m = fp16_to_f32(dm >> 16);
@@ -209,7 +209,7 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         const int N = fbits(g.fmt_v);
         uint32_t u[16];
         unpack16_rt(N, R.v + r * 16 * N, pp, u);
-        if (KV == KIND_Q1) {
+        if (kind_affine(KV)) {
             const uint32_t dm = *(const uint32_t*)(R.vs + r * 16 + 4 * b);
             const float dv = fp16_to_f32(dm & 0xFFFFu), mv = fp16_to_f32(dm >> 16);
 #pragma unroll
@@ -219,10 +219,10 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
             const float off = (float)(1 << (N - 1));
 #pragma unroll
             for (int e = 0; e < 16; ++e) vx[e] = ((float)u[e] - off) * dv;
-            if (KV == KIND_KVARN) {
+        }
+        if (kind_paged(KV)) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) vx[e] *= fp16_to_f32(R.vch[16 * pp + e]);
-            }
+            for (int e = 0; e < 16; ++e) vx[e] *= fp16_to_f32(R.vch[16 * pp + e]);
         }
     } else {
         const uint4* q = (const uint4*)(R.v + r * 256 + 32 * pp);
@@ -256,7 +256,7 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         L.dk[b][r] = d;
         L.mk[b][r] = m;
     }
-    if (KK == KIND_KVARN && quant && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
+    if (kind_paged(KK) && quant && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
 }
 
 template <int KK, int KV>
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
     const bool qvalid = qi < a.n_new;
     const int64_t pos = a.n - a.n_new + (qvalid ? qi : a.n_new - 1);
     const int64_t pos_min = a.n - a.n_new + kPfQ * tile;             // the tile's first query
-    const bool kv_k = KK == KIND_KVARN && quant;
+    const bool kv_k = kind_paged(KK) && quant;
 
     // ---- query: the lane's 64 dims {16 idx + 8 hh + c}, log2 domain, as hi + lo binary16 ----
     h8 qb[8], ql[8];                 // the operand of the current page: query = qb + ql
@@ -370,7 +370,8 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
         }
     };
     if (KK == KIND_Q1) make_qsum();
-    // KVarN keys: q'' = (H q / 128) * c_K of the page, again as hi + lo
+    // KVarN keys: q'' = (H q / 128) * c_K of the page, again as hi + lo; over affine blocks
+    // the minimum term takes the block sums of this page's operand
     auto page_operand = [&](const PfLds& B) {
 #pragma unroll
         for (int idx = 0; idx < 8; ++idx)
@@ -381,6 +382,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
                 qb[idx][c] = hi;
                 ql[idx][c] = (_Float16)(v - (float)hi);
             }
+        if (KK == KIND_KVARN1) make_qsum();
     };
 
     float mrun = kNeg, lrun = 0.0f;
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
                     const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
                     for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(dv[c], T[4 * r4 + c], Sacc[4 * r4 + c]);
-                    if (KK == KIND_Q1) {
+                    if (kind_affine(KK)) {
                         const float4 mm = *(const float4*)&B.mk[b][8 * r4 + 4 * hh];
                         const float mv[4] = {mm.x, mm.y, mm.z, mm.w};
 #pragma unroll
@@ -573,7 +575,8 @@ int launch_pf_v(const PrefillArgs& a, hipStream_t st)
     case KIND_BF16: return launch_pf<KK, KIND_BF16>(a, st);
     case KIND_Q0: return launch_pf<KK, KIND_Q0>(a, st);
     case KIND_Q1: return launch_pf<KK, KIND_Q1>(a, st);
-    default: return launch_pf<KK, KIND_KVARN>(a, st);
+    case KIND_KVARN: return launch_pf<KK, KIND_KVARN>(a, st);
+    default: return launch_pf<KK, KIND_KVARN1>(a, st);
     }
 }
 
@@ -587,11 +590,12 @@ int launch_prefill(const PrefillArgs& a, void* stream)
     case KIND_BF16: rc = launch_pf_v<KIND_BF16>(a, st); break;
     case KIND_Q0: rc = launch_pf_v<KIND_Q0>(a, st); break;
     case KIND_Q1: rc = launch_pf_v<KIND_Q1>(a, st); break;
-    default: rc = launch_pf_v<KIND_KVARN>(a, st); break;
+    case KIND_KVARN: rc = launch_pf_v<KIND_KVARN>(a, st); break;
+    default: rc = launch_pf_v<KIND_KVARN1>(a, st); break;
     }
     if (rc) return rc;
     const int n = a.n_new * a.g.n_q_heads;
-    if (fkind(a.g.fmt_v) == KIND_KVARN)
+    if (kind_paged(fkind(a.g.fmt_v)))
         hipLaunchKernelGGL(k_prefill_merge<true>, dim3(n), dim3(128), 0, st, a);
     else
         hipLaunchKernelGGL(k_prefill_merge<false>, dim3(n), dim3(128), 0, st, a);

@@ -21,7 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 FORMATS = ["bf16", "q2_0", "q2_1", "q3_0", "q3_1", "q4_0", "q4_1", "q5_0", "q5_1", "q6_0",
-           "q6_1", "q8_0", "q8_1", "kvarn2", "kvarn3", "kvarn4", "kvarn5", "kvarn6", "kvarn8"]
+           "q6_1", "q8_0", "q8_1", "kvarn2", "kvarn3", "kvarn4", "kvarn5", "kvarn6", "kvarn8",
+           "kvarn2_1", "kvarn3_1", "kvarn4_1", "kvarn5_1", "kvarn6_1", "kvarn8_1"]
 FORMAT_ID = {n: i for i, n in enumerate(FORMATS)}
 
 KV_OK, KV_EINVAL, KV_ENOSPC, KV_EUNSUPPORTED, KV_EEMPTY, KV_EDEVICE, KV_ESIZE = 0, -1, -2, -3, -4, -5, -6

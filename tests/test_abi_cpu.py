@@ -64,7 +64,8 @@ def test_format_table_matches_sizes():
     sizes = {"q2_0": 40, "q2_1": 48, "q3_0": 56, "q3_1": 64, "q4_0": 72, "q4_1": 80,
              "q5_0": 88, "q5_1": 96, "q6_0": 104, "q6_1": 112, "q8_0": 136, "q8_1": 144,
              "kvarn2": 42, "kvarn3": 58, "kvarn4": 74, "kvarn5": 90, "kvarn6": 106,
-             "kvarn8": 138, "bf16": 256}
+             "kvarn8": 138, "kvarn2_1": 50, "kvarn3_1": 66, "kvarn4_1": 82, "kvarn5_1": 98,
+             "kvarn6_1": 114, "kvarn8_1": 146, "bf16": 256}
     for name, b in sizes.items():
         bits, cb, sb, pb = kvq.format_info(name)
         assert cb + sb + pb // 128 == b

@@ -21,7 +21,7 @@ TOL = 2e-3
 
 
 @pytest.mark.parametrize("wl", ["c1_q4_0_ctx4096", "c3_kvarn_ctx65536"])
-@pytest.mark.parametrize("fmt", ["q4_0", "q3_1", "kvarn4", "q8_0/q4_1", "kvarn2/q6_0"])
+@pytest.mark.parametrize("fmt", ["q4_0", "q3_1", "kvarn4", "q8_0/q4_1", "kvarn2/q6_0", "kvarn4_1"])
 def test_f16_tail_streams_and_decode(fmt, wl):
     n, tail, H = 1500, 300, 2
     with O.canonical("f16"):

@@ -44,7 +44,7 @@ def _check(cache, fmt, wl, n, H, q_heads):
 
 @pytest.mark.parametrize("tail", [0, 300])
 @pytest.mark.parametrize("fmt", ["q2_0", "q3_1", "q4_0", "q5_1", "q6_0", "q8_0", "kvarn2", "kvarn4",
-                                 "kvarn6", "bf16"])
+                                 "kvarn6", "bf16", "kvarn4_1", "kvarn2_1"])
 def test_kld_matches_oracle(fmt, tail):
     wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
     n, H = 5000, 2

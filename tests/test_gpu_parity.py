@@ -129,7 +129,8 @@ def test_every_format_small(fmt):
 # widths (whole pages for both streams as soon as one of them is KVarN).
 MIXED_PAIRS = ["q8_0/q4_0", "q4_0/q4_1", "q4_1/q4_0", "q6_1/q2_0", "bf16/q4_0", "q5_0/bf16",
                "kvarn4/q4_0", "q4_0/kvarn4", "kvarn8/kvarn3", "kvarn4/q8_0", "q3_1/kvarn5",
-               "kvarn4/q4_1", "q4_1/kvarn4"]
+               "kvarn4/q4_1", "q4_1/kvarn4", "kvarn4_1/q4_0", "q4_1/kvarn3_1", "kvarn4_1/kvarn4",
+               "kvarn8_1/kvarn2_1", "bf16/kvarn5_1"]
 
 
 @pytest.mark.parametrize("fmt", MIXED_PAIRS)
@@ -156,7 +157,12 @@ FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4
               "q6_0/q4_0", "q4_1/q6_1", "kvarn5/kvarn5"]
 
 
-@pytest.mark.parametrize("fmt", FAST_PAIRS)
+# kvarnN_1 (KVarN over the affine block quantizer) decodes in the generic kernel: the same
+# many-page shape for it, alone and beside other formats.
+GENERIC_MANY_PAGES = ["kvarn4_1", "kvarn3_1/kvarn3_1", "kvarn2_1/q4_1", "q8_0/kvarn6_1", "kvarn8_1/kvarn4"]
+
+
+@pytest.mark.parametrize("fmt", FAST_PAIRS + GENERIC_MANY_PAGES)
 def test_fast_kernel_mixed_pairs_many_pages(fmt):
     """The fast kernel (every code width) with different key and value formats: 8
     KV heads, 24k tokens (many pages per pair of waves, a partial last page, a 1024-token

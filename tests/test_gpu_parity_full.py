@@ -1,8 +1,8 @@
 """GPU parity at the workloads' full sizes, through the C ABI, in the launch configuration of
 the benchmark (same library entry points, same split planner).
 
-  * 65,536-token sweep: every (format, tail) pair of the block-format sweep and the three
-    KVarN formats, one layer x 8 KV heads x 32 query heads.  Codes, block scales, channel
+  * 65,536-token sweep: every (format, tail) pair of the block-format sweep, the three
+    KVarN formats and kvarn4_1, one layer x 8 KV heads x 32 query heads.  Codes, block scales, channel
     scales and live ring rows of all 16 streams byte-identical to the oracle; decode
     attention of all 32 query heads within 2e-3 (normwise per head) of the oracle's
     binary64 attention over the same dequantized values.
@@ -113,7 +113,7 @@ def test_sweep_64k_every_format_and_tail(fmt, tail, rows_c2):
     _run_64k("c2_sweep_ctx65536", fmt, tail, rows_c2)
 
 
-@pytest.mark.parametrize("fmt", synth.WORKLOADS["c3_kvarn_ctx65536"]["fmts"])
+@pytest.mark.parametrize("fmt", list(synth.WORKLOADS["c3_kvarn_ctx65536"]["fmts"]) + ["kvarn4_1"])
 def test_kvarn_64k_tail_1024(fmt, rows_c3):
     _run_64k("c3_kvarn_ctx65536", fmt, 1024, rows_c3)
 

@@ -58,7 +58,7 @@ def _prefill_case(fmt, n, n_new, tail, H=2):
 
 @pytest.mark.parametrize("tail", [0, 100, 1024])
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q3_1", "q2_0", "kvarn4", "kvarn2", "bf16", "q4_1/kvarn4",
-                                 "kvarn3/q5_1"])
+                                 "kvarn3/q5_1", "kvarn4_1", "kvarn3_1/q4_1", "q4_0/kvarn2_1", "kvarn8_1/kvarn4"])
 def test_prefill_matches_oracle(fmt, tail):
     _prefill_case(fmt, 1500, 160, tail)
 
