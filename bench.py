@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic_kvarn4_ctx240000.md")
-DECODE_SOURCES = ["kvq_decode_ws.h", "kvq_decode_ws_k4.hip", "kvq_decode_ws.hip", "kvq_decode.hip",
+DECODE_SOURCES = ["kvq_decode_ws.h", "kvq_decode_ws_key.hip", "kvq_decode_ws.hip", "kvq_decode.hip",
                   "kvq_merge.hip", "kvq_host.cpp", "kvq_internal.h", "kvq_device.h"]
 
 

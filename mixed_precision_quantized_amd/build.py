@@ -7,6 +7,7 @@ Packed fp32 instructions are disabled for all device code.
 import os
 import subprocess
 import sys
+import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -20,19 +21,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
           "-Wno-unused-command-line-argument", "-I" + INCLUDE]
 
-UNITS = [
+# longest first: the prefill kernels, then the fast decode kernel (one object per key format
+# id 1..24, each against every value format), then the rest
+UNITS = [("kvq_prefill.hip", [])]
+UNITS += [("kvq_decode_ws_key.hip", ["-DKVQ_WS_FK=%d" % f], "kvq_decode_ws_key_f%d" % f) for f in range(1, 25)]
+UNITS += [
     ("kvq_host.cpp", ["-ffp-contract=off"]),
     ("kvq_append.hip", ["-ffp-contract=off"]),
     ("kvq_decode.hip", []),
     ("kvq_decode_ws.hip", []),
-    ("kvq_decode_ws_k2.hip", []),
-    ("kvq_decode_ws_k3.hip", []),
-    ("kvq_decode_ws_k4.hip", []),
-    ("kvq_decode_ws_k5.hip", []),
-    ("kvq_decode_ws_k6.hip", []),
-    ("kvq_decode_ws_k8.hip", []),
     ("kvq_merge.hip", []),
-    ("kvq_prefill.hip", []),
     ("kvq_debug.hip", ["-ffp-contract=off"]),
 ]
 
@@ -48,28 +46,44 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every translation unit and link libkvq.so; returns its path."""
+    """Compile every translation unit and link libkvq.so; returns its path.  Each compiler's
+    output goes to a log file next to its object (the kernel headers' inline-asm clobber
+    warnings run to hundreds of KB per unit, more than a pipe holds)."""
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    procs = []
-    for src, extra in UNITS:
+    running = []                                  # (cmd, process, log file)
+
+    def reap(block):
+        while running:
+            done = [r for r in running if r[1].poll() is not None]
+            for cmd, p, log in done:
+                running.remove((cmd, p, log))
+                log.close()
+                if p.returncode != 0:
+                    with open(log.name) as f:
+                        sys.stderr.write(f.read()[-20000:])
+                    raise RuntimeError("compile failed: " + cmd[-3])
+            if done or not block:
+                return
+            time.sleep(0.2)
+
+    for unit in UNITS:
+        src, extra = unit[0], unit[1]
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(BUILD, (unit[2] if len(unit) > 2 else src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = ["hipcc"] + COMMON + extra + lang + ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        while len(running) >= jobs:
+            reap(True)
+        log = open(obj + ".log", "w")
+        running.append((cmd, subprocess.Popen(cmd, stdout=log, stderr=subprocess.STDOUT), log))
         objs.append(obj)
-        while len([p for _, p in procs if p.poll() is None]) >= jobs:
-            procs[0][1].wait()
-    for cmd, p in procs:
-        out, err = p.communicate()
-        if p.returncode != 0:
-            sys.stderr.write(out + err)
-            raise RuntimeError("compile failed: " + cmd[-3])
+    while running:
+        reap(True)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)

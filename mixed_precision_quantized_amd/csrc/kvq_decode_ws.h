@@ -1,6 +1,6 @@
-// kvq_decode_ws.h -- fast decode attention for 2-, 3-, 4- and 8-bit caches (qN_0, qN_1,
-// kvarnN), gfx950.  The kernel template; each kvq_decode_ws_kN.hip instantiates the key
-// formats of one code width against every value format.
+// kvq_decode_ws.h -- fast decode attention for quantized caches of 2- to 6- and 8-bit codes
+// (qN_0, qN_1, kvarnN, kvarnN_1), gfx950.  The kernel template; kvq_decode_ws_key.hip
+// instantiates one key format against every value format per translation unit.
 //
 // Same work split as the generic kernel (kvq_decode.hip): 128-token quantized pages and
 // 32-token ring chunks, balanced splits, partial results merged by kvq_merge.hip.  One
@@ -36,6 +36,9 @@
 //     values accumulate in the rotated domain scaled by the page's c_V and are rotated
 //     back once in the merge (x = H Yhat / 128, H the unnormalized Sylvester Hadamard
 //     matrix).
+//  kvarnN_1 (KVarN pages over affine blocks): keys add m * sum(q'') per block, taken from
+//     each page's operand; the value minima are folded into the accumulator at every page
+//     change, while it still carries that page's c_V.
 //  Ring (BF16 tail) workgroups use the same pairing with binary32 arithmetic.
 #pragma once
 
@@ -491,12 +494,13 @@ __device__ __forceinline__ void lds_fwht4(float (*buf)[kD])
     __syncthreads();
 }
 
-// FK, FV: key and value formats (qN_0, qN_1 or kvarnN with N = 2, 3, 4 or 8, independently).
+// FK, FV: key and value formats (any quantized format, independently).
 template <int FK, int FV>
 __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 {
-    constexpr bool KVARN_K = fkind(FK) == KIND_KVARN, KVARN_V = fkind(FV) == KIND_KVARN;
-    constexpr bool AFF_K = fkind(FK) == KIND_Q1, AFF_V = fkind(FV) == KIND_Q1;
+    // KVARN_*: paged, rotated formats (kvarnN, kvarnN_1); AFF_*: affine blocks (qN_1, kvarnN_1)
+    constexpr bool KVARN_K = kind_paged(fkind(FK)), KVARN_V = kind_paged(fkind(FV));
+    constexpr bool AFF_K = kind_affine(fkind(FK)), AFF_V = kind_affine(fkind(FV));
     constexpr int NK = fbits(FK), NV = fbits(FV);
     constexpr int RK = 16 * NK, RV = 16 * NV;                       // code bytes per token row
     constexpr int SB_K = AFF_K ? 16 : 8, SB_V = AFF_V ? 16 : 8;   // scale bytes per token row
@@ -989,6 +993,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 ms *= al[vj];
                 msd *= al[vj];
             }
+            if (KVARN_V && AFF_V && page_start) {
+                // kvarnN_1 values: the minima summed so far carry the previous page's channel
+                // scales, so they join the accumulator (at its 2^s' code scale) before it moves
+                // to this page's; the lane's partial sums, like its accumulator's
+                const float mo = fmaf((float)(1 << (NV - 1)), msd, ms);
+                const f32x4 m4 = {quad_bcast(mo, 0), quad_bcast(mo, 1), quad_bcast(mo, 2), quad_bcast(mo, 3)};
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int s = (NV * r) & 7;
+                    D[r] += m4 * (float)(1 << (s < 10 - NV ? s : 10 - NV));
+                }
+                ms = 0.0f;
+                msd = 0.0f;
+            }
             if (KVARN_V && page_start) {
                 // this page's value channel scales: move the accumulator to them (it is zero
                 // before the first page, so the first move is inert)
@@ -1277,6 +1295,7 @@ int ws_value_switch(int op, int fmt_v, const DecodeArgs* a, int n_wgs, hipStream
         KVQ_WS_CASE(1) KVQ_WS_CASE(2) KVQ_WS_CASE(3) KVQ_WS_CASE(4) KVQ_WS_CASE(5) KVQ_WS_CASE(6)
         KVQ_WS_CASE(7) KVQ_WS_CASE(8) KVQ_WS_CASE(9) KVQ_WS_CASE(10) KVQ_WS_CASE(11) KVQ_WS_CASE(12)
         KVQ_WS_CASE(13) KVQ_WS_CASE(14) KVQ_WS_CASE(15) KVQ_WS_CASE(16) KVQ_WS_CASE(17) KVQ_WS_CASE(18)
+        KVQ_WS_CASE(19) KVQ_WS_CASE(20) KVQ_WS_CASE(21) KVQ_WS_CASE(22) KVQ_WS_CASE(23) KVQ_WS_CASE(24)
     default: return op == 0 ? (int)hipErrorInvalidValue : 0;
     }
 #undef KVQ_WS_CASE

@@ -157,12 +157,13 @@ FAST_PAIRS = ["q4_0/q4_1", "q4_1/q4_0", "kvarn4/q4_0", "q4_0/kvarn4", "kvarn4/q4
               "q6_0/q4_0", "q4_1/q6_1", "kvarn5/kvarn5"]
 
 
-# kvarnN_1 (KVarN over the affine block quantizer) decodes in the generic kernel: the same
-# many-page shape for it, alone and beside other formats.
-GENERIC_MANY_PAGES = ["kvarn4_1", "kvarn3_1/kvarn3_1", "kvarn2_1/q4_1", "q8_0/kvarn6_1", "kvarn8_1/kvarn4"]
+# kvarnN_1 (KVarN over the affine block quantizer): every width as keys and as values, alone
+# and beside the other kinds (the value minima cross page boundaries; affine 8-bit keys)
+KVARN1_PAIRS = ["kvarn4_1", "kvarn3_1/kvarn3_1", "kvarn2_1/q4_1", "q8_0/kvarn6_1", "kvarn8_1/kvarn4",
+                "kvarn5_1/kvarn5_1", "kvarn6_1/q2_0", "q4_0/kvarn8_1", "kvarn4/kvarn2_1", "kvarn8_1/kvarn8_1"]
 
 
-@pytest.mark.parametrize("fmt", FAST_PAIRS + GENERIC_MANY_PAGES)
+@pytest.mark.parametrize("fmt", FAST_PAIRS + KVARN1_PAIRS)
 def test_fast_kernel_mixed_pairs_many_pages(fmt):
     """The fast kernel (every code width) with different key and value formats: 8
     KV heads, 24k tokens (many pages per pair of waves, a partial last page, a 1024-token
