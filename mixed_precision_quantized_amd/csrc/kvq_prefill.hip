@@ -259,8 +259,12 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
     if (kind_paged(KK) && quant && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
 }
 
+// Two workgroups per CU (two waves per SIMD) where the registers allow: the kernel is
+// latency-bound at one wave per SIMD (+55 % for block-format keys at 52-68 B of spills).
+// Paged keys keep one: the rotated query and the page operand need about 150 more
+// registers per lane.
 template <int KK, int KV>
-__global__ __launch_bounds__(256) void k_prefill(PrefillArgs a)
+__global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(PrefillArgs a)
 {
     // Wave h computes query head h of the group (32 queries) and, with the others, stages
     // the blocks: block i + 2 is loaded to raw LDS and block i + 1 unpacked while block i is
