@@ -21,20 +21,20 @@ namespace {
 
 constexpr int kG = 4;
 constexpr int kCols = kD / 4;                 // float4 columns of one head's accumulator
-constexpr int kGroups = 32;                   // split groups: thread = (group, column)
-constexpr int kThreads = kGroups * kCols;     // 1024
+constexpr int kGroups = 8;                    // split groups: thread = (group, column)
+constexpr int kThreads = kGroups * kCols;     // 256
 
-// One workgroup per (sequence, KV head, query head of the group).  Thread (g, c) merges
-// float4 column c over the splits g, g + 32, ... with its own running maximum, so all its
-// loads are independent and issue together (a wave reads two splits' full rows); the 32
-// groups then combine through LDS.
+// One workgroup per (sequence, KV head, query head of the group).  Thread (g, c) folds
+// float4 column c over the splits g, g + 8, ... with its own running maximum, all loads of
+// a batch issued together; the 8 groups then combine through LDS (three barriers), and
+// wave 0 finishes the dims in registers: lane l holds dims l and l + 64, so the inverse
+// rotation of KVarN is one in-lane butterfly (span 64) and six cross-lane ones.
 template <bool KVARN>
 __global__ __launch_bounds__(kThreads) void k_merge(DecodeArgs a)
 {
     __shared__ float4 rq[kGroups][kCols], rt[kGroups][kCols];   // [group][column]
     __shared__ float gm[kGroups], gl[kGroups];
     __shared__ float vq[kD], vt[kD];
-    __shared__ float ML[2];
 
     const int tid = threadIdx.x, c = tid % kCols, g = tid / kCols;
     const int H = a.g.n_kv_heads;
@@ -78,51 +78,51 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeArgs a)
     }
     if (c == 0) { gm[g] = mx; gl[g] = L; }
     __syncthreads();
-    if (tid < 64) {                           // one wave: maximum and normalizer over groups
-        const float m = tid < kGroups ? gm[tid] : -1.0e30f;
-        float M = m;
+    // every thread: the common maximum and the normalizer over the 8 groups
+    float M = gm[0];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float T = tid < kGroups ? gl[tid] * __builtin_amdgcn_exp2f(m - M) : 0.0f;
+    for (int gg = 1; gg < kGroups; ++gg) M = fmaxf(M, gm[gg]);
+    float T = 0.0f;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) T += __shfl_xor(T, o);
-        if (tid == 0) { ML[0] = M; ML[1] = T; }
-    }
-    __syncthreads();
+    for (int gg = 0; gg < kGroups; ++gg) T += gl[gg] * __builtin_amdgcn_exp2f(gm[gg] - M);
     {
         // rescale to the common maximum before the sum, so the column sums below are plain adds
-        const float w = __builtin_amdgcn_exp2f(mx - ML[0]);
+        const float w = __builtin_amdgcn_exp2f(mx - M);
         rq[g][c] = make_float4(aq.x * w, aq.y * w, aq.z * w, aq.w * w);
         rt[g][c] = make_float4(at.x * w, at.y * w, at.z * w, at.w * w);
     }
     __syncthreads();
-    if (tid < 2 * kD) {
-        // thread = (quantized | ring part, dim): 32 adds down the groups
+    {
+        // thread = (quantized | ring part, dim): 8 adds down the groups
         const int part = tid / kD, d = tid % kD, cc = d >> 2, k = d & 3;
         const float4 (*r)[kCols] = part ? rt : rq;
         float sum = 0.0f;
-#pragma unroll 8
+#pragma unroll
         for (int gg = 0; gg < kGroups; ++gg) sum += reinterpret_cast<const float*>(&r[gg][cc])[k];
         (part ? vt : vq)[d] = sum;
     }
-    if (KVARN) {
-        // x = H yhat / 128, butterflies of span 1, 2, .., 64
-        for (int span = 1; span < kD; span <<= 1) {
-            __syncthreads();
-            if (tid < kD / 2) {
-                const int lo = tid & (span - 1);
-                const int i = ((tid - lo) << 1) | lo;
-                const float x = vq[i], y = vq[i + span];
-                vq[i] = x + y;
-                vq[i + span] = x - y;
-            }
-        }
-    }
     __syncthreads();
-    if (tid < kD) {
-        float q = vq[tid];
-        if (KVARN) q *= (1.0f / 128.0f);
-        a.out[((int64_t)sq.in_idx * a.g.n_q_heads + head * kG + h) * kD + tid] = (q + vt[tid]) / ML[1];
+    if (tid < 64) {
+        const int l = tid;
+        float x0 = vq[l], x1 = vq[l + 64];
+        if (KVARN) {
+            // x = H yhat / 128: span 64 inside the lane, spans 32 .. 1 across lanes
+            const float u = x0 + x1, w = x0 - x1;
+            x0 = u;
+            x1 = w;
+#pragma unroll
+            for (int sp = 32; sp >= 1; sp >>= 1) {
+                const float y0 = __shfl_xor(x0, sp), y1 = __shfl_xor(x1, sp);
+                const bool up = (l & sp) != 0;
+                x0 = up ? y0 - x0 : x0 + y0;
+                x1 = up ? y1 - x1 : x1 + y1;
+            }
+            x0 *= (1.0f / 128.0f);
+            x1 *= (1.0f / 128.0f);
+        }
+        float* o = a.out + ((int64_t)sq.in_idx * a.g.n_q_heads + head * kG + h) * kD;
+        o[l] = (x0 + vt[l]) / T;
+        o[l + 64] = (x1 + vt[l + 64]) / T;
     }
 }
 
