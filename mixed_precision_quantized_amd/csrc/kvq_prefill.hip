@@ -20,14 +20,18 @@
 // binary32 product of that block's 32 dims, and the affine minimum m as m * sum(q) of the
 // block, so the keys are used exactly.  (Rounding dequantized keys to binary16 would not do:
 // keys with 15x outlier channels reach |k| ~ 800, where binary16 keeps 0.25 absolute.)  The
-// query (times the page's channel scales for KVarN keys) enters as two binary16 terms,
-// q = hi + lo, one MFMA each: one rounding of q alone cost up to 1.9e-3 of the output on the
-// 64k block-format workload.  Values are dequantized to binary16 (|v| is small) and the
+// query enters as two binary16 terms, q = hi + lo, one MFMA each: one rounding of q alone
+// cost up to 1.9e-3 of the output on the 64k block-format workload.  Values are dequantized to binary16 (|v| is small) and the
 // probabilities are rounded to binary16 before the P V product.
 //
-// KVarN (either inner quantizer), as in decode: keys are scored in the rotated domain with q'' = (H q / 128) * c_K
-// of the page; values accumulate in the rotated domain and are rotated back once in the
-// merge (quantized and ring blocks never share a split, so each split is in one domain).
+// KVarN (either inner quantizer): keys are scored in the rotated domain against
+// q' = H q / 128.  The page's key channel scale goes to the key side: c (u - o) is exact in
+// binary32 and is held as two exact binary16 terms hi + lo (11 and at most 8 significant
+// bits), scored as q'_hi hi + q'_lo hi + q'_hi lo (q'_lo lo is below 2^-20 of the term);
+// no per-page query operand is built.  Over affine blocks the minimum term takes
+// m sum_j q'_j c_j per page.  Values accumulate in the rotated domain and are rotated back
+// once in the merge (quantized and ring blocks never share a split, so each split is in one
+// domain).
 #include "kvq_device.h"
 
 namespace kvq {
@@ -42,6 +46,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct alignas(16) PfLds {
     _Float16 kc[kPfKB][kD + 8];     // key codes (or exact values), token-major; +8: bank spread
+    _Float16 kl[kPfKB][kD + 8];     // paged keys: c (u - o) = kc + kl, both binary16-exact
     _Float16 vt[kD][kPfKB + 8];     // dequantized values, dim-major
     float dk[4][kPfKB];             // key block scales [block][token] (1 for exact rows)
     float mk[4][kPfKB];             // key block minima (affine codes)
@@ -58,9 +63,11 @@ __device__ __forceinline__ const char* pf_stream(const CacheGeom& g, int seq, in
 // rows) are loaded straight to LDS by buffer loads two blocks ahead of use (no registers,
 // the latency overlaps the compute of two blocks); one block ahead, the waves unpack them
 // into the binary16 operand buffers.
+template <bool BIG>
 struct alignas(16) PfRawL {
-    uint8_t k[8192];       // key codes (32 rows of 16 N bytes) or BF16 rows (32 x 256 B)
-    uint8_t v[8192];
+    static constexpr int kRows = BIG ? 8192 : 4096;    // BF16 rows (32 x 256 B), or 32 rows of 16 N <= 128 B
+    uint8_t k[kRows];
+    uint8_t v[kRows];
     uint8_t ks[512];       // block-scale rows (8 or 16 B per token)
     uint8_t vs[512];
     uint16_t kch[128];     // KVarN channel scales of the block's page
@@ -112,18 +119,19 @@ __device__ __forceinline__ PfStream pf_stream_rsrc(const PrefillArgs& a, const c
     return S;
 }
 
-template <int KK, int KV>
-__device__ __forceinline__ void pf_dma(PfRawL& R, const PrefillArgs& a, const PfStream& SK, const PfStream& SV,
+template <int KK, int KV, bool RING, bool BIG>
+__device__ __forceinline__ void pf_dma(PfRawL<BIG>& R, const PrefillArgs& a, const PfStream& SK, const PfStream& SV,
                                        int64_t tb, int nt, int wave, int lane)
 {
     auto stream = [&](const PfStream& S, bool coded, bool kvarn, uint8_t* dst, uint8_t* sdst, uint16_t* cdst,
                       int swave, int cwave) {
-        if (!S.ring) {
+        if (!RING) {
+            // the block's 2 rb chunks of 16 B (256 for codes of 8 bits or less: one per thread)
             const int base = (int)tb * S.rb;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < (BIG ? 2 : 1); ++i) {
                 const int c0 = 64 * (wave + 4 * i);
-                pf_dma16(S.rows, base + 16 * (c0 + lane), dst + 16 * c0);
+                if (c0 + lane < 2 * S.rb) pf_dma16(S.rows, base + 16 * (c0 + lane), dst + 16 * c0);
             }
             if (coded && wave == swave && lane < 32) pf_dma16(S.scales, (int)tb * S.sb + 16 * lane, sdst);
             if (kvarn && wave == cwave && lane < 16) pf_dma16(S.chan, (int)(tb / kPage) * 256 + 16 * lane, cdst);
@@ -173,8 +181,8 @@ __device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part,
 
 // Unpack a raw block into the operand buffers.  Thread tid: token r = tid >> 3, dims
 // 16 (tid & 7) .. of both streams.
-template <int KK, int KV>
-__device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const PrefillArgs& a, int nt, bool quant, int tid)
+template <int KK, int KV, bool RING, bool BIG>
+__device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const PrefillArgs& a, int nt, bool quant, int tid)
 {
     const CacheGeom& g = a.g;
     const int r = tid >> 3, pp = tid & 7, b = pp >> 1;
@@ -188,6 +196,12 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         const float off = kind_affine(KK) ? 0.0f : (float)(1 << (N - 1));
 #pragma unroll
         for (int e = 0; e < 16; ++e) kx[e] = (float)u[e] - off;
+        if (kind_paged(KK) && !RING) {
+            // the page's key channel scale on the key side: c (u - o) is exact in binary32
+            // (11 + N significant bits) and splits into two exact binary16 terms
+#pragma unroll
+            for (int e = 0; e < 16; ++e) kx[e] *= fp16_to_f32(R.kch[16 * pp + e]);
+        }
         if (kind_affine(KK)) {
             const uint32_t dm = *(const uint32_t*)(R.ks + r * 16 + 4 * b);
             d = fp16_to_f32(dm & 0xFFFFu);
@@ -249,6 +263,18 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         uint4* dst = (uint4*)&L.kc[r][16 * pp];
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
         dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        if (kind_paged(KK) && !RING) {
+            // low parts: c (u - o) - hi, at most 8 significant bits
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const h2 hv = __builtin_bit_cast(h2, w[i]);
+                const h2 v = {(_Float16)(kx[2 * i] - (float)hv.x), (_Float16)(kx[2 * i + 1] - (float)hv.y)};
+                w[i] = __builtin_bit_cast(uint32_t, v);
+            }
+            uint4* dl = (uint4*)&L.kl[r][16 * pp];
+            dl[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dl[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) L.vt[16 * pp + e][r] = (_Float16)vx[e];
@@ -256,28 +282,31 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL& R, const Prefi
         L.dk[b][r] = d;
         L.mk[b][r] = m;
     }
-    if (kind_paged(KK) && quant && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
+    if (kind_paged(KK) && !RING && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
 }
 
-// Two workgroups per CU (two waves per SIMD) where the registers allow: the kernel is
-// latency-bound at one wave per SIMD (+55 % for block-format keys at 52-68 B of spills).
-// Paged keys keep one: the rotated query and the page operand need about 150 more
-// registers per lane.
-template <int KK, int KV>
-__global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(PrefillArgs a)
+// RING: the kernel of the ring (16-bit) splits, else of the quantized splits.  The
+// quantized kernel runs two workgroups per CU (two waves per SIMD): at one wave per SIMD
+// the kernel is latency-bound (two gave +55 % at 52-68 B of spills per lane).  Its raw
+// staging holds code rows only (at most 4 KB per stream), so that two workgroups fit the
+// LDS; BIG staging (BF16 rows: the ring splits, bf16-format streams) runs one per CU, and
+// so do kvarnN_1 keys (their per-page block sums would spill ~440 B per lane at two).
+template <int KK, int KV, bool RING, bool BIG = RING || KK == KIND_BF16 || KV == KIND_BF16>
+__global__ __launch_bounds__(256, BIG || KK == KIND_KVARN1 ? 1 : 2) void k_prefill(PrefillArgs a)
 {
     // Wave h computes query head h of the group (32 queries) and, with the others, stages
     // the blocks: block i + 2 is loaded to raw LDS and block i + 1 unpacked while block i is
     // computed; one barrier per block.
     __shared__ PfLds L[2];
-    __shared__ PfRawL RW[2];
+    __shared__ PfRawL<BIG> RW[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = a.splits_q + a.splits_t;
-    const int sp = blockIdx.x % S;
-    const int tile = (blockIdx.x / S) % a.tiles;
-    const int head = blockIdx.x / (S * a.tiles);
-    const bool quant = sp < a.splits_q;
+    const int SS = RING ? a.splits_t : a.splits_q;                   // splits of this kernel
+    const int sp = (RING ? a.splits_q : 0) + blockIdx.x % SS;
+    const int tile = (blockIdx.x / SS) % a.tiles;
+    const int head = blockIdx.x / (SS * a.tiles);
+    constexpr bool quant = !RING;
     const CacheGeom& g = a.g;
     const char* kst = pf_stream(g, a.seq, a.layer, head, 0);
     const char* vst = pf_stream(g, a.seq, a.layer, head, 1);
@@ -301,11 +330,10 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
     const bool qvalid = qi < a.n_new;
     const int64_t pos = a.n - a.n_new + (qvalid ? qi : a.n_new - 1);
     const int64_t pos_min = a.n - a.n_new + kPfQ * tile;             // the tile's first query
-    const bool kv_k = kind_paged(KK) && quant;
+    constexpr bool kv_k = kind_paged(KK) && !RING;
 
     // ---- query: the lane's 64 dims {16 idx + 8 hh + c}, log2 domain, as hi + lo binary16 ----
-    h8 qb[8], ql[8];                 // the operand of the current page: query = qb + ql
-    h8 rb[8], rl[8];                 // KVarN: the rotated query H q / 128 (before c_K)
+    h8 qb[8], ql[8];                 // the query operand (paged keys: H q / 128) = qb + ql
     {
         float qf[8][8];
         const int64_t base = ((int64_t)(qvalid ? qi : 0) * g.n_q_heads + head * kG + h) * kD;
@@ -357,10 +385,6 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
                 qb[idx][c] = hi;
                 ql[idx][c] = (_Float16)(qf[idx][c] - (float)hi);
             }
-        if (kv_k) {
-#pragma unroll
-            for (int idx = 0; idx < 8; ++idx) { rb[idx] = qb[idx]; rl[idx] = ql[idx]; }
-        }
     }
     float qsum[4];
     auto make_qsum = [&]() {
@@ -374,19 +398,21 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
         }
     };
     if (KK == KIND_Q1) make_qsum();
-    // KVarN keys: q'' = (H q / 128) * c_K of the page, again as hi + lo; over affine blocks
-    // the minimum term takes the block sums of this page's operand
-    auto page_operand = [&](const PfLds& B) {
+    // paged keys over affine blocks: the minimum term m sum_j q'_j c_j takes the block sums
+    // of the rotated query times the page's key channel scales, per page
+    auto page_qsum = [&](const PfLds& B) {
 #pragma unroll
-        for (int idx = 0; idx < 8; ++idx)
+        for (int b = 0; b < 4; ++b) {
+            float s = 0.0f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float v = ((float)rb[idx][c] + (float)rl[idx][c]) * B.ck[16 * idx + 8 * hh + c];
-                const _Float16 hi = (_Float16)v;
-                qb[idx][c] = hi;
-                ql[idx][c] = (_Float16)(v - (float)hi);
-            }
-        if (KK == KIND_KVARN1) make_qsum();
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int idx = 2 * b + k2;
+                    s = fmaf((float)qb[idx][c] + (float)ql[idx][c], B.ck[16 * idx + 8 * hh + c], s);
+                }
+            qsum[b] = s + __shfl_xor(s, 32);
+        }
     };
 
     float mrun = kNeg, lrun = 0.0f;
@@ -398,9 +424,9 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
     int64_t page = -1;
     // key rows of this lane in the 32x32 accumulators: i(r) = 8 (r / 4) + 4 hh + r % 4
     auto compute = [&](const PfLds& B, int64_t tb, int nt) __attribute__((always_inline)) {
-        if (kv_k && tb / kPage != page) {
+        if (kv_k && KK == KIND_KVARN1 && tb / kPage != page) {
             page = tb / kPage;
-            page_operand(B);
+            page_qsum(B);
         }
         // S^T: keys x queries
         f32x16 Sacc;
@@ -418,6 +444,11 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
                 const h8 A = *(const h8*)&B.kc[j][16 * idx + 8 * hh];
                 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qb[idx], T, 0, 0, 0);
                 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, ql[idx], T, 0, 0, 0);
+                if (kv_k) {
+                    // low key term against the high query term (lo x lo is below 2^-20)
+                    const h8 Al = *(const h8*)&B.kl[j][16 * idx + 8 * hh];
+                    T = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, qb[idx], T, 0, 0, 0);
+                }
             }
             if (scaled) {
 #pragma unroll
@@ -490,18 +521,18 @@ __global__ __launch_bounds__(256, kind_paged(KK) ? 1 : 2) void k_prefill(Prefill
             }
     };
     const PfStream SK = pf_stream_rsrc(a, kst, g.k, g.fmt_k, quant), SV = pf_stream_rsrc(a, vst, g.v, g.fmt_v, quant);
-    if (nb > 0) pf_dma<KK, KV>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
-    if (nb > 1) pf_dma<KK, KV>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
+    if (nb > 0) pf_dma<KK, KV, RING, BIG>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
+    if (nb > 1) pf_dma<KK, KV, RING, BIG>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
     pf_wait_vm0();
     __syncthreads();
-    if (nb > 0) pf_unpack<KK, KV>(L[0], RW[0], a, nt_of(0), quant, tid);
+    if (nb > 0) pf_unpack<KK, KV, RING, BIG>(L[0], RW[0], a, nt_of(0), quant, tid);
     // iteration i: L[i & 1] holds block i, RW[(i + 1) & 1] raw block i + 1 (loaded during
     // block i - 1); RW[i & 1] is free for block i + 2
-    auto step = [&](int i, PfLds& Lc, PfLds& Ln, PfRawL& Rn, PfRawL& Rf) __attribute__((always_inline)) {
+    auto step = [&](int i, PfLds& Lc, PfLds& Ln, PfRawL<BIG>& Rn, PfRawL<BIG>& Rf) __attribute__((always_inline)) {
         pf_wait_vm0();
         __syncthreads();
-        if (i + 1 < nb) pf_unpack<KK, KV>(Ln, Rn, a, nt_of(i + 1), quant, tid);
-        if (i + 2 < nb) pf_dma<KK, KV>(Rf, a, SK, SV, tb_of(i + 2), nt_of(i + 2), wave, lane);
+        if (i + 1 < nb) pf_unpack<KK, KV, RING, BIG>(Ln, Rn, a, nt_of(i + 1), quant, tid);
+        if (i + 2 < nb) pf_dma<KK, KV, RING, BIG>(Rf, a, SK, SV, tb_of(i + 2), nt_of(i + 2), wave, lane);
         compute(Lc, tb_of(i), nt_of(i));
     };
     for (int i = 0; i < nb; i += 2) {
@@ -567,8 +598,11 @@ __global__ __launch_bounds__(128) void k_prefill_merge(PrefillArgs a)
 template <int KK, int KV>
 int launch_pf(const PrefillArgs& a, hipStream_t st)
 {
-    const int n = a.g.n_kv_heads * a.tiles * (a.splits_q + a.splits_t);
-    hipLaunchKernelGGL((k_prefill<KK, KV>), dim3(n), dim3(256), 0, st, a);
+    // quantized splits and ring splits: one kernel each (their staging differs)
+    if (a.splits_q > 0)
+        hipLaunchKernelGGL((k_prefill<KK, KV, false>), dim3(a.g.n_kv_heads * a.tiles * a.splits_q), dim3(256), 0, st, a);
+    if (a.splits_t > 0)
+        hipLaunchKernelGGL((k_prefill<KK, KV, true>), dim3(a.g.n_kv_heads * a.tiles * a.splits_t), dim3(256), 0, st, a);
     return (int)hipGetLastError();
 }
 
