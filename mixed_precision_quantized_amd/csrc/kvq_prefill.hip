@@ -119,10 +119,12 @@ __device__ __forceinline__ PfStream pf_stream_rsrc(const PrefillArgs& a, const c
     return S;
 }
 
-template <int KK, int KV, bool RING, bool BIG>
+// NW waves: 4 load both streams, 8 split them (waves 0-3 keys, 4-7 values).
+template <int KK, int KV, bool RING, bool BIG, int NW>
 __device__ __forceinline__ void pf_dma(PfRawL<BIG>& R, const PrefillArgs& a, const PfStream& SK, const PfStream& SV,
-                                       int64_t tb, int nt, int wave, int lane)
+                                       int64_t tb, int nt, int wave_, int lane)
 {
+    const int wave = wave_ & 3;
     auto stream = [&](const PfStream& S, bool coded, bool kvarn, uint8_t* dst, uint8_t* sdst, uint16_t* cdst,
                       int swave, int cwave) {
         if (!RING) {
@@ -146,8 +148,8 @@ __device__ __forceinline__ void pf_dma(PfRawL<BIG>& R, const PrefillArgs& a, con
             }
         }
     };
-    stream(SK, KK != KIND_BF16, kind_paged(KK), R.k, R.ks, R.kch, 0, 2);
-    stream(SV, KV != KIND_BF16, kind_paged(KV), R.v, R.vs, R.vch, 1, 3);
+    if (NW == 4 || wave_ < 4) stream(SK, KK != KIND_BF16, kind_paged(KK), R.k, R.ks, R.kch, 0, 2);
+    if (NW == 4 || wave_ >= 4) stream(SV, KV != KIND_BF16, kind_paged(KV), R.v, R.vs, R.vch, 1, 3);
 }
 
 // 16 N-bit codes of part `part` of a row held at lds row (dword aligned)
@@ -179,17 +181,19 @@ __device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part,
     }
 }
 
-// Unpack a raw block into the operand buffers.  Thread tid: token r = tid >> 3, dims
-// 16 (tid & 7) .. of both streams.
-template <int KK, int KV, bool RING, bool BIG>
+// Unpack a raw block into the operand buffers.  Thread tid (0..255): token r = tid >> 3,
+// dims 16 (tid & 7) .. of the keys (PART 1), the values (PART 2) or both (PART 0).
+template <int KK, int KV, bool RING, bool BIG, int PART>
 __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const PrefillArgs& a, int nt, bool quant, int tid)
 {
+    constexpr bool DK = PART != 2, DV = PART != 1;
     const CacheGeom& g = a.g;
     const int r = tid >> 3, pp = tid & 7, b = pp >> 1;
     const bool valid = r < nt;
     float kx[16], vx[16];
     float d = 1.0f, m = 0.0f;
-    if (quant && KK != KIND_BF16) {
+    if (!DK) {
+    } else if (quant && KK != KIND_BF16) {
         const int N = fbits(g.fmt_k);
         uint32_t u[16];
         unpack16_rt(N, R.k + r * 16 * N, pp, u);
@@ -219,7 +223,8 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             kx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
     }
-    if (quant && KV != KIND_BF16) {
+    if (!DV) {
+    } else if (quant && KV != KIND_BF16) {
         const int N = fbits(g.fmt_v);
         uint32_t u[16];
         unpack16_rt(N, R.v + r * 16 * N, pp, u);
@@ -252,7 +257,7 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
 #pragma unroll
         for (int e = 0; e < 16; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
     }
-    {
+    if (DK) {
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         uint32_t w[8];
 #pragma unroll
@@ -276,55 +281,61 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             dl[1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
     }
+    if (DV) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) L.vt[16 * pp + e][r] = (_Float16)vx[e];
-    if ((pp & 1) == 0) {
+        for (int e = 0; e < 16; ++e) L.vt[16 * pp + e][r] = (_Float16)vx[e];
+    }
+    if (DK && (pp & 1) == 0) {
         L.dk[b][r] = d;
         L.mk[b][r] = m;
     }
-    if (kind_paged(KK) && !RING && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
+    if (DK && kind_paged(KK) && !RING && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
 }
 
 // RING: the kernel of the ring (16-bit) splits, else of the quantized splits.  The
-// quantized kernel runs two workgroups per CU (two waves per SIMD): at one wave per SIMD
-// the kernel is latency-bound (two gave +55 % at 52-68 B of spills per lane).  Its raw
-// staging holds code rows only (at most 4 KB per stream), so that two workgroups fit the
-// LDS; BIG staging (BF16 rows: the ring splits, bf16-format streams) runs one per CU, and
-// so do kvarnN_1 keys (their per-page block sums would spill ~440 B per lane at two).
-template <int KK, int KV, bool RING, bool BIG = RING || KK == KIND_BF16 || KV == KIND_BF16>
-__global__ __launch_bounds__(256, BIG || KK == KIND_KVARN1 ? 1 : 2) void k_prefill(PrefillArgs a)
+// quantized kernel runs NT = 2 query tiles per workgroup: 8 waves (two per SIMD: at one
+// the kernel is latency-bound) share each staged and unpacked block, and its raw staging
+// holds code rows only (at most 4 KB per stream).  BIG staging (BF16 rows: the ring
+// splits, bf16-format streams) and kvarnN_1 keys (their per-page block sums would spill
+// ~440 B per lane within 256 registers) run one tile of 4 waves.
+template <int KK, int KV, bool RING, bool BIG = RING || KK == KIND_BF16 || KV == KIND_BF16,
+          int NT = (BIG || KK == KIND_KVARN1) ? 1 : 2>
+__global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 {
-    // Wave h computes query head h of the group (32 queries) and, with the others, stages
-    // the blocks: block i + 2 is loaded to raw LDS and block i + 1 unpacked while block i is
-    // computed; one barrier per block.
+    // Wave w computes query head w % 4 of the group for the 32 queries of tile w / 4 and,
+    // with the others, stages the blocks: block i + 2 is loaded to raw LDS and block i + 1
+    // unpacked while block i is computed; one barrier per block.
     __shared__ PfLds L[2];
     __shared__ PfRawL<BIG> RW[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = a.splits_q + a.splits_t;
     const int SS = RING ? a.splits_t : a.splits_q;                   // splits of this kernel
+    const int tiles_g = (a.tiles + NT - 1) / NT;                     // tile groups
     const int sp = (RING ? a.splits_q : 0) + blockIdx.x % SS;
-    const int tile = (blockIdx.x / SS) % a.tiles;
-    const int head = blockIdx.x / (SS * a.tiles);
+    const int tg = (blockIdx.x / SS) % tiles_g;
+    const int head = blockIdx.x / (SS * tiles_g);
+    const int tile = NT * tg + (wave >> 2);                          // this wave's tile
     constexpr bool quant = !RING;
     const CacheGeom& g = a.g;
     const char* kst = pf_stream(g, a.seq, a.layer, head, 0);
     const char* vst = pf_stream(g, a.seq, a.layer, head, 1);
-    const int64_t pos_max = a.n - a.n_new + min(kPfQ * tile + kPfQ, a.n_new) - 1;
+    // the workgroup's last query
+    const int64_t pos_max = a.n - a.n_new + min(kPfQ * NT * (tg + 1), a.n_new) - 1;
 
     // ---- key range of the split (32-token blocks of the quantized or the ring region) ------
     const int64_t r0 = quant ? 0 : a.n_q, r1 = quant ? a.n_q : a.n;
     const int blk0 = (quant ? sp : sp - a.splits_q) * a.bps;
     const int nblk = (int)((r1 - r0 + kPfKB - 1) / kPfKB);
     const int blk1 = min(blk0 + a.bps, nblk);
-    // causal: no key after the tile's last query is seen
+    // causal: no key after the workgroup's last query is seen
     const int blk_end = pos_max < r0 ? blk0 : (int)min<int64_t>(blk1, (pos_max - r0) / kPfKB + 1);
     const int nb = max(0, blk_end - blk0);
     auto tb_of = [&](int i) { return r0 + (int64_t)(blk0 + i) * kPfKB; };
     auto nt_of = [&](int i) { return (int)min<int64_t>(kPfKB, r1 - tb_of(i)); };
 
     // ================================ compute waves ================================
-    const int h = wave;                                              // query head of the group
+    const int h = wave & 3;                                          // query head of the group
     const int j = lane & 31, hh = lane >> 5;
     const int qi = kPfQ * tile + j;                                  // query index in the chunk
     const bool qvalid = qi < a.n_new;
@@ -521,18 +532,24 @@ __global__ __launch_bounds__(256, BIG || KK == KIND_KVARN1 ? 1 : 2) void k_prefi
             }
     };
     const PfStream SK = pf_stream_rsrc(a, kst, g.k, g.fmt_k, quant), SV = pf_stream_rsrc(a, vst, g.v, g.fmt_v, quant);
-    if (nb > 0) pf_dma<KK, KV, RING, BIG>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
-    if (nb > 1) pf_dma<KK, KV, RING, BIG>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
+    if (nb > 0) pf_dma<KK, KV, RING, BIG, 4 * NT>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
+    if (nb > 1) pf_dma<KK, KV, RING, BIG, 4 * NT>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
     pf_wait_vm0();
     __syncthreads();
-    if (nb > 0) pf_unpack<KK, KV, RING, BIG>(L[0], RW[0], a, nt_of(0), quant, tid);
+    // keys by threads 0-255 and values by 256-511 (NT = 2), or both by every thread
+    auto unpack = [&](PfLds& Ld, const PfRawL<BIG>& Rr, int nt) __attribute__((always_inline)) {
+        if constexpr (NT == 1) pf_unpack<KK, KV, RING, BIG, 0>(Ld, Rr, a, nt, quant, tid);
+        else if (tid < 256) pf_unpack<KK, KV, RING, BIG, 1>(Ld, Rr, a, nt, quant, tid);
+        else pf_unpack<KK, KV, RING, BIG, 2>(Ld, Rr, a, nt, quant, tid - 256);
+    };
+    if (nb > 0) unpack(L[0], RW[0], nt_of(0));
     // iteration i: L[i & 1] holds block i, RW[(i + 1) & 1] raw block i + 1 (loaded during
     // block i - 1); RW[i & 1] is free for block i + 2
     auto step = [&](int i, PfLds& Lc, PfLds& Ln, PfRawL<BIG>& Rn, PfRawL<BIG>& Rf) __attribute__((always_inline)) {
         pf_wait_vm0();
         __syncthreads();
-        if (i + 1 < nb) pf_unpack<KK, KV, RING, BIG>(Ln, Rn, a, nt_of(i + 1), quant, tid);
-        if (i + 2 < nb) pf_dma<KK, KV, RING, BIG>(Rf, a, SK, SV, tb_of(i + 2), nt_of(i + 2), wave, lane);
+        if (i + 1 < nb) unpack(Ln, Rn, nt_of(i + 1));
+        if (i + 2 < nb) pf_dma<KK, KV, RING, BIG, 4 * NT>(Rf, a, SK, SV, tb_of(i + 2), nt_of(i + 2), wave, lane);
         compute(Lc, tb_of(i), nt_of(i));
     };
     for (int i = 0; i < nb; i += 2) {
@@ -541,6 +558,7 @@ __global__ __launch_bounds__(256, BIG || KK == KIND_KVARN1 ? 1 : 2) void k_prefi
     }
     pf_wait_vm0();
     // ---- partial result of the split: m, l and acc[128] per query (dims 32 b + i(r)) --------
+    if (tile >= a.tiles) return;                                    // the odd tile group's empty half
     float* pp = a.partials + (((((int64_t)head * a.tiles + tile) * S + sp) * kG + h) * kPfQ + j) * (kD + 2);
     if (hh == 0) {
         pp[0] = mrun;
@@ -599,8 +617,10 @@ template <int KK, int KV>
 int launch_pf(const PrefillArgs& a, hipStream_t st)
 {
     // quantized splits and ring splits: one kernel each (their staging differs)
+    constexpr int NQ = (KK == KIND_BF16 || KV == KIND_BF16 || KK == KIND_KVARN1) ? 1 : 2;   // tiles per workgroup
     if (a.splits_q > 0)
-        hipLaunchKernelGGL((k_prefill<KK, KV, false>), dim3(a.g.n_kv_heads * a.tiles * a.splits_q), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_prefill<KK, KV, false>), dim3(a.g.n_kv_heads * ((a.tiles + NQ - 1) / NQ) * a.splits_q),
+                           dim3(256 * NQ), 0, st, a);
     if (a.splits_t > 0)
         hipLaunchKernelGGL((k_prefill<KK, KV, true>), dim3(a.g.n_kv_heads * a.tiles * a.splits_t), dim3(256), 0, st, a);
     return (int)hipGetLastError();
