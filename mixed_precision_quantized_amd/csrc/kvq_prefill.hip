@@ -293,13 +293,13 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
 }
 
 // RING: the kernel of the ring (16-bit) splits, else of the quantized splits.  The
-// quantized kernel runs NT = 2 query tiles per workgroup: 8 waves (two per SIMD: at one
-// the kernel is latency-bound) share each staged and unpacked block, and its raw staging
-// holds code rows only (at most 4 KB per stream).  BIG staging (BF16 rows: the ring
-// splits, bf16-format streams) and kvarnN_1 keys (their per-page block sums would spill
-// ~440 B per lane within 256 registers) run one tile of 4 waves.
+// kernel runs NT = 2 query tiles per workgroup: 8 waves (two per SIMD: at one the kernel
+// is latency-bound) share each staged and unpacked block.  The quantized kernel's raw
+// staging holds code rows only (at most 4 KB per stream); BIG staging holds BF16 rows (the
+// ring splits, bf16-format streams).  kvarnN_1 keys run one tile of 4 waves: their per-page
+// block sums would spill ~230 B per lane within 256 registers.
 template <int KK, int KV, bool RING, bool BIG = RING || KK == KIND_BF16 || KV == KIND_BF16,
-          int NT = (BIG || KK == KIND_KVARN1) ? 1 : 2>
+          int NT = (KK == KIND_KVARN1 && !RING) ? 1 : 2>
 __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 {
     // Wave w computes query head w % 4 of the group for the 32 queries of tile w / 4 and,
@@ -617,12 +617,13 @@ template <int KK, int KV>
 int launch_pf(const PrefillArgs& a, hipStream_t st)
 {
     // quantized splits and ring splits: one kernel each (their staging differs)
-    constexpr int NQ = (KK == KIND_BF16 || KV == KIND_BF16 || KK == KIND_KVARN1) ? 1 : 2;   // tiles per workgroup
+    constexpr int NQ = KK == KIND_KVARN1 ? 1 : 2;   // tiles per workgroup (quantized kernel; ring: 2)
     if (a.splits_q > 0)
         hipLaunchKernelGGL((k_prefill<KK, KV, false>), dim3(a.g.n_kv_heads * ((a.tiles + NQ - 1) / NQ) * a.splits_q),
                            dim3(256 * NQ), 0, st, a);
     if (a.splits_t > 0)
-        hipLaunchKernelGGL((k_prefill<KK, KV, true>), dim3(a.g.n_kv_heads * a.tiles * a.splits_t), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_prefill<KK, KV, true>), dim3(a.g.n_kv_heads * ((a.tiles + 1) / 2) * a.splits_t),
+                           dim3(512), 0, st, a);
     return (int)hipGetLastError();
 }
 
