@@ -356,7 +356,7 @@ int64_t kv_decode_workspace_bytes(const kv_cache* c, int32_t n_seqs)
 namespace {
 // Split plan of one prefill call: workgroups = KV heads x query tiles x key splits, about
 // two per CU; quantized and ring blocks never share a split.
-struct PfPlan { int32_t tiles, splits_q, splits_t, bps, splits_max; };
+struct PfPlan { int32_t tiles, splits_q, splits_t, bps, bps_t, splits_max; };
 PfPlan prefill_plan(const kv_cache* c, int64_t n, int64_t n_q, int32_t n_new)
 {
     PfPlan p;
@@ -367,8 +367,10 @@ PfPlan prefill_plan(const kv_cache* c, int64_t n, int64_t n_q, int32_t n_new)
     const int64_t splits = std::max<int64_t>(1, (target + per - 1) / per);
     p.bps = (int32_t)std::max<int64_t>(1, (nbq + nbt + splits - 1) / splits);
     p.splits_q = (int32_t)((nbq + p.bps - 1) / p.bps);
-    p.splits_t = (int32_t)((nbt + p.bps - 1) / p.bps);
-    p.splits_max = (int32_t)(splits + 2);
+    // the ring region (a few thousand tokens) is its own launch: spread it as widely
+    p.bps_t = (int32_t)std::max<int64_t>(1, (nbt + splits - 1) / splits);
+    p.splits_t = (int32_t)((nbt + p.bps_t - 1) / p.bps_t);
+    p.splits_max = (int32_t)(2 * splits + 2);
     return p;
 }
 }  // namespace
@@ -409,6 +411,8 @@ int kv_prefill_attn(kv_cache* c, int32_t layer, int32_t seq_id, int32_t n_new, c
     a.splits_q = p.splits_q;
     a.splits_t = p.splits_t;
     a.bps = p.bps;
+    a.bps_t = p.bps_t;
+    if (p.splits_q + p.splits_t > p.splits_max) return KV_EUNSUPPORTED;   // the workspace's bound
     a.q = q;
     a.out = out;
     a.partials = (float*)workspace;

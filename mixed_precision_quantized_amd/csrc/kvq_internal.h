@@ -136,8 +136,8 @@ struct PrefillArgs {
     float scale_log2;     // softmax_scale * log2(e)
     int32_t tiles;        // ceil(n_new / kPfQ)
     int32_t splits_q, splits_t;   // key splits over the quantized blocks / the ring blocks
-    int32_t bps;          // kPfKB-token blocks per split
-    int32_t pad_;
+    int32_t bps;          // kPfKB-token blocks per split of the quantized region
+    int32_t bps_t;        // the same for the ring region
     const void* q;        // [n_new][n_q_heads][128]
     float* out;           // [n_new][n_q_heads][128]
     float* partials;      // [n_kv_heads][tiles][splits][4][kPfQ][kD + 2]: m, l, acc

@@ -325,9 +325,10 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 
     // ---- key range of the split (32-token blocks of the quantized or the ring region) ------
     const int64_t r0 = quant ? 0 : a.n_q, r1 = quant ? a.n_q : a.n;
-    const int blk0 = (quant ? sp : sp - a.splits_q) * a.bps;
+    const int bps = RING ? a.bps_t : a.bps;
+    const int blk0 = (quant ? sp : sp - a.splits_q) * bps;
     const int nblk = (int)((r1 - r0 + kPfKB - 1) / kPfKB);
-    const int blk1 = min(blk0 + a.bps, nblk);
+    const int blk1 = min(blk0 + bps, nblk);
     // causal: no key after the workgroup's last query is seen
     const int blk_end = pos_max < r0 ? blk0 : (int)min<int64_t>(blk1, (pos_max - r0) / kPfKB + 1);
     const int nb = max(0, blk_end - blk0);
