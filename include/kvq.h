@@ -31,8 +31,11 @@
  *  are: block = 32 consecutive dims; qN_0 symmetric with an fp16 scale from the signed
  *  max-magnitude element; qN_1 affine (fp16 step and fp16 min); kvarnN = unnormalized
  *  Walsh-Hadamard rotation, 8 Sinkhorn iterations over a page of 128 tokens, fp16
- *  channel scales per page, then qN_0 on the normalized values; codes packed as a
- *  little-endian N-bit stream per token.
+ *  channel scales per page, then qN_0 on the normalized values; kvarnN_1 = the same
+ *  page normalization with qN_1 on the normalized values (the var-norm switch over an
+ *  affine base type: "Экспериментальные методы ...", section "Конфигурация KV-кэша:
+ *  примеры для типовых сценариев"); codes packed as a little-endian N-bit stream per
+ *  token.
  *
  * Conventions for every call:
  *  - Ownership: the library never allocates or frees device memory.  The cache buffer,
