@@ -169,6 +169,10 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
     run(gen)
     t_enc = run(enc)
     t_att = run(att)
+    # the same unit alone on one core (no other thread running)
+    t1 = time.perf_counter()
+    att(0)
+    t_one = time.perf_counter() - t1
     byts = units * decode_bytes_layer(fmt, ctx, n_q, 1)
     return {
         "value": round(byts / t_att / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
@@ -178,6 +182,8 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
         "seconds": round(t_att, 2),
         "append_tokens_per_s": round(units * ctx / (64 * 8) / t_enc, 1),
         "append_seconds": round(t_enc, 2),
+        "single_core": {"value": round(byts / units / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                        "sample": "one of the same units, alone", "seconds": round(t_one, 2)},
     }
 
 
