@@ -36,7 +36,7 @@ def _prefill_case(fmt, n, n_new, tail, H=2):
     wl = "c3_kvarn_ctx65536" if "kvarn" in fmt else "c2_sweep_ctx65536"
     cache = T.make_cache(fmt, 1, H, 4 * H, tail_tokens=tail, n_seqs=1, max_tokens=n)
     T.fill(cache, wl, 0, [0], H, n - n_new, T.chunk_list(n - n_new, [777, 1, 300]))
-    T.fill(cache, wl, 0, [0], H, n_new, T.chunk_list(n_new, [n_new // 3, 1]), t_start=n - n_new)
+    T.fill(cache, wl, 0, [0], H, n_new, T.chunk_list(n_new, [max(1, n_new // 3), 1]), t_start=n - n_new)
     qs = torch.stack([T.query(wl, 0, 0, step, 4 * H, "cuda") for step in range(n_new)], 0).contiguous()
     out = cache.prefill(0, 0, qs).cpu().numpy()
     n_, n_q = cache.seq_get(0, 0)
@@ -65,6 +65,16 @@ def test_prefill_matches_oracle(fmt, tail):
 
 def test_prefill_chunk_512_partial_tile():
     _prefill_case("kvarn4", 3000, 500, 1024)
+
+
+# shapes at the edges of the launch plan: every token in the ring (no quantized split), no
+# ring (no ring split), a one-token chunk (one tile, the other half of its pair empty), a
+# chunk that is the whole sequence, and three tiles (an odd count) over several pages
+@pytest.mark.parametrize("fmt,n,n_new,tail", [("kvarn4", 700, 160, 1024), ("q4_0", 700, 96, 0),
+                                              ("kvarn3/q4_1", 1300, 1, 200), ("q8_0", 257, 257, 64),
+                                              ("kvarn4_1", 900, 70, 0), ("bf16", 600, 33, 100)])
+def test_prefill_plan_edges(fmt, n, n_new, tail):
+    _prefill_case(fmt, n, n_new, tail)
 
 
 def test_prefill_full_size_sampled():
