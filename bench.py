@@ -296,7 +296,7 @@ def main():
         prefill_bench(args)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)." % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
