@@ -181,14 +181,17 @@ __device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part,
     }
 }
 
-// Unpack a raw block into the operand buffers.  Thread tid (0..255): token r = tid >> 3,
-// dims 16 (tid & 7) .. of the keys (PART 1), the values (PART 2) or both (PART 0).
+// Unpack a raw block into the operand buffers.  Thread tid (0..255): token r, dims 16 pp ..
+// of the keys (PART 1), the values (PART 2) or both (PART 0); r = tid >> 3, pp = tid & 7,
+// except for values alone (r = tid & 31, pp = tid >> 5).
 template <int KK, int KV, bool RING, bool BIG, int PART>
 __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const PrefillArgs& a, int nt, bool quant, int tid)
 {
     constexpr bool DK = PART != 2, DV = PART != 1;
     const CacheGeom& g = a.g;
-    const int r = tid >> 3, pp = tid & 7, b = pp >> 1;
+    // values alone: token-fastest threads, so that the dim-major value stores of a wave fall
+    // on consecutive halves of a row (16-way bank conflicts with dims-fastest threads)
+    const int r = PART == 2 ? (tid & 31) : (tid >> 3), pp = PART == 2 ? (tid >> 5) : (tid & 7), b = pp >> 1;
     const bool valid = r < nt;
     float kx[16], vx[16];
     float d = 1.0f, m = 0.0f;
