@@ -279,7 +279,7 @@ def prefill_bench(args):
     tf = flops / (ms * 1e-3) / 1e12
     print(json.dumps({"metric": "chunked-prefill attention, chunk tokens/s per layer", "value": round(c / (ms * 1e-3), 1),
                       "unit": "tokens/s", "ms_per_call": round(ms, 4), "higher_is_better": True, "data": "synthetic",
-                      "dtype": "f16 MFMA operands (exact codes, two-term query), f32 accumulate",
+                      "dtype": "f32", "operands": "f16 MFMA operands (exact codes, two-term query), f32 accumulate",
                       "config": {"workload": "1 layer x 8 KV heads x 32 q heads x d128, chunk %d at the end of %d "
                                              "tokens, %s, tail %d" % (c, n, args.fmt, args.tail)},
                       "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
@@ -399,7 +399,8 @@ def main():
         "metric": "decode-attn KV read GB/s (% of HBM peak) @240k ctx; append tokens/s",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 accumulate (i8 and f16 MFMA operands)", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f32", "operands": "i8 (scores) and f16 (values) MFMA operands, f32 accumulate",
+        "data": "synthetic",
         "config": {"workload": "decode step, 64 layers x 8 KV heads x 32 q heads x d128, ctx %d, %s, "
                                "BF16 tail %d, batch 1" % (args.ctx, args.fmt, args.tail),
                    "layers": L, "kv_heads": H, "q_heads": QH, "ctx": args.ctx, "fmt": args.fmt,
