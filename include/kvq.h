@@ -86,7 +86,9 @@ enum { KV_IN_BF16 = 0, KV_IN_F32 = 1 };
 typedef struct {
     int32_t n_layers;      /* >= 1 */
     int32_t n_kv_heads;    /* >= 1 */
-    int32_t n_q_heads;     /* multiple of n_kv_heads; n_q_heads / n_kv_heads <= 8 */
+    int32_t n_q_heads;     /* n_q_heads / n_kv_heads must be 4 (the decode, prefill and KL
+                            * kernels are built for GQA groups of 4; other groups return
+                            * KV_EUNSUPPORTED) */
     int32_t head_dim;      /* must be 128 */
     int32_t fmt_k, fmt_v;  /* kv_format of the key and value caches (may differ) */
     int32_t tail_tokens;   /* T: newest tokens kept at 16 bits (0 = quantize everything) */
@@ -121,12 +123,15 @@ int kv_cache_destroy(kv_cache* cache);
  * layer >= 0: k and v are [sum(n_new)][n_kv_heads][128] for that layer;
  * layer == -1: k and v are [n_layers][sum(n_new)][n_kv_heads][128] (all layers).
  * Tokens of sequence seq_ids[i] occupy rows [sum_{j<i} n_new[j], ...) in call order.
- * in_dtype: KV_IN_BF16 (bits copied) or KV_IN_F32 (rounded to bf16, nearest-even).
- * Every appended value is first made bf16; tokens that fall below the tail boundary
+ * in_dtype: KV_IN_BF16 or KV_IN_F32.  Every appended value is first made canonical: with a
+ * BF16 tail, bf16 input is copied and fp32 input rounded to bf16 (nearest even); with an
+ * F16 tail (tail_dtype), both are rounded to binary16 (nearest even, saturated to +-65504,
+ * zero as +0).  Tokens that fall below the tail boundary
  * n_q = max(n_q, G*floor(max(0, n-T)/G)) are encoded with the stream's format (G = 128
- * when a format is KVarN: whole pages, else 1), newer ones are written to the BF16 ring.
+ * when a format is KVarN: whole pages, else 1), newer ones are written to the 16-bit ring.
  * Errors: KV_EINVAL (bad layer/seq/ids/pointers/dtype), KV_ENOSPC (capacity), and with
- * layer == -1, KV_EINVAL if the layers of a sequence disagree on their token counts. */
+ * layer == -1, KV_EINVAL if the layers of a sequence disagree on their token counts;
+ * KV_EDEVICE if a launch fails. */
 int kv_append(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
               const int32_t* n_new, const void* k, const void* v, int32_t in_dtype,
               void* stream);
@@ -143,7 +148,9 @@ int64_t kv_decode_workspace_bytes(const kv_cache* cache, int32_t n_seqs);
  *   s_t = softmax_scale * q_h . k_t,  out_h = sum_t exp(s_t - max) v_t / sum_t exp(s_t - max)
  * over every token t < n of the sequence: dequantized rows t < n_q, BF16 ring rows after.
  * No mask and no positional transform (keys arrive position-encoded).  Reads the cache
- * only.  Errors: KV_EINVAL, KV_EEMPTY (a sequence with n == 0), KV_ESIZE (workspace). */
+ * only.  Errors: KV_EINVAL, KV_EEMPTY (a sequence with n == 0), KV_ESIZE (workspace),
+ * KV_EUNSUPPORTED (more than 32 sequences in one call, or a split plan above 8192
+ * workgroups), KV_EDEVICE (a launch failed or the device could not be queried). */
 int kv_decode_attn(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                    const void* q, int32_t q_dtype, float softmax_scale, float* out,
                    void* workspace, int64_t ws_bytes, void* stream);
