@@ -6,6 +6,10 @@
 // kernel reads every packed row once, coalesced, and dequantizes in registers.  It is not
 // a dense contraction at 4 query heads per KV head: no matrix cores.
 //
+// This binary32 kernel serves the pairs that hold a bf16 stream (bf16 keys, bf16 values or
+// both); every pair of quantized formats runs the matrix-core kernel of kvq_decode_ws.h.
+// Its dequantization also feeds the attention-KL harness at the end of this file.
+//
 // Work split (split-K flash decode): the tokens of each (sequence, KV head) are cut into
 // units (128-token quantized pages, 32-token ring chunks); every workgroup owns a run of
 // units of one kind, sized so the whole grid is resident at once.  Each wave keeps an
@@ -18,23 +22,10 @@
 // once, quantized values are accumulated in the rotated domain, and the merged quantized
 // accumulator is rotated back once at the end; ring tokens stay in the original domain.
 #include <float.h>
-#include <stdlib.h>
 
 #include "kvq_device.h"
 
 namespace kvq {
-
-// KVQ_DECODE_GENERIC=1 selects the generic kernel for every format (the fast 4-bit
-// kernel is otherwise used where it applies); read once per process.
-bool decode_generic_forced()
-{
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("KVQ_DECODE_GENERIC");
-        v = (e && e[0] == '1') ? 1 : 0;
-    }
-    return v == 1;
-}
 
 namespace {
 
@@ -364,10 +355,13 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
     }
 }
 
+// Pairs with a bf16 stream (every other pair runs the fast kernel, kvq_decode_ws.hip):
+// bf16 keys and values <0, 0>; bf16 keys with any value format, or quantized keys with bf16
+// values, <FK, -1> (the value format is switched per block at run time).
 template <int FMT>
 int launch_fmt(const DecodeArgs& a, int n_wgs, hipStream_t st)
 {
-    if (a.g.fmt_v == FMT) hipLaunchKernelGGL((k_decode<FMT, FMT>), dim3(n_wgs), dim3(256), 0, st, a);
+    if (FMT == 0 && a.g.fmt_v == 0) hipLaunchKernelGGL((k_decode<0, 0>), dim3(n_wgs), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((k_decode<FMT, -1>), dim3(n_wgs), dim3(256), 0, st, a);
     return (int)hipGetLastError();
 }
@@ -376,8 +370,8 @@ template <int FMT>
 int occ_fmt(bool mixed)
 {
     int n = 0;
-    hipError_t e = mixed ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT, -1>, 256, 0)
-                         : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT, FMT>, 256, 0);
+    hipError_t e = (FMT != 0 || mixed) ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<FMT, -1>, 256, 0)
+                                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<0, 0>, 256, 0);
     return e == hipSuccess ? n : 0;
 }
 
@@ -391,8 +385,7 @@ int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
 
 int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)
 {
-    if (decode_fast_supported(a.g.fmt_k, a.g.fmt_v) && !decode_generic_forced())
-        return launch_decode_fast(a, n_wgs, stream);
+    if (decode_fast_supported(a.g.fmt_k, a.g.fmt_v)) return launch_decode_fast(a, n_wgs, stream);
     hipStream_t st = (hipStream_t)stream;
     switch (a.g.fmt_k) {
     case 0: return launch_fmt<0>(a, n_wgs, st);
@@ -427,7 +420,7 @@ int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group)
 {
     (void)group;
-    if (decode_fast_supported(fmt_k, fmt_v) && !decode_generic_forced()) return decode_fast_wgs_per_cu(fmt_k, fmt_v);
+    if (decode_fast_supported(fmt_k, fmt_v)) return decode_fast_wgs_per_cu(fmt_k, fmt_v);
     static int cache[kNumFormats][2] = {{0}};
     if (fmt_k < 0 || fmt_k >= kNumFormats || fmt_v < 0 || fmt_v >= kNumFormats) return 0;
     const int mx = fmt_v != fmt_k ? 1 : 0;

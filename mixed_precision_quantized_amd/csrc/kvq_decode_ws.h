@@ -16,16 +16,20 @@
 // drift apart: the oldest wins instruction issue).  In each group of four waves the K
 // waves sit on SIMDs 0, 1 or 2, 3 alternately, so every SIMD runs both roles.
 //
-//  K: the query of each head is a 16-bit fixed-point vector per 32-dim block (scale
-//     S = max|q| / 32639) split into a low and a high signed byte; the scores of 16 tokens
-//     x 2 blocks are one v_mfma_i32_16x16x64_i8 whose rows are (head, block, byte) and
-//     whose other operand is the unpacked codes (one byte each, in an order fixed per code
-//     width that the query operand follows), so each lane scores one head of one token.  The integer dot products are exact; the accumulator starts at the code
-//     offset's share and the per-(token, block) scale applies afterwards.  Codes and
-//     scales go to registers, three steps in flight, through buffer loads that read rows
-//     past the end of a page as zero.
+//  K: the query of each head is a 31-bit fixed-point vector per 32-dim block (scale
+//     S ~ max|q| / (127 2^24)) written as four signed digit bytes; the scores of 16 tokens
+//     x 2 blocks are two v_mfma_i32_16x16x64_i8 (digits 0-1 and 2-3) whose rows are (head,
+//     block, digit) and whose other operand is the unpacked codes (one byte each, in an
+//     order fixed per code width that the query operand follows), so each lane scores one
+//     head of one token.  The integer dot products are exact; the two 32-bit parts meet
+//     in binary32, the code offset's share (o S sum(q_int)) is subtracted there, and the
+//     per-(token, block) scale applies afterwards.  Codes and scales go to registers,
+//     three steps in flight, through buffer loads that read rows past the end of a page
+//     as zero.
 //  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
-//     the binary16 weights p*d of the four heads, B = the centred codes 2^s (u - o) of one
+//     the binary16 weights (2^15 p)(d 2^e) of the four heads (2^e a power of two per lane
+//     quad that keeps every weight between 2^12 and far above the binary16 subnormals),
+//     B = the centred codes 2^s (u - o) of one
 //     dim per column as exact binary16 integers (v_perm interleaves the bytes of a token
 //     pair; masking a code in place at bit offset s and or-ing 0x6400 gives 1024 + 2^s u,
 //     one v_pk_add_f16 centres two codes; 2^-s is applied once at the end), K = the four
@@ -53,8 +57,9 @@ namespace {
 
 constexpr int kG = 4;
 constexpr float kNeg = -1.0e30f;
-constexpr float kQLim = 32639.0f;        // |q_int| bound: q_int + 128 fits a signed 16-bit word
+constexpr float kQLim = 2130706432.0f;   // |q_int| bound 127 * 2^24: four balanced base-256 digits
 constexpr int kP = 8;                    // (K wave, V wave) pairs per workgroup
+constexpr float kPScale = 32768.0f;      // binary16 probabilities are stored as 2^15 p (p <= 1)
 constexpr int kThreads = 128 * kP;       // one workgroup per CU
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -234,13 +239,14 @@ struct alignas(16) PBuf {
     float pad[4];
 };
 
-// Query operand of the score MFMA for one pair: 16-bit fixed-point query per (head, 32-dim
-// block) split into a low and a high signed byte, q_int = 256 hi + lo, the dims of every
-// 8-dim group stored even dims first (the order in which the code nibbles unpack).
+// Query operand of the score MFMA for one pair: 31-bit fixed-point query per (head, 32-dim
+// block) as four balanced base-256 digits, q_int = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3 with every
+// d in [-128, 127], in the dim order in which the codes of each width unpack.
 struct alignas(16) QMat {
-    int8_t qa[2][kG][kD];    // [byte: lo, hi][head][permuted dim]
+    int8_t qa[4][kG][kD];    // [digit][head][permuted dim]
     float S[kG][4];          // [head][block] scale of q_int
-    int off[kG][4];          // [head][block] sum of q_int
+    float qsum[kG][4];       // [head][block] S * sum(q_int)
+    int sum[kG][4][2];       // [head][block] sums of the low (d0 + 2^8 d1) and high (d2 + 2^8 d3) parts
 };
 
 // The value accumulators a pair leaves at its end (wacc) live in the pair's own ring, which
@@ -248,10 +254,14 @@ struct alignas(16) QMat {
 template <int NV>
 struct alignas(16) WsLds {
     static constexpr int KS = ring_depth<NV>();
-    float qs[kG][kD];
+    union {
+        float qs[kG][kD];    // the query of a ring workgroup
+        QMat qm[kP];         // the score operand of each pair (quantized workgroups; KVarN
+                             // rebuilds it two steps before each page, once the current
+                             // page's operand is in registers)
+    };
     Stage<NV> st[kP][KS];    // LDS rings of the value waves
     PBuf pb[kP][KS];         // [pair][step % KS]
-    QMat qm[kP][2];          // [pair][page parity] (KVarN builds the next page's ahead)
     float wm[kP][kG], wl[kP][kG];
     __device__ float* wacc(int p) { return reinterpret_cast<float*>(&st[p][0]); }   // [kG][kD]
 };
@@ -411,11 +421,11 @@ __device__ __forceinline__ i32x4 unpack_k(const uint32_t (&w)[kwin_dwords<N>()],
 // 8-dim group g8 (lane & 15); the four lanes of a quad hold one 32-dim block.  q: the lane's
 // 8 query values; cw: the 8 key channel scales of the group (KVarN) or null.  The digits
 // of element e of a half-block go to byte kpos<N>(e) of that half's 16 bytes.
-//   q_int = round(q * inv), inv = 32639 / max|q| of the block, |q_int| <= 32639; one fma
-//   with 1.5 * 2^23 + 128 leaves q_int + 128 in the low 16 bits of the result (the sum
-//   stays in [2^23, 2^24), where the float spacing is 1).  Its high byte is the signed high
-//   digit h8 and its low byte l8 + 128, so q_int = 256 h8 + l8 with l8 in [-128, 127]
-//   (flipping bit 7 of the low byte gives l8).
+//   q_int = rint(q * inv), inv = 127 * 2^24 / max|q| of the block; its balanced base-256
+//   digits: d0 = the low byte of q_int, x1 = (q_int + 128) >> 8, d1 = the low byte of x1,
+//   x2 = (x1 + 128) >> 8, and so on (arithmetic shifts), each digit in [-128, 127].  A
+//   31-bit range keeps elements far below the block maximum (a key channel scale spread of
+//   2^20 in a block, or a query outlier 1000x its block) with 8 or more significant bits.
 template <int N>
 __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const uint4* cw, int lane)
 {
@@ -432,47 +442,46 @@ __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const u
     amax = fmaxf(fmaxf(amax, fabsf(v[3])), fabsf(v[4]));
     amax = fmaxf(fmaxf(amax, fabsf(v[5])), fabsf(v[6]));
     amax = quad_max(fmaxf(amax, fabsf(v[7])));
-    const float inv = amax > 0.0f ? kQLim * __builtin_amdgcn_rcpf(amax) : 0.0f;
-    uint32_t qb[8];
-    uint32_t bsum = 0u;
+    // inv * amax <= 127 * 2^24 up to the rounding of the reciprocal: the bound is met with a
+    // margin of 2^-7 (the top digit then stays within [-128, 127])
+    const float inv = amax > 0.0f ? (kQLim * 0.9921875f) * __builtin_amdgcn_rcpf(amax) : 0.0f;
+    // N = 4, 8: the lane's 8 elements fill 8 consecutive bytes per digit ((even | odd)
+    // elements for N = 4, in order for N = 8), packed as they are made; other widths spread
+    // the positions over the half-block, one byte store per digit
+    uint32_t w[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+    int slo = 0, shi = 0;               // sums of the low and high 16-bit parts
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        qb[e] = __float_as_uint(fmaf(v[e], inv, 12583040.0f));      // 1.5 * 2^23 + 128
-        bsum += qb[e];
-    }
-    int isum = (int)(bsum - 8u * 0x4B400080u);                        // sum of q_int
-    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR1, 0xF, 0xF, false);
-    isum += __builtin_amdgcn_mov_dpp(isum, QP_XOR2, 0xF, 0xF, false);
-    // bytes (0, 1) of elements (a, b) -> [a.0, b.0, a.1, b.1]
-    auto pair = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05010400u); };
-    if constexpr (N == 4 || N == 8) {
-        // the lane's 8 elements fill 8 consecutive bytes: (even | odd) elements for N = 4,
-        // in order for N = 8
-        const uint32_t ta = N == 4 ? pair(qb[0], qb[2]) : pair(qb[0], qb[1]);
-        const uint32_t tb = N == 4 ? pair(qb[4], qb[6]) : pair(qb[2], qb[3]);
-        const uint32_t tc = N == 4 ? pair(qb[1], qb[3]) : pair(qb[4], qb[5]);
-        const uint32_t td = N == 4 ? pair(qb[5], qb[7]) : pair(qb[6], qb[7]);
-        const uint32_t lo0 = __builtin_amdgcn_perm(tb, ta, 0x05040100u) ^ 0x80808080u;
-        const uint32_t lo1 = __builtin_amdgcn_perm(td, tc, 0x05040100u) ^ 0x80808080u;
-        const uint32_t hi0 = __builtin_amdgcn_perm(tb, ta, 0x07060302u);
-        const uint32_t hi1 = __builtin_amdgcn_perm(td, tc, 0x07060302u);
-        *(uint2*)&Q.qa[0][h][8 * g8] = make_uint2(lo0, lo1);
-        *(uint2*)&Q.qa[1][h][8 * g8] = make_uint2(hi0, hi1);
-    } else {
-        // positions spread over the half-block: one byte store per digit
-        uint8_t* b0 = (uint8_t*)&Q.qa[0][h][16 * (g8 >> 1)];
-        uint8_t* b1 = (uint8_t*)&Q.qa[1][h][16 * (g8 >> 1)];
-        const bool odd = g8 & 1;
+        const int x = (int)__builtin_rintf(v[e] * inv);
+        const int x1 = (x + 128) >> 8, x2 = (x1 + 128) >> 8, x3 = (x2 + 128) >> 8;
+        const int dig[4] = {x, x1, x2, x3};
+        slo += x - (x2 << 16);
+        shi += x2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int p = odd ? kpos<N>(8 + e) : kpos<N>(e);
-            b0[p] = (uint8_t)(qb[e] ^ 0x80u);
-            b1[p] = (uint8_t)(qb[e] >> 8);
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (N == 4 || N == 8) {
+                const int wi = N == 4 ? (e & 1) : (e >> 2), bi = N == 4 ? (e >> 1) : (e & 3);
+                w[k][wi] |= ((uint32_t)dig[k] & 0xFFu) << (8 * bi);
+            } else {
+                uint8_t* bk = (uint8_t*)&Q.qa[k][h][16 * (g8 >> 1)];
+                bk[(g8 & 1) ? kpos<N>(8 + e) : kpos<N>(e)] = (uint8_t)dig[k];
+            }
         }
     }
+    if constexpr (N == 4 || N == 8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *(uint2*)&Q.qa[k][h][8 * g8] = make_uint2(w[k][0], w[k][1]);
+    }
+    slo += __builtin_amdgcn_mov_dpp(slo, QP_XOR1, 0xF, 0xF, false);
+    slo += __builtin_amdgcn_mov_dpp(slo, QP_XOR2, 0xF, 0xF, false);
+    shi += __builtin_amdgcn_mov_dpp(shi, QP_XOR1, 0xF, 0xF, false);
+    shi += __builtin_amdgcn_mov_dpp(shi, QP_XOR2, 0xF, 0xF, false);
     if ((g8 & 3) == 0) {
-        Q.S[h][kb] = amax * (1.0f / kQLim);
-        Q.off[h][kb] = isum;
+        const float S = amax * (1.0f / (kQLim * 0.9921875f));
+        Q.S[h][kb] = S;
+        Q.qsum[h][kb] = S * fmaf((float)shi, 65536.0f, (float)slo);
+        Q.sum[h][kb][0] = slo;
+        Q.sum[h][kb][1] = shi;
     }
 }
 
@@ -610,16 +619,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         const char* kcodes = kst + g.k.codes;
         const char* kscales = kst + g.k.scales;
         const char* kchan = kst + g.k.cscale;
-        QMat* Qb = S.qm[pr];
-        i32x4 A[2], Ci[2];
-        float Sc[4], Qs[4];
+        QMat& Qb = S.qm[pr];
+        // A[bp] / A2[bp]: digits (0, 1) / (2, 3) of the rows.  The code offset o: for block
+        // formats a binary32 term -o S sum(q_int) per block (Qo); for KVarN keys, whose query
+        // operand carries the channel scales (elements up to 10^4 or more beside small
+        // centred codes, where that term would cancel), exactly in the integer sums: the low
+        // part's share in the accumulator (Ci), the high part's subtracted before the parts
+        // meet (Oh).  The affine minimum enters as S sum(q_int) (Qs) times the block's m.
+        i32x4 A[2], A2[2];
+        float Sc[4], Qs[4], Qo[4];
+        i32x4 Ci[KVARN_K ? 2 : 1];
+        int Oh[KVARN_K ? 2 : 1][2];
         auto load_a = [&](const QMat& Q) {
             const int m = n16, dig = m & 1, sel = (m >> 1) & 1, h = m >> 2;
 #pragma unroll
             for (int bp = 0; bp < 2; ++bp) {
                 const i32x4 z = {0, 0, 0, 0};
-                A[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[dig][h][32 * (2 * bp + sel) + 16 * (q4 & 1)] : z;
-                Ci[bp] = OFF_K == 0 ? z : (i32x4){-OFF_K * Q.off[q4][2 * bp], 0, -OFF_K * Q.off[q4][2 * bp + 1], 0};
+                const int o = 32 * (2 * bp + sel) + 16 * (q4 & 1);
+                A[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[dig][h][o] : z;
+                A2[bp] = sel == (q4 >> 1) ? *(const i32x4*)&Q.qa[2 + dig][h][o] : z;
+                if constexpr (KVARN_K) {
+                    Ci[bp] = (i32x4){-OFF_K * Q.sum[q4][2 * bp][0], 0, -OFF_K * Q.sum[q4][2 * bp + 1][0], 0};
+                    Oh[bp][0] = OFF_K * Q.sum[q4][2 * bp][1];
+                    Oh[bp][1] = OFF_K * Q.sum[q4][2 * bp + 1][1];
+                }
             }
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -628,7 +651,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 // is the rounded query against the dequantized key, d u + m, exactly; its
                 // error is then sum((q - q_hat) k), small where a block holds one outlier
                 // channel (the other keys are near 0, while d u - 8 d or d u are not)
-                Qs[b] = AFF_K ? Q.S[q4][b] * (float)Q.off[q4][b] : 0.0f;
+                Qs[b] = AFF_K ? Q.qsum[q4][b] : 0.0f;
+                Qo[b] = KVARN_K ? 0.0f : (float)(-OFF_K) * Q.qsum[q4][b];
             }
         };
         // Codes and scales of one step, straight to registers through buffer loads whose
@@ -682,7 +706,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         uint4 cfirst = make_uint4(0u, 0u, 0u, 0u);
         // three register stages, loads issued two steps ahead of their use
         // KR register stages (two where three would not fit in the registers: wide KVarN keys)
-        constexpr int KR = (KVARN_K && NK >= 5) ? 2 : 3;
+        constexpr int KR = KVARN_K ? 2 : 3;
         KLoad X, Y, Z;
         if (J > 0) {
             if (KVARN_K) cfirst = chan_load(0);        // first, so that its wait is exact
@@ -735,14 +759,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             }
         }
         if (!KVARN_K) {
-            build_qmat<NK>(Qb[0], qv, nullptr, lane);
+            build_qmat<NK>(Qb, qv, nullptr, lane);
             wave_sync_lds();
-            load_a(Qb[0]);
+            load_a(Qb);
         } else if (J > 0) {
-            // first page now; each later page's operand is built two steps before it starts
-            build_qmat<NK>(Qb[0], qv, &cfirst, lane);
+            // first page now; each later page's operand is built two steps before it starts,
+            // over the current page's, which is in registers by then (a wave's LDS accesses
+            // complete in order)
+            build_qmat<NK>(Qb, qv, &cfirst, lane);
             wave_sync_lds();
-            load_a(Qb[0]);
+            load_a(Qb);
         }
         // slot: the probability buffer of step j, j % KS
         auto kstep = [&](int j, const KLoad& L, int slot) __attribute__((always_inline)) {
@@ -751,11 +777,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             const int t_end = min(t_page + kPage, nq);
             if (KVARN_K && (j & 3) == 0 && j > 0) {
                 wave_sync_lds();
-                load_a(Qb[(j >> 2) & 1]);
+                load_a(Qb);
             }
             if (KVARN_K && (j & 3) == 2) {
                 // the next page's operand into the other buffer (read at that page's start)
-                build_qmat<NK>(Qb[((j >> 2) + 1) & 1], qv, &L.ch, lane);
+                build_qmat<NK>(Qb, qv, &L.ch, lane);
             }
             float sc[2];
 #pragma unroll
@@ -764,21 +790,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 #pragma unroll
                 for (int bp = 0; bp < 2; ++bp) {
                     const i32x4 Bm = unpack_k<NK>(L.c[T][bp], ks);
-                    const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, Ci[bp], 0, 0, 0);
-                    const int t0 = (C.y << 8) + C.x, t1 = (C.w << 8) + C.z;
+                    const i32x4 z4 = {0, 0, 0, 0};
+                    // integer dot of each block, sum(q_int (u - o)): the low (digits 0, 1) and
+                    // high (digits 2, 3) parts are exact in 32 bits and meet in binary32
+                    float t0, t1;
+                    if constexpr (KVARN_K) {
+                        const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, Ci[bp], 0, 0, 0);
+                        const i32x4 C2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A2[bp], Bm, z4, 0, 0, 0);
+                        t0 = fmaf((float)((C2.y << 8) + C2.x - Oh[bp][0]), 65536.0f, (float)((C.y << 8) + C.x)) * Sc[2 * bp];
+                        t1 = fmaf((float)((C2.w << 8) + C2.z - Oh[bp][1]), 65536.0f, (float)((C.w << 8) + C.z)) * Sc[2 * bp + 1];
+                    } else {
+                        const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[bp], Bm, z4, 0, 0, 0);
+                        const i32x4 C2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A2[bp], Bm, z4, 0, 0, 0);
+                        t0 = fmaf(fmaf((float)((C2.y << 8) + C2.x), 65536.0f, (float)((C.y << 8) + C.x)), Sc[2 * bp], Qo[2 * bp]);
+                        t1 = fmaf(fmaf((float)((C2.w << 8) + C2.z), 65536.0f, (float)((C.w << 8) + C.z)), Sc[2 * bp + 1], Qo[2 * bp + 1]);
+                    }
                     // block scales as binary16 operands of v_fma_mix (no conversion)
                     uint32_t w0, w1;
                     if (AFF_K) {
                         w0 = bp ? L.s[T].z : L.s[T].x;
                         w1 = bp ? L.s[T].w : L.s[T].y;
-                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
-                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)lo_half(w1), acc);
+                        acc = fmaf(t0, (float)lo_half(w0), acc);
+                        acc = fmaf(t1, (float)lo_half(w1), acc);
                         acc = fmaf(Qs[2 * bp], (float)hi_half(w0), acc);
                         acc = fmaf(Qs[2 * bp + 1], (float)hi_half(w1), acc);
                     } else {
                         w0 = bp ? L.s[T].y : L.s[T].x;
-                        acc = fmaf((float)t0 * Sc[2 * bp], (float)lo_half(w0), acc);
-                        acc = fmaf((float)t1 * Sc[2 * bp + 1], (float)hi_half(w0), acc);
+                        acc = fmaf(t0, (float)lo_half(w0), acc);
+                        acc = fmaf(t1, (float)hi_half(w0), acc);
                     }
                 }
                 sc[T] = acc;
@@ -802,8 +841,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             const float p1 = __builtin_amdgcn_exp2f(sc[1] - mh);
             ls = fmaf(ls, al, p0 + p1);
             PBuf& P = S.pb[pr][slot];
-            P.ph[q4][n16] = (_Float16)p0;
-            P.ph[q4][16 + n16] = (_Float16)p1;
+            P.ph[q4][n16] = (_Float16)(p0 * kPScale);
+            P.ph[q4][16 + n16] = (_Float16)(p1 * kPScale);
             if (n16 == 0) P.alpha[q4] = al;
             __syncthreads();
         };
@@ -940,6 +979,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         float cvr[8];                 // c_V of the lane's dims on the current page (KVarN)
 #pragma unroll
         for (int r = 0; r < 8; ++r) cvr[r] = 1.0f;
+        // Value-weight exponent of the wave: the weights enter the MFMA as binary16
+        // (2^15 p) * (d 2^ve), with d 2^ve < 2^-3 for every block scale the wave has seen, so
+        // a weight stays below 2^12 and far above the binary16 subnormals whatever the
+        // magnitude of the values.  ve starts at 15 and only decreases: when a step brings a
+        // larger scale, ve drops so that the largest scale sits in [2^-5, 2^-4) and the
+        // accumulator (binary32) is rescaled by the exact power of two.  ve is uniform over
+        // the wave (scalar registers).
+        int ve = 15;
         // 0x64006400 kept in a register so that the mask-and-or is one v_and_or_b32
         uint32_t k6400 = 0x64006400u;
         asm volatile("" : "+v"(k6400));
@@ -997,7 +1044,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 // kvarnN_1 values: the minima summed so far carry the previous page's channel
                 // scales, so they join the accumulator (at its 2^s' code scale) before it moves
                 // to this page's; the lane's partial sums, like its accumulator's
-                const float mo = fmaf((float)(1 << (NV - 1)), msd, ms);
+                // (the sums carry the 2^15 of the probabilities, the accumulator also 2^ve)
+                const float mo = fmaf((float)(1 << (NV - 1)), msd, ms) * __builtin_ldexpf(1.0f, ve);
                 const f32x4 m4 = {quad_bcast(mo, 0), quad_bcast(mo, 1), quad_bcast(mo, 2), quad_bcast(mo, 3)};
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
@@ -1019,23 +1067,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     cvr[r] = cn;
                 }
             }
+            // the step's block scales (two token pairs per half), gathered by 16-bit LDS loads
+            const _Float16* sc16 = (const _Float16*)B.scales;
+            constexpr int SW = SB_V / 2;                       // binary16 words per scale row
+            const int so = (AFF_V ? 2 : 1) * vblk;
+            auto dpair = [&](int hf, int i) __attribute__((always_inline)) -> half2_t {
+                const int sx = 8 * hf + tg + 4 * i;
+                return (half2_t){sc16[SW * (2 * sx) + so], sc16[SW * (2 * sx + 1) + so]};
+            };
+            {
+                // a scale of the step at or above 2^(-3 - ve): lower ve for the whole wave
+                const u16x2 m = {0x7FFF, 0x7FFF};
+                u16x2 r = __builtin_bit_cast(u16x2, dpair(0, 0)) & m;
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(0, 1)) & m);
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(1, 0)) & m);
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(1, 1)) & m);
+                const uint32_t dm = r.x > r.y ? r.x : r.y;  // binary16 bits of the largest |d|
+                const uint32_t lim = (uint32_t)max(0, 12 - ve) << 10;     // 2^(-3 - ve)
+                if (__builtin_amdgcn_ballot_w64(dm >= lim)) {
+                    // the wave's largest scale in [2^e, 2^(e+1)) (binary16 subnormals: e = -14
+                    // bounds them); ve puts it in [2^-5, 2^-4)
+                    uint32_t wm = dm;
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) wm = max(wm, (uint32_t)__shfl_xor((int)wm, o));
+                    const int ef = (int)(__builtin_amdgcn_readfirstlane(wm) >> 10);
+                    const int nve = max(-24, -5 - ((ef == 0 ? 1 : ef) - 15));
+                    const float f = __builtin_ldexpf(1.0f, nve - ve);
+#pragma unroll
+                    for (int r2 = 0; r2 < 8; ++r2) D[r2] *= f;
+                    ve = nve;
+                }
+            }
+            asm volatile("" ::: "memory");                   // reload the scales below (registers)
+            const uint32_t vh = ve >= -14 ? (uint32_t)(ve + 15) << 10 : 1u << (ve + 24);
+            const half2_t vsc = __builtin_bit_cast(half2_t, vh | (vh << 16));   // {2^ve, 2^ve}
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int s0 = 8 * hf + tg, s1 = s0 + 4;
                 const VRun x0 = vrun(B.codes, s0), x1 = vrun(B.codes, 16 + s0);
                 const VRun x2 = vrun(B.codes, s1), x3 = vrun(B.codes, 16 + s1);
-                // A: binary16 p (written by the K wave) times the binary16 block scales, two
-                // tokens per packed multiply; the scale pairs are gathered by 16-bit LDS loads
+                // A: binary16 2^15 p (written by the K wave) times the scaled binary16 block
+                // scales, two tokens per packed multiply
                 const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
                 const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
-                const _Float16* sc16 = (const _Float16*)B.scales;
-                constexpr int SW = SB_V / 2;                   // binary16 words per scale row
-                const int so = (AFF_V ? 2 : 1) * vblk;
-                const half2_t d01 = {sc16[SW * (2 * s0) + so], sc16[SW * (2 * s0 + 1) + so]};
-                const half2_t d23 = {sc16[SW * (2 * s1) + so], sc16[SW * (2 * s1 + 1) + so]};
-                const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * d01);
-                const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * d23);
+                const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * (dpair(hf, 0) * vsc));
+                const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * (dpair(hf, 1) * vsc));
                 if (AFF_V) {
+                    const half2_t d01 = dpair(hf, 0), d23 = dpair(hf, 1);
                     const half2_t m01 = {sc16[SW * (2 * s0) + so + 1], sc16[SW * (2 * s0 + 1) + so + 1]};
                     const half2_t m23 = {sc16[SW * (2 * s1) + so + 1], sc16[SW * (2 * s1 + 1) + so + 1]};
                     msd = __builtin_amdgcn_fdot2(p01, d01, msd, false);
@@ -1068,17 +1146,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             if (j < J) { vstep(j, i); ++j; }
 #pragma unroll 1
         for (++j; j <= Jmax; ++j) __syncthreads();
-        // sum the four token groups (lanes l ^ 16, l ^ 32); offsets of all heads of the block
+        // sum the four token groups (lanes l ^ 16, l ^ 32), each first freed of its own weight
+        // scale 2^(15 + ve); offsets of all heads of the block
+        const float unscale = __builtin_ldexpf(1.0f, -15 - ve);
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                float x = D[r][c];
+                float x = D[r][c] * unscale;
                 x += __shfl_xor(x, 16);
                 x += __shfl_xor(x, 32);
                 D[r][c] = x;
             }
-        ms = fmaf((float)(1 << (NV - 1)), msd, ms);       // sum of p (m + o d)
+        ms = fmaf((float)(1 << (NV - 1)), msd, ms) * (1.0f / kPScale);    // sum of p (m + o d)
         ms += __shfl_xor(ms, 16);
         ms += __shfl_xor(ms, 32);
         const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};

@@ -160,7 +160,6 @@ int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of t
 bool decode_fast_supported(int fmt_k, int fmt_v);
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream);
 int decode_fast_wgs_per_cu(int fmt_k, int fmt_v);
-bool decode_generic_forced();
 int device_cu_count();
 
 }  // namespace kvq

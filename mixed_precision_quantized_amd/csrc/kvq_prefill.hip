@@ -19,10 +19,18 @@
 // integers, exact in binary16); the block scale d of each (token, block) is applied to the
 // binary32 product of that block's 32 dims, and the affine minimum m as m * sum(q) of the
 // block, so the keys are used exactly.  (Rounding dequantized keys to binary16 would not do:
-// keys with 15x outlier channels reach |k| ~ 800, where binary16 keeps 0.25 absolute.)  The
-// query enters as two binary16 terms, q = hi + lo, one MFMA each: one rounding of q alone
-// cost up to 1.9e-3 of the output on the 64k block-format workload.  Values are dequantized to binary16 (|v| is small) and the
-// probabilities are rounded to binary16 before the P V product.
+// keys with 15x outlier channels reach |k| ~ 800, where binary16 keeps 0.25 absolute.)
+// 16-bit key rows (ring, bf16 format) enter as k 2^-s with the power of two s per (token,
+// block) that puts the block's largest |k| in [2^14, 2^15), and d = 2^s: exact for every
+// bf16 value of the block down to 2^-24 of its maximum, beyond binary16's range included.
+// The query enters as two binary16 terms, q 2^-sq = hi + lo, one MFMA each (sq per query,
+// its largest |q| in [2^7, 2^8); the scores are scaled back by 2^sq): one rounding of q
+// alone cost up to 1.9e-3 of the output on the 64k block-format workload.  Values enter as
+// binary16 v 2^sv, with one sv per workgroup taken from a bound on |v| over its split (read
+// from the block scales and channel scales, or from the 16-bit rows, before the loop) so
+// that |v 2^sv| < 2^15; the probabilities as binary16 2^15 p.  Neither then overflows, and
+// neither loses small values to the binary16 subnormals, whatever the values' magnitude;
+// the split's accumulator is scaled back by 2^-(15 + sv).
 //
 // KVarN (either inner quantizer): keys are scored in the rotated domain against
 // q' = H q / 128.  The page's key channel scale goes to the key side: c (u - o) is exact in
@@ -185,7 +193,8 @@ __device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part,
 // of the keys (PART 1), the values (PART 2) or both (PART 0); r = tid >> 3, pp = tid & 7,
 // except for values alone (r = tid & 31, pp = tid >> 5).
 template <int KK, int KV, bool RING, bool BIG, int PART>
-__device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const PrefillArgs& a, int nt, bool quant, int tid)
+__device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const PrefillArgs& a, int nt, bool quant, int tid,
+                                          float vmul)
 {
     constexpr bool DK = PART != 2, DV = PART != 1;
     const CacheGeom& g = a.g;
@@ -225,6 +234,19 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             kx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
             kx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
+        // the block's largest |k| (its other half is in the neighbouring lane) to [2^14, 2^15)
+        float amax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(kx[e]));
+        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+        if (amax > 0.0f) {
+            const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+            const int sh = min(126, max(-126, (ex == 0 ? 1 : ex) - 127 - 14));
+            const float f = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) kx[e] *= f;
+            d = __builtin_ldexpf(1.0f, sh);
+        }
     }
     if (!DV) {
     } else if (quant && KV != KIND_BF16) {
@@ -255,6 +277,10 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             vx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
             vx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
+    }
+    if (DV) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vx[e] *= vmul;
     }
     if (!valid) {
 #pragma unroll
@@ -309,6 +335,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
     // unpacked while block i is computed; one barrier per block.
     __shared__ PfLds L[2];
     __shared__ PfRawL<BIG> RW[2];
+    __shared__ float vbnd[2][4 * NT];      // per wave: bound of |v| over the split, and of |c_V|
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = a.splits_q + a.splits_t;
@@ -347,7 +374,8 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
     constexpr bool kv_k = kind_paged(KK) && !RING;
 
     // ---- query: the lane's 64 dims {16 idx + 8 hh + c}, log2 domain, as hi + lo binary16 ----
-    h8 qb[8], ql[8];                 // the query operand (paged keys: H q / 128) = qb + ql
+    h8 qb[8], ql[8];                 // the query operand (paged keys: H q / 128) = (qb + ql) qmul
+    float qmul = 1.0f;
     {
         float qf[8][8];
         const int64_t base = ((int64_t)(qvalid ? qi : 0) * g.n_q_heads + head * kG + h) * kD;
@@ -390,6 +418,23 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
                     const float y = __shfl_xor(qf[idx][c], 32);
                     qf[idx][c] = (hh ? y - qf[idx][c] : qf[idx][c] + y) * (1.0f / 128.0f);
                 }
+        }
+        // power of two of the query: its largest |q| (over the lane pair) to [2^7, 2^8)
+        float amax = 0.0f;
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(qf[idx][c]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        if (amax > 0.0f) {
+            const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+            const int sq = min(126, max(-126, (ex == 0 ? 1 : ex) - 127 - 7));
+            const float f = __builtin_ldexpf(1.0f, -sq);
+            qmul = __builtin_ldexpf(1.0f, sq);
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) qf[idx][c] *= f;
         }
 #pragma unroll
         for (int idx = 0; idx < 8; ++idx)
@@ -446,7 +491,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
         f32x16 Sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) Sacc[r] = 0.0f;
-        const bool scaled = quant && KK != KIND_BF16;
+        constexpr bool aff_k = !RING && kind_affine(KK);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             f32x16 T;
@@ -464,25 +509,22 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
                     T = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, qb[idx], T, 0, 0, 0);
                 }
             }
-            if (scaled) {
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 dd = *(const float4*)&B.dk[b][8 * r4 + 4 * hh];
-                    const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 dd = *(const float4*)&B.dk[b][8 * r4 + 4 * hh];
+                const float dv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(dv[c], T[4 * r4 + c], Sacc[4 * r4 + c]);
-                    if (kind_affine(KK)) {
-                        const float4 mm = *(const float4*)&B.mk[b][8 * r4 + 4 * hh];
-                        const float mv[4] = {mm.x, mm.y, mm.z, mm.w};
+                for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(dv[c], T[4 * r4 + c], Sacc[4 * r4 + c]);
+                if (aff_k) {
+                    const float4 mm = *(const float4*)&B.mk[b][8 * r4 + 4 * hh];
+                    const float mv[4] = {mm.x, mm.y, mm.z, mm.w};
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(mv[c], qsum[b], Sacc[4 * r4 + c]);
-                    }
+                    for (int c = 0; c < 4; ++c) Sacc[4 * r4 + c] = fmaf(mv[c], qsum[b], Sacc[4 * r4 + c]);
                 }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Sacc[r] += T[r];
             }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Sacc[r] *= qmul;
         // mask: rows past the block's end, and keys later than the query (only blocks that
         // reach the tile's first query or end early need it; unused query slots are never
         // read back)
@@ -522,7 +564,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) pb[k2][c] = (_Float16)p[8 * k2 + c];
+            for (int c = 0; c < 8; ++c) pb[k2][c] = (_Float16)(p[8 * k2 + c] * 32768.0f);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -537,13 +579,87 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
     const PfStream SK = pf_stream_rsrc(a, kst, g.k, g.fmt_k, quant), SV = pf_stream_rsrc(a, vst, g.v, g.fmt_v, quant);
     if (nb > 0) pf_dma<KK, KV, RING, BIG, 4 * NT>(RW[0], a, SK, SV, tb_of(0), nt_of(0), wave, lane);
     if (nb > 1) pf_dma<KK, KV, RING, BIG, 4 * NT>(RW[1], a, SK, SV, tb_of(1), nt_of(1), wave, lane);
+    // ---- a bound on |v| over the split's value rows, read while the first blocks load ------
+    // quantized: |d| 2^(N-1) (symmetric) or |d| (2^N - 1) + |m| (affine) per (token, block),
+    // times the largest |c_V| of the split's pages; 16-bit rows: their largest |v|
+    {
+        float vb = 0.0f, cb = 0.0f;
+        if (nb > 0) {
+            const int64_t t0 = tb_of(0), t1 = tb_of(nb - 1) + nt_of(nb - 1);
+            const int nthr = 256 * NT;
+            if (quant && KV != KIND_BF16) {
+                const int N = fbits(g.fmt_v);
+                const char* vsc = vst + g.v.scales;
+                if (kind_affine(KV)) {
+                    const float top = (float)((1 << N) - 1);
+                    for (int64_t t = t0 + tid; t < t1; t += nthr) {
+                        const uint4 w = *(const uint4*)(vsc + t * 16);
+                        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            vb = fmaxf(vb, fmaf(fabsf(fp16_to_f32(ww[i] & 0xFFFFu)), top, fabsf(fp16_to_f32(ww[i] >> 16))));
+                    }
+                } else {
+                    const float off = (float)(1 << (N - 1));
+                    for (int64_t t = t0 + tid; t < t1; t += nthr) {
+                        const uint2 w = *(const uint2*)(vsc + t * 8);
+                        const float d4 = fmaxf(fmaxf(fabsf(fp16_to_f32(w.x & 0xFFFFu)), fabsf(fp16_to_f32(w.x >> 16))),
+                                               fmaxf(fabsf(fp16_to_f32(w.y & 0xFFFFu)), fabsf(fp16_to_f32(w.y >> 16))));
+                        vb = fmaxf(vb, d4 * off);
+                    }
+                }
+                if (kind_paged(KV)) {
+                    const uint16_t* ch = (const uint16_t*)(vst + g.v.cscale);
+                    for (int64_t i = (t0 / kPage) * kD + tid; i < ((t1 - 1) / kPage + 1) * kD; i += nthr)
+                        cb = fmaxf(cb, fabsf(fp16_to_f32(ch[i])));
+                }
+            } else {
+                const bool f16r = !quant && g.tail_f16;
+                for (int64_t i = t0 * 16 + tid; i < t1 * 16; i += nthr) {
+                    const int64_t t = i >> 4;
+                    const char* row = quant ? vst + g.v.codes + t * 256 : vst + g.v.ring + (t % g.ring_slots) * 256;
+                    const uint4 w = *(const uint4*)(row + 16 * (i & 15));
+                    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        vb = fmaxf(vb, fmaxf(fabsf(canon_to_f32(ww[k] & 0xFFFFu, f16r)), fabsf(canon_to_f32(ww[k] >> 16, f16r))));
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            vb = fmaxf(vb, __shfl_xor(vb, o));
+            cb = fmaxf(cb, __shfl_xor(cb, o));
+        }
+        if (lane == 0) {
+            vbnd[0][wave] = vb;
+            vbnd[1][wave] = cb;
+        }
+    }
     pf_wait_vm0();
     __syncthreads();
+    // value exponent sv: the bound times 2^sv in [2^14, 2^15)
+    float vmul = 1.0f, ounscale = 1.0f / 32768.0f;
+    {
+        float vmax = 0.0f, cmax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4 * NT; ++w) {
+            vmax = fmaxf(vmax, vbnd[0][w]);
+            cmax = fmaxf(cmax, vbnd[1][w]);
+        }
+        const float bound = (quant && kind_paged(KV)) ? vmax * cmax : vmax;
+        if (bound > 0.0f) {
+            const int ex = (int)((__float_as_uint(bound) >> 23) & 0xFFu);
+            const int sv = min(126, max(-126, 14 - ((ex == 0 ? 1 : ex) - 127)));
+            vmul = __builtin_ldexpf(1.0f, sv);
+            ounscale = __builtin_ldexpf(1.0f, -15 - sv);
+        }
+    }
     // keys by threads 0-255 and values by 256-511 (NT = 2), or both by every thread
     auto unpack = [&](PfLds& Ld, const PfRawL<BIG>& Rr, int nt) __attribute__((always_inline)) {
-        if constexpr (NT == 1) pf_unpack<KK, KV, RING, BIG, 0>(Ld, Rr, a, nt, quant, tid);
-        else if (tid < 256) pf_unpack<KK, KV, RING, BIG, 1>(Ld, Rr, a, nt, quant, tid);
-        else pf_unpack<KK, KV, RING, BIG, 2>(Ld, Rr, a, nt, quant, tid - 256);
+        if constexpr (NT == 1) pf_unpack<KK, KV, RING, BIG, 0>(Ld, Rr, a, nt, quant, tid, vmul);
+        else if (tid < 256) pf_unpack<KK, KV, RING, BIG, 1>(Ld, Rr, a, nt, quant, tid, vmul);
+        else pf_unpack<KK, KV, RING, BIG, 2>(Ld, Rr, a, nt, quant, tid - 256, vmul);
     };
     if (nb > 0) unpack(L[0], RW[0], nt_of(0));
     // iteration i: L[i & 1] holds block i, RW[(i + 1) & 1] raw block i + 1 (loaded during
@@ -570,7 +686,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pp[2 + 32 * b + 8 * (r >> 2) + 4 * hh + (r & 3)] = O[b][r];
+        for (int r = 0; r < 16; ++r) pp[2 + 32 * b + 8 * (r >> 2) + 4 * hh + (r & 3)] = O[b][r] * ounscale;
 }
 
 // One workgroup of 128 threads per (query, query head): merge the splits; the quantized
