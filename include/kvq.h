@@ -155,6 +155,21 @@ int kv_decode_attn(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t
                    const void* q, int32_t q_dtype, float softmax_scale, float* out,
                    void* workspace, int64_t ws_bytes, void* stream);
 
+/* kv_decode_attn without a workspace and without allocating device memory, for callers
+ * that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (less the workspace) and results as kv_decode_attn,
+ * with which it shares its kernels.  The split partials go to a fixed array inside the
+ * library: 1024 partials, 4,259,840 bytes per device, held from the first call on that
+ * device until the process ends; the split plan is capped at 1024 workgroups (the fast
+ * kernel's plans use 256 per 256 compute units).  Errors: as kv_decode_attn, plus KV_ESIZE
+ * when even the smallest plan (2 workgroups per sequence and KV head) exceeds the array,
+ * KV_EDEVICE if the array cannot be located.  Every call on one device uses that same
+ * array: calls that overlap on one device (other streams, other threads) race and must be
+ * ordered by the caller. */
+int kv_decode_attn_noalloc(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                           const void* q, int32_t q_dtype, float softmax_scale, float* out,
+                           void* stream);
+
 /* Bytes of workspace needed by kv_prefill_attn for a chunk of n_new tokens at any length
  * up to max_tokens (per-split partial results; no initialization needed; calls sharing it
  * must be stream-ordered). */

@@ -458,21 +458,38 @@ int kv_attn_kld(kv_cache* c, int32_t layer, int32_t seq_id, const void* q, int32
     return launch_kld(a, stream) ? KV_EDEVICE : KV_OK;
 }
 
-int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
-                   const void* q, int32_t q_dtype, float softmax_scale, float* out,
-                   void* workspace, int64_t ws_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the decode entry points (everything but the workspace).
+int decode_check(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                 int32_t q_dtype, float softmax_scale, const float* out)
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers) return KV_EINVAL;
     if (!distinct_valid_ids(c, n_seqs, seq_ids)) return KV_EINVAL;
     if (n_seqs > kMaxSeqsPerLaunch) return KV_EUNSUPPORTED;
-    if (!q || !out || !workspace) return KV_EINVAL;
+    if (!q || !out) return KV_EINVAL;
     if (q_dtype != KV_IN_BF16 && q_dtype != KV_IN_F32) return KV_EINVAL;
     if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
         return KV_EINVAL;
-    if (ws_bytes < kv_decode_workspace_bytes(c, n_seqs)) return KV_ESIZE;
+    return KV_OK;
+}
+
+int decode_nonempty(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids)
+{
     for (int i = 0; i < n_seqs; ++i)
         if (n_at(c, seq_ids[i], layer) == 0) return KV_EEMPTY;
+    return KV_OK;
+}
 
+// Split plan (at most max_wgs workgroups, each leaving one partial) and launch of a checked
+// decode call; `partials` holds max_wgs partials.  KV_EUNSUPPORTED if even the smallest plan
+// (one quantized and one ring split per sequence and KV head) needs more.
+int decode_launch(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                  int32_t q_dtype, float softmax_scale, float* out, void* partials, int64_t max_wgs,
+                  void* stream)
+{
     DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.g = c->geom;
@@ -482,8 +499,7 @@ int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* se
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.q = q;
     a.out = out;
-    a.partials = (float*)workspace;
-
+    a.partials = (float*)partials;
     const int H = c->cfg.n_kv_heads;
     int64_t total_units = 0, max_uq = 1, max_ut = 1;
     for (int i = 0; i < n_seqs; ++i) {
@@ -504,7 +520,7 @@ int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* se
     int cus = device_cu_count();
     int per_cu = decode_wgs_per_cu(c->cfg.fmt_k, c->cfg.fmt_v, c->geom.group);
     if (cus <= 0 || per_cu <= 0) return KV_EDEVICE;
-    const int64_t target = (int64_t)cus * per_cu;
+    const int64_t target = std::min<int64_t>((int64_t)cus * per_cu, max_wgs);
     int64_t upw = std::max<int64_t>(1, (total_units + 4 * target - 1) / (4 * target));
     auto plan = [&](int64_t uq, int64_t ut) {
         int64_t w = 0;
@@ -531,11 +547,45 @@ int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* se
         ++upw;
     }
     wgs = plan(upw, upw_t);
-    if (wgs > kMaxDecodeWGs) return KV_EUNSUPPORTED;
+    if (wgs > max_wgs) return KV_EUNSUPPORTED;
     a.units_per_wg = (int32_t)upw;
     a.units_per_wg_t = (int32_t)upw_t;
     int rc = launch_decode(a, (int)wgs, stream);
     return rc ? KV_EDEVICE : KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_decode_attn(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                   const void* q, int32_t q_dtype, float softmax_scale, float* out,
+                   void* workspace, int64_t ws_bytes, void* stream)
+{
+    int rc = decode_check(c, layer, n_seqs, seq_ids, q, q_dtype, softmax_scale, out);
+    if (rc) return rc;
+    if (!workspace) return KV_EINVAL;
+    if (ws_bytes < kv_decode_workspace_bytes(c, n_seqs)) return KV_ESIZE;
+    if ((rc = decode_nonempty(c, layer, n_seqs, seq_ids))) return rc;
+    return decode_launch(c, layer, n_seqs, seq_ids, q, q_dtype, softmax_scale, out, workspace, kMaxDecodeWGs,
+                         stream);
+}
+
+int kv_decode_attn_noalloc(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                           const void* q, int32_t q_dtype, float softmax_scale, float* out, void* stream)
+{
+    int rc = decode_check(c, layer, n_seqs, seq_ids, q, q_dtype, softmax_scale, out);
+    if (rc) return rc;
+    if ((rc = decode_nonempty(c, layer, n_seqs, seq_ids))) return rc;
+    // the smallest plan (one quantized and one ring split per sequence and KV head) must fit
+    // the device array: a clear error before any device call
+    if ((int64_t)n_seqs * c->cfg.n_kv_heads * 2 > kScratchWGs) return KV_ESIZE;
+    int64_t bytes = 0;
+    void* scratch = decode_scratch(&bytes);
+    if (!scratch) return KV_EDEVICE;
+    if (bytes < kScratchWGs * kPartialFloats * 4) return KV_EDEVICE;
+    rc = decode_launch(c, layer, n_seqs, seq_ids, q, q_dtype, softmax_scale, out, scratch, kScratchWGs, stream);
+    return rc == KV_EUNSUPPORTED ? KV_ESIZE : rc;
 }
 
 int kv_seq_get(const kv_cache* c, int32_t seq, int32_t layer, int64_t* n, int64_t* n_q)

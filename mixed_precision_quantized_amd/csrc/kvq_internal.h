@@ -146,6 +146,7 @@ int launch_prefill(const PrefillArgs& a, void* stream);          // kvq_prefill.
 
 constexpr int kPartialFloats = kMaxGroup * (kD + 2);   // m, l, acc[128] per query head
 constexpr int kMaxDecodeWGs = 8192;
+constexpr int kScratchWGs = 1024;   // decode partials in the library's own device array
 
 // Kernel launchers (implemented in the .hip translation units).  Return 0 on a
 // successful launch, or the HIP error code.
@@ -161,5 +162,8 @@ bool decode_fast_supported(int fmt_k, int fmt_v);
 int launch_decode_fast(const DecodeArgs& a, int n_wgs, void* stream);
 int decode_fast_wgs_per_cu(int fmt_k, int fmt_v);
 int device_cu_count();
+// The decode partials array of the current device for callers that cannot allocate
+// (kvq_merge.hip); its size in *bytes; null if the device or the array cannot be located.
+void* decode_scratch(int64_t* bytes);
 
 }  // namespace kvq

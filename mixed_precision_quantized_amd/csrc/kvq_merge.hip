@@ -13,9 +13,17 @@
 // KVarN (both inner quantizers): the quantized splits accumulate rotated values (Yhat, with x = H Yhat / 128 and H
 // the unnormalized Sylvester Hadamard matrix), the BF16 ring splits original values; the
 // quantized sum is rotated back here once, before the two are added.
+#include <mutex>
+
 #include "kvq_device.h"
 
 namespace kvq {
+
+// Split partials of kv_decode_attn_noalloc, for callers that cannot allocate: one array of
+// kScratchWGs partials (4,259,840 bytes) per device, kept until the process ends and shared
+// by every such call on that device.  The partials need no initialization (each workgroup
+// writes its own in full).
+static __device__ __align__(256) float scratch[kScratchWGs * kPartialFloats];
 
 namespace {
 
@@ -127,6 +135,25 @@ __global__ __launch_bounds__(kThreads) void k_merge(DecodeArgs a)
 }
 
 }  // namespace
+
+// Device address of this device's `scratch`, looked up on the first call per device with
+// that device current (the host-side name is not a device address).
+void* decode_scratch(int64_t* bytes)
+{
+    constexpr int kMaxDevices = 64;
+    static void* ptr[kMaxDevices] = {nullptr};
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptr[dev] = p;
+    }
+    *bytes = (int64_t)sizeof(scratch);
+    return ptr[dev];
+}
 
 int launch_merge(const DecodeArgs& a, void* stream)
 {

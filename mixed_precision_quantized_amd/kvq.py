@@ -74,6 +74,8 @@ def lib():
         L.kv_decode_workspace_bytes.restype = _i64
         L.kv_decode_attn.argtypes = [_vp, _i32, _i32, _i32p, _vp, _i32, ctypes.c_float, _vp, _vp, _i64, _vp]
         L.kv_decode_attn.restype = ctypes.c_int
+        L.kv_decode_attn_noalloc.argtypes = [_vp, _i32, _i32, _i32p, _vp, _i32, ctypes.c_float, _vp, _vp]
+        L.kv_decode_attn_noalloc.restype = ctypes.c_int
         L.kv_prefill_workspace_bytes.argtypes = [_vp, _i32]
         L.kv_prefill_workspace_bytes.restype = _i64
         L.kv_prefill_attn.argtypes = [_vp, _i32, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _i64, _vp]
@@ -194,6 +196,19 @@ class Cache:
                                   ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(self.ws.data_ptr()),
                                   self.ws.numel(), _stream(stream))
         _check(rc, "kv_decode_attn")
+        return out
+
+    def decode_noalloc(self, layer, seq_ids, q, out, softmax_scale=None, stream=None):
+        """decode() through kv_decode_attn_noalloc: no workspace, the library's own device
+        array (calls on one device must not overlap); `out` is caller-provided."""
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(128)
+        dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
+        rc = lib().kv_decode_attn_noalloc(self.h, int(layer), len(seq_ids), _ids(seq_ids),
+                                          ctypes.c_void_p(q.data_ptr()), dt, float(softmax_scale),
+                                          ctypes.c_void_p(out.data_ptr()), _stream(stream))
+        _check(rc, "kv_decode_attn_noalloc")
         return out
 
     def prefill(self, layer, seq_id, q, softmax_scale=None, out=None, ws=None, stream=None):

@@ -139,6 +139,11 @@ def test_append_decode_spill_validation_paths():
     assert L.kv_decode_attn(h, 0, 1, ids, ptr, 0, float("nan"), ptr, ptr, ws, None) == kvq.KV_EINVAL
     assert L.kv_decode_attn(h, 0, 1, ids, ptr, 5, 0.1, ptr, ptr, ws, None) == kvq.KV_EINVAL
     assert L.kv_decode_attn(h, 3, 1, ids, ptr, 0, 0.1, ptr, ptr, ws, None) == kvq.KV_EINVAL
+    # the allocation-free entry point checks the same arguments before any device call
+    assert L.kv_decode_attn_noalloc(h, 0, 1, ids, ptr, 0, 0.1, ptr, None) == kvq.KV_EEMPTY
+    assert L.kv_decode_attn_noalloc(h, 3, 1, ids, ptr, 0, 0.1, ptr, None) == kvq.KV_EINVAL
+    assert L.kv_decode_attn_noalloc(h, 0, 1, ids, None, 0, 0.1, ptr, None) == kvq.KV_EINVAL
+    assert L.kv_decode_attn_noalloc(None, 0, 1, ids, ptr, 0, 0.1, ptr, None) == kvq.KV_EINVAL
     # spill: keep larger than the tail, bad seq
     assert L.kv_spill_tail(h, 0, 0, 17, None) == kvq.KV_EINVAL
     assert L.kv_spill_tail(h, 0, 5, 0, None) == kvq.KV_EINVAL
@@ -164,4 +169,18 @@ def test_kvarn_granule_rules():
     assert offs[2] > 0 and offs[1] > offs[0] and offs[3] > offs[2]
     assert L.kv_seq_set(h, 0, 0, 200, 100) == kvq.KV_EINVAL    # n_q must be a page multiple
     assert L.kv_seq_set(h, 0, 0, 200, 128) == kvq.KV_OK
+    L.kv_cache_destroy(h)
+
+
+def test_noalloc_rejects_plans_beyond_its_array():
+    """kv_decode_attn_noalloc: a plan that cannot fit the library's 1024-partial device array
+    (600 KV heads need at least 1200 workgroups) is rejected before any device call."""
+    L = kvq.lib()
+    c = cfg(H=600, QH=2400, M=256)
+    rc, h = _handle(c)
+    assert rc == 0
+    assert L.kv_seq_set(h, 0, 0, 10, 10) == kvq.KV_OK       # 10 quantized tokens (tail 0)
+    ids = kvq._ids([0])
+    ptr = ctypes.c_void_p(FAKE)
+    assert L.kv_decode_attn_noalloc(h, 0, 1, ids, ptr, 0, 0.1, ptr, None) == kvq.KV_ESIZE
     L.kv_cache_destroy(h)
