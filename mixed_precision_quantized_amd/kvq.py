@@ -18,7 +18,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# the in-tree build; KVQ_LIB_PATH may name another build of the same library (the HIP
+# library either way: there is no CPU path)
+LIB_PATH = os.environ.get("KVQ_LIB_PATH") or os.path.join(HERE, "libkvq.so")
 
 FORMATS = ["bf16", "q2_0", "q2_1", "q3_0", "q3_1", "q4_0", "q4_1", "q5_0", "q5_1", "q6_0",
            "q6_1", "q8_0", "q8_1", "kvarn2", "kvarn3", "kvarn4", "kvarn5", "kvarn6", "kvarn8",
