@@ -11,7 +11,11 @@ Reported (one JSON line):
              (every quantized row K+V plus every BF16 ring row, read once) / their time
   roofline   the decode kernel against HBM peak (8 TB/s), per launch from HIP events
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
-  append_tokens_per_s  64-layer appends of 512-token chunks (whole-model tokens per second)
+  append     the ragged batch (16 sequences, lengths uniform on [8000, 120000], 64 layers,
+             kvarn3, BF16 tail 1024): one step appends a 512-token chunk to every sequence on
+             all 64 layers, then decodes all 64 layers for the 16 sequences.  Sequence-tokens
+             per second with an HBM roof (826 B per stream-token) and an ALU co-roof (the page
+             encoder's lane operations), and the ragged decode's KV read rate.
 """
 from __future__ import annotations
 
@@ -71,6 +75,9 @@ def parse():
     p.add_argument("--append-reps", type=int, default=4)
     p.add_argument("--cpu-units", type=int, default=16, help="(layer, kv head) units of the CPU sample")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-ragged", action="store_true", help="skip the 16-sequence append + decode leg")
+    p.add_argument("--ragged-steps", type=int, default=5)
+    p.add_argument("--ragged-only", action="store_true", help="only the 16-sequence leg (its own JSON line)")
     p.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
                    help="chunked-prefill attention: time a CHUNK-token chunk at the end of --ctx tokens")
     p.add_argument("--kld", action="store_true",
@@ -97,6 +104,119 @@ def decode_bytes_layer(fmt, n, n_q, heads):
     block scales, amortized channel scales) plus every BF16 ring row, read once."""
     fk, fv = split_fmt(fmt)
     return heads * (n_q * (stream_bytes(fk) + stream_bytes(fv)) + (n - n_q) * 2 * 256)
+
+
+# Lane operations of the KVarN page encoder per stream-token (one 128-dim vector), counted
+# from its definition: FWHT-128 (7 x 128 add/sub), squares (128), 8 Sinkhorn iterations of a
+# row pass and a column pass (each a multiply and an add per element: 4 x 128), the
+# reciprocal channel scaling (128) and the block encode (max, scale, round, clamp, pack:
+# 5 x 128); per-row and per-column square roots and reciprocals are amortized over 128.
+KVARN_OPS_PER_STREAM_TOKEN = 7 * 128 + 128 + 8 * 4 * 128 + 128 + 5 * 128
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz: single (not packed, not fused) lane operations/s
+ALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def append_bytes_stream_token(fmt, tail, in_bytes=256):
+    """Algorithmic HBM bytes per stream-token of a steady-state append: the input row, the
+    ring write and the ring read when the token spills (both only with a tail), the encoded
+    row (codes, block scales, amortized channel scales)."""
+    ring = 2 * 256 if tail > 0 else 0
+    return in_bytes + ring + stream_bytes(fmt)
+
+
+def ragged_leg(args):
+    """The 16-sequence ragged workload: fill, then steps of (512-token append on all 64 layers
+    for every sequence, 64 batched decodes); append and decode timed apart with HIP events."""
+    import torch
+    from mixed_precision_quantized_amd import kvq, synth
+    wl = "c5_ragged16_64l"
+    w = synth.WORKLOADS[wl]
+    fmt, tail, chunk, S = w["fmts"][0], w["tail"], w["chunk"], w["n_seqs"]
+    L, H, QH = w["layers"], w["kv_heads"], w["q_heads"]
+    lens = synth.seq_lengths(wl)
+    nsteps = args.warmup + args.ragged_steps
+    cache = kvq.Cache(L, H, QH, fmt, tail_tokens=tail, n_seqs=S, max_tokens=max(lens) + nsteps * chunk + 128)
+    seqs = list(range(S))
+
+    def rows(layer, spans):
+        k = torch.cat([torch.stack([synth.kv_rows(wl, s, layer, h, 0, a, b, "cuda") for h in range(H)], 1)
+                       for s, a, b in spans], 0)
+        v = torch.cat([torch.stack([synth.kv_rows(wl, s, layer, h, 1, a, b, "cuda") for h in range(H)], 1)
+                       for s, a, b in spans], 0)
+        return synth.to_bf16_bits(k).contiguous(), synth.to_bf16_bits(v).contiguous()
+
+    t0 = time.time()
+    for layer in range(L):
+        t = [0] * S
+        while any(t[s] < lens[s] for s in seqs):
+            spans = [(s, t[s], min(lens[s], t[s] + 16384)) for s in seqs if t[s] < lens[s]]
+            k, v = rows(layer, spans)
+            cache.append(layer, [s for s, _, _ in spans], [b - a for _, a, b in spans], k, v)
+            for s, a, b in spans:
+                t[s] = b
+        if layer % 16 == 15:
+            torch.cuda.synchronize()
+            print("  ragged: filled layer %d" % layer, file=sys.stderr, flush=True)
+    print("  ragged fill %.1f s, cache %.2f GiB" % (time.time() - t0, cache.nbytes / 2**30), file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((S, QH, 128), dtype=torch.float32, device="cuda")
+    qs = [torch.stack([synth.to_bf16_bits(synth.q_rows(wl, s, l, 0, QH, "cuda")) for s in seqs], 0).contiguous()
+          for l in range(L)]
+    app_ms, dec_ms, dec_bytes = [], [], []
+    for i in range(nsteps):
+        # the step's input, [L][16 x 512][H][128] per stream (made before the timed region)
+        spans = [(s, lens[s] + i * chunk, lens[s] + (i + 1) * chunk) for s in seqs]
+        kv = [rows(l, spans) for l in range(L)]
+        K = torch.stack([x[0] for x in kv], 0).contiguous()
+        V = torch.stack([x[1] for x in kv], 0).contiguous()
+        del kv
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        cache.append(-1, seqs, [chunk] * S, K, V)
+        ev[1].record(stream)
+        for l in range(L):
+            cache.decode(l, seqs, qs[l], out=out)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            app_ms.append(ev[0].elapsed_time(ev[1]))
+            dec_ms.append(ev[1].elapsed_time(ev[2]))
+            b = 0.0
+            for s in seqs:
+                n, n_q = cache.seq_get(s, 0)
+                b += L * decode_bytes_layer(fmt, n, n_q, H)
+            dec_bytes.append(b)
+        del K, V
+    print("  ragged: %d steps done" % nsteps, file=sys.stderr, flush=True)
+    a_ms = sum(app_ms) / len(app_ms)
+    tokens = S * chunk
+    tps = tokens / (a_ms * 1e-3)
+    bst = append_bytes_stream_token(fmt, tail)
+    streams = L * H * 2
+    hbm_gbs = tokens * streams * bst / (a_ms * 1e-3) / 1e9
+    ops = tokens * streams * KVARN_OPS_PER_STREAM_TOKEN if fmt.startswith("kvarn") else 0
+    alu = ops / (a_ms * 1e-3)
+    d_ms = sum(dec_ms) / len(dec_ms)
+    d_gbs = sum(dec_bytes) / len(dec_bytes) / (d_ms * 1e-3) / 1e9
+    del cache
+    torch.cuda.empty_cache()
+    return {
+        "workload": "16 sequences (lengths uniform on [8000, 120000], seeded), 64 layers x 8 KV heads x 32 q heads "
+                    "x d128, %s, BF16 tail %d; a step appends %d tokens to every sequence on all 64 layers"
+                    % (fmt, tail, chunk),
+        "lengths": lens, "steps": len(app_ms),
+        "tokens_per_s": round(tps, 1), "unit": "sequence-tokens/s", "ms_per_step": round(a_ms, 4),
+        "bytes_per_stream_token": bst, "bytes_per_sequence_token": bst * streams,
+        "roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "one 64-layer append call (ring write, spill, page encode)"},
+        "alu_roof": {"bound": "alu", "achieved": round(alu / 1e12, 3), "peak": round(ALU_PEAK_LANE_OPS / 1e12, 3),
+                     "unit": "T lane-ops/s", "frac": round(alu / ALU_PEAK_LANE_OPS, 4),
+                     "ops_per_stream_token": KVARN_OPS_PER_STREAM_TOKEN if ops else 0},
+        "ragged_decode": {"value": round(d_gbs, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * d_gbs / HBM_PEAK_GBS, 2),
+                          "ms_per_step": round(d_ms, 4), "bytes_per_step": int(sum(dec_bytes) / len(dec_bytes))},
+    }
 
 
 def copy_probe(nbytes):
@@ -302,6 +422,10 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.ragged_only:
+        print(json.dumps({"metric": "ragged append sequence-tokens/s; ragged decode KV read GB/s",
+                          "data": "synthetic", "append": ragged_leg(args)}), flush=True)
+        return
     import torch
     from mixed_precision_quantized_amd import kvq, synth
 
@@ -390,6 +514,10 @@ def main():
     torch.cuda.synchronize()
     app_tps = ch * args.append_reps / (a0.elapsed_time(a1) * 1e-3)
 
+    del cache, K_all, V_all
+    torch.cuda.empty_cache()
+    ragged = None if args.no_ragged else ragged_leg(args)
+
     cpu = None
     if not args.no_cpu:
         print("  cpu baseline ...", file=sys.stderr, flush=True)
@@ -407,7 +535,9 @@ def main():
                    "tail": args.tail, "batch": 1},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_ms_per_step": round(dec_ms, 4),
-        "append_tokens_per_s": round(app_tps, 1),
+        "append_tokens_per_s": ragged["tokens_per_s"] if ragged else None,
+        "append": ragged,
+        "append_single_seq_tokens_per_s": round(app_tps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.fmt, args.ctx, args.tail, H),

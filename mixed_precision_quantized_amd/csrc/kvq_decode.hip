@@ -228,14 +228,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
     const int tid = threadIdx.x;
     const int bid = blockIdx.x;
     // ---- which (sequence, KV head, split) ------------------------------------------------
-    int e = 0;
-    for (int i = 1; i < a.n_seqs; ++i)
-        if (a.seqs[i].wg_base <= bid) e = i;
-    const DecodeSeq& sq = a.seqs[e];
-    const int S = sq.splits_q + sq.splits_t;
-    const int r = bid - sq.wg_base;
-    const int head = r / S;
-    const int sp = r % S;
+    const DecodeWork wk = decode_work(a, bid);
+    const DecodeSeq& sq = a.seqs[wk.e];
+    const int head = wk.head;
+    const int sp = wk.sp;
     const bool quant = sp < sq.splits_q;
     const int upw = quant ? a.units_per_wg : a.units_per_wg_t;
     const int u_lo = (quant ? sp : sp - sq.splits_q) * upw;
@@ -339,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecodeArgs a)
     }
     __syncthreads();
     // ---- merge the 4 waves, write this workgroup's partial -----------------------------------
-    float* part_out = a.partials + (int64_t)bid * kPartialFloats;
+    float* part_out = a.partials + (int64_t)wk.slot * kPartialFloats;
     for (int i = tid; i < kG * kD; i += blockDim.x) {
         const int h = i / kD, d = i % kD;
         float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));

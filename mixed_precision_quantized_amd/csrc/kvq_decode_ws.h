@@ -541,14 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
     const int wg4 = wave >> 2, w4 = wave & 3;
     const int pr = 2 * wg4 + (w4 & 1);
     const bool kwave = ((w4 >> 1) ^ (wg4 & 1)) == 0;
-    int e = 0;
-    for (int i = 1; i < a.n_seqs; ++i)
-        if (a.seqs[i].wg_base <= bid) e = i;
-    const DecodeSeq& sq = a.seqs[e];
-    const int SPL = sq.splits_q + sq.splits_t;
-    const int rr = bid - sq.wg_base;
-    const int head = rr / SPL;
-    const int sp = rr % SPL;
+    const DecodeWork wk = decode_work(a, bid);
+    const DecodeSeq& sq = a.seqs[wk.e];
+    const int head = wk.head;
+    const int sp = wk.sp;
     const bool quant = sp < sq.splits_q;
     const int upw = quant ? a.units_per_wg : a.units_per_wg_t;
     const int u_lo = (quant ? sp : sp - sq.splits_q) * upw;
@@ -1344,7 +1340,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
     }
 
     __syncthreads();
-    float* part_out = a.partials + (int64_t)bid * kPartialFloats;
+    float* part_out = a.partials + (int64_t)wk.slot * kPartialFloats;
     for (int i = tid; i < kG * kD; i += blockDim.x) {
         const int h = i / kD, d = i % kD;
         float M = S.wm[0][h];

@@ -14,6 +14,30 @@
 
 namespace kvq {
 
+// The split that workgroup b of a decode launch runs: every quantized split first
+// (sequence by sequence, then head by head), every ring split after them, so that in a
+// launch of several waves the small ring splits fill the end.  Its partial goes to slot
+// wg_base + head (splits_q + splits_t) + sp of the sequence, sp counting the quantized
+// splits first.
+struct DecodeWork { int e, head, sp, slot; };
+__device__ inline DecodeWork decode_work(const DecodeArgs& a, int b)
+{
+    const bool quant = b < a.q_wgs;
+    const int r0 = quant ? b : b - a.q_wgs;
+    int e = 0;
+    for (int i = 1; i < a.n_seqs; ++i)
+        if ((quant ? a.seqs[i].q_base : a.seqs[i].t_base) <= r0) e = i;
+    const DecodeSeq& s = a.seqs[e];
+    const int rr = r0 - (quant ? s.q_base : s.t_base);
+    const int ns = quant ? s.splits_q : s.splits_t;
+    DecodeWork w;
+    w.e = e;
+    w.head = rr / ns;
+    w.sp = (quant ? 0 : s.splits_q) + rr % ns;
+    w.slot = s.wg_base + w.head * (s.splits_q + s.splits_t) + w.sp;
+    return w;
+}
+
 // ------------------------------------------------------------------ format traits
 // Bits N per code of each format (bf16 = 16).
 __host__ __device__ constexpr int fbits(int f)

@@ -514,14 +514,22 @@ int decode_launch(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq
         max_uq = std::max<int64_t>(max_uq, s.units_q);
         max_ut = std::max<int64_t>(max_ut, s.units_t);
     }
-    // Balanced split, sized so that the whole grid is resident at once.  A 32-token ring
-    // unit (16 KB of BF16 rows, binary32 arithmetic) takes about 1.25 times as long as a
-    // 128-token quantized page, so ring workgroups get 0.8 as many units.
+    // Balanced split.  Ring units and quantized pages never share a workgroup, so every
+    // (sequence, KV head) needs one workgroup of each kind at least; while those are few
+    // (at most an eighth of the resident workgroups) the grid is one resident wave, else up
+    // to 4 waves of smaller splits, which the hardware hands out as workgroups finish (the
+    // ring splits come last and fill the end).  A 32-token ring unit (16 KB of BF16 rows,
+    // binary32 arithmetic) takes about 1.25 times as long as a 128-token quantized page, so
+    // ring workgroups get 0.8 as many units (up to 0.9x when that saves a workgroup).
     int cus = device_cu_count();
     int per_cu = decode_wgs_per_cu(c->cfg.fmt_k, c->cfg.fmt_v, c->geom.group);
     if (cus <= 0 || per_cu <= 0) return KV_EDEVICE;
-    const int64_t target = std::min<int64_t>((int64_t)cus * per_cu, max_wgs);
-    int64_t upw = std::max<int64_t>(1, (total_units + 4 * target - 1) / (4 * target));
+    const int64_t slots = (int64_t)cus * per_cu;
+    int64_t min_wgs = 0;
+    for (int i = 0; i < n_seqs; ++i)
+        min_wgs += (int64_t)H * ((a.seqs[i].units_q > 0) + (a.seqs[i].units_t > 0));
+    const int64_t waves = std::min<int64_t>(4, std::max<int64_t>(1, (8 * min_wgs + slots - 1) / slots));
+    const int64_t target = std::min<int64_t>(slots * waves, max_wgs);
     auto plan = [&](int64_t uq, int64_t ut) {
         int64_t w = 0;
         for (int i = 0; i < n_seqs; ++i) {
@@ -535,21 +543,31 @@ int decode_launch(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq
         }
         return w;
     };
-    int64_t upw_t = 1, wgs = 0;
-    for (;;) {
-        // ring workgroups take 0.8 as many units, up to 0.9x when that saves a workgroup
-        bool fit = false;
-        const int64_t t_hi = std::max<int64_t>(1, (9 * upw + 9) / 10);
-        for (upw_t = std::max<int64_t>(1, 4 * upw / 5); upw_t <= t_hi; ++upw_t)
-            if (plan(upw, upw_t) <= target) { fit = true; break; }
-        if (!fit) upw_t = t_hi;
-        if (fit || (upw >= max_uq && upw_t >= max_ut)) break;
-        ++upw;
+    auto t_lo = [](int64_t u) { return std::max<int64_t>(1, 4 * u / 5); };
+    auto t_hi = [](int64_t u) { return std::max<int64_t>(1, (9 * u + 9) / 10); };
+    // the fewest units per workgroup that fit the target (the count falls as units grow)
+    int64_t lo = std::max<int64_t>(1, (total_units + 4 * target - 1) / (4 * target));
+    int64_t hi = std::max<int64_t>(lo, std::max<int64_t>(max_uq, (10 * max_ut + 8) / 9 + 1));
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (plan(mid, t_hi(mid)) <= target) hi = mid; else lo = mid + 1;
     }
-    wgs = plan(upw, upw_t);
+    const int64_t upw = lo;
+    int64_t upw_t = t_hi(upw);
+    for (int64_t t = t_lo(upw); t < t_hi(upw); ++t)
+        if (plan(upw, t) <= target) { upw_t = t; break; }
+    const int64_t wgs = plan(upw, upw_t);
     if (wgs > max_wgs) return KV_EUNSUPPORTED;
     a.units_per_wg = (int32_t)upw;
     a.units_per_wg_t = (int32_t)upw_t;
+    int32_t qb = 0, tb = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        a.seqs[i].q_base = qb;
+        a.seqs[i].t_base = tb;
+        qb += H * a.seqs[i].splits_q;
+        tb += H * a.seqs[i].splits_t;
+    }
+    a.q_wgs = qb;
     int rc = launch_decode(a, (int)wgs, stream);
     return rc ? KV_EDEVICE : KV_OK;
 }

@@ -88,7 +88,9 @@ struct DecodeSeq {
     int32_t units_t;      // tail work units (32 tokens)
     int32_t splits_q;     // workgroups per kv head over the quantized region
     int32_t splits_t;     // workgroups per kv head over the BF16 ring
-    int32_t wg_base;      // first workgroup of this sequence
+    int32_t wg_base;      // first partial of this sequence ([head][split] order)
+    int32_t q_base;       // quantized workgroups of the sequences before this one
+    int32_t t_base;       // ring workgroups of the sequences before this one
     int32_t pad_;
 };
 
@@ -100,6 +102,8 @@ struct DecodeArgs {
     int32_t q_dtype;      // 0 bf16, 1 fp32
     float scale_log2;     // softmax_scale * log2(e)
     int32_t units_per_wg_t; // ring units per workgroup
+    int32_t q_wgs;        // quantized workgroups of the launch (they come first)
+    int32_t pad_;
     const void* q;        // [n_seqs][n_q_heads][128]
     float* out;           // [n_seqs][n_q_heads][128]
     float* partials;      // [max_wgs][kPartialFloats]
