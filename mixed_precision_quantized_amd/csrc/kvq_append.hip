@@ -334,17 +334,30 @@ __global__ __launch_bounds__(256) void k_ring_write(AppendArgs a, int64_t tokens
 }
 
 // ------------------------------------------------------------------ KVarN page encoder
-constexpr int kLdsStride = 129;   // padded row of the 128x128 fp32 page (conflict-free rows and columns)
+// One 128 x 128 page of one stream per workgroup of 256 threads.
+//
+// Phases: (1) thread (t, half) loads half of token row t and rotates the row (six
+// butterfly stages in registers, the last across the lane pair); the rotated values y stay
+// in its registers until the encode.  (2) The squares A = y^2 move through LDS, half a page
+// at a time, into the register tile of the Sinkhorn layout: thread (r0, c0) holds
+// A[r0 + 16 k][c0 + 16 m], k, m = 0..7 (r0, c0 = the low 4 bits of token and channel).
+// (3) Every Sinkhorn sum adds 128 products in the halving-tree order (index bit 6 first,
+// bit 0 last): bits 6..4 are the k or m of the tile, in registers; the row sums' bits 3..0
+// are c0, the lane bits 0..3, combined by DPP (lane ^ 8, ^ 4, ^ 2, ^ 1, every lane
+// ending with the total); the column sums' bits 3..0 are r0, which spans the four waves,
+// so the partials go through LDS and 128 threads finish one column each.  Each reciprocal
+// is taken once (one row per lane of a 16-lane row, then broadcast; one column per
+// thread).  (4) fp16 channel scales, (5) normalize and block-encode the thread's own
+// half-row, pack, store.
+constexpr int kRedStride = 144;   // row of the column partials (rows 16 words apart in the banks)
 
-// tree64 over a register array: for w = 32, 16, ..., 1: v[i] += v[i+w] for i < w.
-__device__ __forceinline__ float tree64(float (&v)[64])
+// XOR swizzle of the transposition buffer [64][128]: column j of token row tl (0..63) sits
+// at word tl * 128 + (j ^ swz(tl, j >> 6)).  Bank conflict free both for the row writes
+// (lanes = 32 tokens x 2 halves) and for the tile reads (lanes = 16 channels x 4 tokens).
+__device__ __forceinline__ int swz(int tl, int h)
 {
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) v[i] = v[i] + v[i + w];
-    }
-    return v[0];
+    const int b0 = (tl >> 2) & 1, b1 = (tl >> 3) & 1, b2 = ((tl >> 4) ^ (tl >> 1)) & 1;
+    return b0 | (b1 << 1) | (b2 << 2) | (h << 3) | ((tl & 1) << 4) | (((tl >> 1) & 1) << 5);
 }
 
 __device__ __forceinline__ float swap_pair(float x)
@@ -353,13 +366,23 @@ __device__ __forceinline__ float swap_pair(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// within each row of 16 lanes: lane ^ 8 (rotate by 8), lane ^ 2, lane ^ 1 (quad
+// permutes); rotate by 4 stands for lane ^ 4 once lanes l and l ^ 8 hold equal values
+constexpr int kRor8 = 0x128, kRor4 = 0x124, kXor2 = 0x4E, kXor1 = 0xB1;
+constexpr int kNewBcast0 = 0x150;   // row_newbcast:n, lane n of the row to the whole row
+
 template <int N, bool AFF>
 __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages, int streams_mask)
 {
-    __shared__ float As[kPage * kLdsStride];   // squares A[t][j]
-    __shared__ float part[2][kPage];           // tree halves (even / odd indices)
-    __shared__ float inv_s[kPage];             // reciprocals 1/c2 or 1/r2 of the current step
-    __shared__ float scale_s[kPage];           // r2 or c2 of the current step
+    __shared__ float tr[64 * kD];              // squares of half a page, swizzled
+    __shared__ float red[16 * kRedStride];     // column partials [r0][channel]
+    __shared__ float ic_s[kPage];              // 1 / c2 of the last column step
+    __shared__ float c2_s[kPage];              // c2 of the last iteration
     __shared__ float ic16_s[kPage];            // 1 / fp16 channel scale
 
     const int tid = threadIdx.x;
@@ -405,41 +428,106 @@ __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages,
         float o = swap_pair(y[i]);
         y[i] = half ? (o - y[i]) : (y[i] + o);
     }
-    // ---- 2. squares into LDS -----------------------------------------------------------
+
+    // ---- 2. squares into the Sinkhorn tile, through LDS half a page at a time -----------
+    const int lane = tid & 63;
+    const int c0 = lane & 15;
+    const int r0 = (lane >> 4) | ((tid >> 6) << 2);
+    float A[8][8];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) As[t * kLdsStride + 64 * half + i] = y[i] * y[i];
-    if (tid < kPage) inv_s[tid] = 1.0f;    // 1 / c2 with c2 = 1
-    __syncthreads();
+    for (int hh = 0; hh < 2; ++hh) {
+        if ((t >> 6) == hh) {
+            const int tl = t & 63;
+            const int sw = swz(tl, half);
+#pragma unroll
+            for (int i = 0; i < 64; ++i) tr[tl * kD + ((64 * half + i) ^ sw)] = y[i] * y[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 4 * hh; k < 4 * hh + 4; ++k) {
+            const int tl = r0 + 16 * (k & 3);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) A[k][m] = tr[tl * kD + ((c0 + 16 * m) ^ swz(tl, m >> 2))];
+        }
+        __syncthreads();
+    }
 
     // ---- 3. Sinkhorn: 8 x (row step, column step) ---------------------------------------
-    const int idx = tid & 127;             // token (row step) or channel (column step)
-    const int par = tid >> 7;              // parity class of the summed index
     const float inv128 = 1.0f / 128.0f;
+    float ic[8];                       // 1 / c2 of the thread's channels c0 + 16 m
+#pragma unroll
+    for (int m = 0; m < 8; ++m) ic[m] = 1.0f;
     for (int it = 0; it < 8; ++it) {
+        // row step: r2[t] = (sum_j A[t][j] / c2[j]) / 128
+        float rs[8];
 #pragma unroll
-        for (int step = 0; step < 2; ++step) {
-            float v[64];
-            if (step == 0) {
+        for (int k = 0; k < 8; ++k) {
+            float v[8];
 #pragma unroll
-                for (int k = 0; k < 64; ++k) v[k] = As[idx * kLdsStride + par + 2 * k] * inv_s[par + 2 * k];
-            } else {
+            for (int m = 0; m < 8; ++m) v[m] = A[k][m] * ic[m];
 #pragma unroll
-                for (int k = 0; k < 64; ++k) v[k] = As[(par + 2 * k) * kLdsStride + idx] * inv_s[par + 2 * k];
-            }
-            part[par][idx] = tree64(v);
-            __syncthreads();
-            if (tid < kPage) {
-                float r = (part[0][tid] + part[1][tid]) * inv128;
-                if (!(r >= FLT_MIN)) r = 1.0f;
-                scale_s[tid] = r;
-                inv_s[tid] = 1.0f / r;
-            }
-            __syncthreads();
+            for (int m = 0; m < 4; ++m) v[m] = v[m] + v[m + 4];
+            v[0] = v[0] + v[2];
+            v[1] = v[1] + v[3];
+            float x = v[0] + v[1];
+            x = x + dppf<kRor8>(x);
+            x = x + dppf<kRor4>(x);
+            x = x + dppf<kXor2>(x);
+            x = x + dppf<kXor1>(x);
+            rs[k] = x;
         }
+        // lane c0 of each 16-lane row takes the reciprocal of row k = c0 & 7 (the others
+        // repeat it); the row then gets every lane's value back by broadcast
+        float sel = rs[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) sel = (c0 & 7) == k ? rs[k] : sel;
+        float r = sel * inv128;
+        if (!(r >= FLT_MIN)) r = 1.0f;
+        const float irs = 1.0f / r;
+        float ir[8];
+        ir[0] = dppf<kNewBcast0 + 0>(irs);
+        ir[1] = dppf<kNewBcast0 + 1>(irs);
+        ir[2] = dppf<kNewBcast0 + 2>(irs);
+        ir[3] = dppf<kNewBcast0 + 3>(irs);
+        ir[4] = dppf<kNewBcast0 + 4>(irs);
+        ir[5] = dppf<kNewBcast0 + 5>(irs);
+        ir[6] = dppf<kNewBcast0 + 6>(irs);
+        ir[7] = dppf<kNewBcast0 + 7>(irs);
+        // column step: c2[j] = (sum_t A[t][j] / r2[t]) / 128; the tile's part (token bits
+        // 6..4), then bits 3..0 (r0) by the column's thread
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = A[k][m] * ir[k];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = v[k] + v[k + 4];
+            v[0] = v[0] + v[2];
+            v[1] = v[1] + v[3];
+            red[r0 * kRedStride + c0 + 16 * m] = v[0] + v[1];
+        }
+        __syncthreads();
+        if (tid < kPage) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = red[i * kRedStride + tid];
+#pragma unroll
+            for (int wd = 8; wd >= 1; wd >>= 1) {
+#pragma unroll
+                for (int i = 0; i < wd; ++i) v[i] = v[i] + v[i + wd];
+            }
+            float c = v[0] * inv128;
+            if (!(c >= FLT_MIN)) c = 1.0f;
+            ic_s[tid] = 1.0f / c;
+            c2_s[tid] = c;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 8; ++m) ic[m] = ic_s[c0 + 16 * m];
     }
     // ---- 4. channel scales ----------------------------------------------------------
     if (tid < kPage) {
-        uint32_t c = fp16s_rne(__builtin_sqrtf(scale_s[tid]));
+        uint32_t c = fp16s_rne(__builtin_sqrtf(c2_s[tid]));
         if (c == 0) c = 0x3C00u;
         ic16_s[tid] = 1.0f / fp16_to_f32(c);
         ((uint16_t*)(st + L.cscale + page * 256))[tid] = (uint16_t)c;
