@@ -85,12 +85,11 @@ __device__ __forceinline__ void load_canon(const char* row, bool f32, bool ring,
 }
 
 // clamp(rint(t) + off, 0, top) in binary32, rint = round half to even.
+// (max/min give the same codes as the comparisons: v is never NaN, and -0 converts to 0.)
 __device__ __forceinline__ uint32_t code_of(float t, float off, float top)
 {
-    float v = __builtin_rintf(t) + off;
-    v = v < 0.0f ? 0.0f : v;
-    v = v > top ? top : v;
-    return (uint32_t)v;
+    const float v = __builtin_rintf(t) + off;
+    return (uint32_t)__builtin_fminf(__builtin_fmaxf(v, 0.0f), top);
 }
 
 // Pack 32 N-bit codes into N little-endian 32-bit words.
@@ -369,7 +368,9 @@ __device__ __forceinline__ float swap_pair(float x)
 template <int CTRL>
 __device__ __forceinline__ float dppf(float x)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+    // every lane reads a valid lane in these patterns; bound_ctrl lets the compiler fold
+    // the move into the add that uses it
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // within each row of 16 lanes: lane ^ 8 (rotate by 8), lane ^ 2, lane ^ 1 (quad
 // permutes); rotate by 4 stands for lane ^ 4 once lanes l and l ^ 8 hold equal values
@@ -423,11 +424,11 @@ __global__ __launch_bounds__(256) void k_kvarn_page(AppendArgs a, int64_t pages,
         }
     }
     // stage h = 64 pairs dim i with i+64: the other half lives in the neighbouring lane
+    // (y sg + o with sg = +-1 is y + o or o - y exactly: the product is exact, so the fused
+    // form rounds once, like the sum)
+    const float sg = half ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        float o = swap_pair(y[i]);
-        y[i] = half ? (o - y[i]) : (y[i] + o);
-    }
+    for (int i = 0; i < 64; ++i) y[i] = __builtin_fmaf(y[i], sg, swap_pair(y[i]));
 
     // ---- 2. squares into the Sinkhorn tile, through LDS half a page at a time -----------
     const int lane = tid & 63;
