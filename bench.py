@@ -80,6 +80,8 @@ def parse():
     p.add_argument("--ragged-only", action="store_true", help="only the 16-sequence leg (its own JSON line)")
     p.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
                    help="chunked-prefill attention: time a CHUNK-token chunk at the end of --ctx tokens")
+    p.add_argument("--sweep", action="store_true",
+                   help="context-depth series (decode + prefill) and the 64k format sweeps")
     p.add_argument("--kld", action="store_true",
                    help="attention-fidelity sweep: median KL over query heads, format x tail x context")
     p.add_argument("--copy-probe", type=int, default=0,
@@ -294,8 +296,18 @@ def cpu_baseline(fmt, wl, ctx, tail, units):
     att(0)
     t_one = time.perf_counter() - t1
     byts = units * decode_bytes_layer(fmt, ctx, n_q, 1)
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": round(byts / t_att / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": model, "nproc": os.cpu_count(),
+        "usable_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
         "sample": "%d full-context (layer, KV head) units of the same workload (%d tokens, %s, tail %d), "
                   "one thread each: binary64 decode attention over the oracle's own encoding"
                   % (units, ctx, fmt, tail),
@@ -407,10 +419,123 @@ def prefill_bench(args):
                                    "kernel": "k_prefill + k_prefill_merge", "flops_per_call": flops}}), flush=True)
 
 
+def _fill_layers(cache, wl, L, H, ctx):
+    import torch
+    from mixed_precision_quantized_amd import synth
+    for layer in range(L):
+        t = 0
+        while t < ctx:
+            c = min(16384, ctx - t)
+            k = torch.stack([synth.kv_rows(wl, 0, layer, h, 0, t, t + c, "cuda") for h in range(H)], 1)
+            v = torch.stack([synth.kv_rows(wl, 0, layer, h, 1, t, t + c, "cuda") for h in range(H)], 1)
+            cache.append(layer, [0], [c], synth.to_bf16_bits(k).contiguous(), synth.to_bf16_bits(v).contiguous())
+            t += c
+
+
+def _decode_rate(cache, wl, fmt, L, H, QH, reps=3):
+    """Mean decode launch time over `reps` rounds of the L replica layers (events around the
+    whole round), and the KV read rate from the algorithmic bytes."""
+    import torch
+    from mixed_precision_quantized_amd import synth
+    qs = [synth.to_bf16_bits(synth.q_rows(wl, 0, l, 0, QH, "cuda")).unsqueeze(0).contiguous() for l in range(L)]
+    out = torch.empty((1, QH, 128), dtype=torch.float32, device="cuda")
+    for l in range(L):
+        cache.decode(l, [0], qs[l], out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        for l in range(L):
+            cache.decode(l, [0], qs[l], out=out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * L)
+    n, n_q = cache.seq_get(0, 0)
+    byts = decode_bytes_layer(fmt, n, n_q, H)
+    return us, byts / (us * 1e-6) / 1e9
+
+
+def _replicas(fmt, ctx, tail, H, G, floor_bytes=512e6, cap=64):
+    """Layers of one workload, each a replica of the same shape, so that one round of
+    decodes reads at least floor_bytes (more than the 256 MB last-level cache holds)."""
+    n_q = max(0, (ctx - tail) // G * G)
+    b = decode_bytes_layer(fmt, ctx, n_q, H)
+    return int(min(cap, max(1, math.ceil(floor_bytes / b))))
+
+
+def sweep(args):
+    """Context-depth series (decode and chunked prefill, kvarn4 and q4_0, tail 2048, 4k to
+    240k) and the 64k format sweeps (9 qN formats x tails 0 / 1024 / 2048 on Gaussian keys;
+    kvarn2/3/4 x tail 1024 on Student-t keys), one layer shape (8 KV heads, 32 q heads),
+    replicated over layers so that a round of decodes reads at least 512 MB."""
+    import torch
+    from mixed_precision_quantized_amd import kvq, synth
+    H, QH = 8, 32
+    depth, c2, c3 = [], [], []
+    for fmt in ("kvarn4", "q4_0"):
+        for ctx in (4096, 16384, 32768, 65536, 131072, 240000):
+            tail = 2048
+            G = 128 if fmt.startswith("kvarn") else 1
+            L = _replicas(fmt, ctx, tail, H, G)
+            cache = kvq.Cache(L, H, QH, fmt, tail_tokens=tail, n_seqs=1, max_tokens=ctx)
+            _fill_layers(cache, "c4_ctx240000_64l", L, H, ctx)
+            us, gbs = _decode_rate(cache, "c4_ctx240000_64l", fmt, L, H, QH)
+            row = {"fmt": fmt, "ctx": ctx, "tail": tail, "replicas": L, "decode_us": round(us, 2),
+                   "decode_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+            # chunked prefill: the last 512 tokens as the chunk, per layer
+            c = 512
+            q = torch.stack([synth.to_bf16_bits(synth.q_rows("c4_ctx240000_64l", 0, 0, i, QH, "cuda"))
+                             for i in range(c)], 0).contiguous()
+            ws = torch.empty(int(kvq.lib().kv_prefill_workspace_bytes(cache.h, c)), dtype=torch.uint8, device="cuda")
+            pout = torch.empty((c, QH, 128), dtype=torch.float32, device="cuda")
+            cache.prefill(0, 0, q, out=pout, ws=ws)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            stream = torch.cuda.current_stream()
+            a.record(stream)
+            for l in range(L):
+                cache.prefill(l, 0, q, out=pout, ws=ws)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / L
+            visible = sum(ctx - c + i + 1 for i in range(c))
+            tf = 4.0 * 128 * QH * visible / (ms * 1e-3) / 1e12
+            row.update({"prefill_chunk": c, "prefill_ms": round(ms, 4), "prefill_tokens_per_s": round(c / (ms * 1e-3), 1),
+                        "prefill_tflops": round(tf, 1), "prefill_pct_of_f16_peak": round(100 * tf / 2500.0, 2)})
+            depth.append(row)
+            print("  sweep depth %s %d: %s GB/s" % (fmt, ctx, row["decode_gbs"]), file=sys.stderr, flush=True)
+            del cache, ws, pout, q
+            torch.cuda.empty_cache()
+    for wl, fmts, tails, out in (("c2_sweep_ctx65536", synth.WORKLOADS["c2_sweep_ctx65536"]["fmts"], (0, 1024, 2048), c2),
+                                  ("c3_kvarn_ctx65536", ("kvarn2", "kvarn3", "kvarn4"), (1024,), c3)):
+        ctx = 65536
+        for fmt in fmts:
+            for tail in tails:
+                G = 128 if fmt.startswith("kvarn") else 1
+                L = _replicas(fmt, ctx, tail, H, G)
+                cache = kvq.Cache(L, H, QH, fmt, tail_tokens=tail, n_seqs=1, max_tokens=ctx)
+                _fill_layers(cache, wl, L, H, ctx)
+                us, gbs = _decode_rate(cache, wl, fmt, L, H, QH)
+                out.append({"fmt": fmt, "tail": tail, "replicas": L, "decode_us": round(us, 2),
+                            "decode_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)})
+                del cache
+                torch.cuda.empty_cache()
+        print("  sweep %s done" % wl, file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "decode KV read GB/s and chunked-prefill rate over context depth; 64k format sweeps",
+                      "data": "synthetic", "device": torch.cuda.get_device_name(0),
+                      "config": {"workload": "1 layer shape x 8 KV heads x 32 q heads x d128, batch 1, replicated over "
+                                             "layers so that one round of decodes reads >= 512 MB"},
+                      "depth": depth, "c2_sweep_64k": c2, "c3_kvarn_64k": c3}), flush=True)
+
+
 def main():
     args = parse()
     if args.kld:
         kld_sweep(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
     if args.prefill:
         prefill_bench(args)
