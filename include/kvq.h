@@ -129,6 +129,9 @@ int kv_cache_destroy(kv_cache* cache);
  * zero as +0).  Tokens that fall below the tail boundary
  * n_q = max(n_q, G*floor(max(0, n-T)/G)) are encoded with the stream's format (G = 128
  * when a format is KVarN: whole pages, else 1), newer ones are written to the 16-bit ring.
+ * Values must be finite, and their canonical form too (an fp32 input beyond the largest
+ * bf16 rounds to infinity): the encodings are defined for finite values only, and a block
+ * holding a NaN or an infinity gets unspecified codes and scales.
  * Errors: KV_EINVAL (bad layer/seq/ids/pointers/dtype), KV_ENOSPC (capacity), and with
  * layer == -1, KV_EINVAL if the layers of a sequence disagree on their token counts;
  * KV_EDEVICE if a launch fails. */

@@ -107,16 +107,36 @@ __device__ __forceinline__ void pack32(const uint32_t (&u)[32], uint32_t (&w)[N]
     }
 }
 
+// Largest and smallest of a block.  The inputs are finite (no NaN), so the hardware
+// max/min give the same values as a scan with strict comparisons, except possibly for the
+// sign of a zero extreme, which changes no scale and no code: a zero signed maximum gives
+// d = fp16(+-0) = +0 (all codes at the offset), a zero range gives step +0, and the stored
+// minimum is fp16(+-0) = +0 either way.
+__device__ __forceinline__ void block_max_min(const float (&x)[32], float& mx, float& mn)
+{
+    float a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = __builtin_fmaxf(__builtin_fmaxf(x[i], x[i + 8]), __builtin_fmaxf(x[i + 16], x[i + 24]));
+        b[i] = __builtin_fminf(__builtin_fminf(x[i], x[i + 8]), __builtin_fminf(x[i + 16], x[i + 24]));
+    }
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) {
+            a[i] = __builtin_fmaxf(a[i], a[i + w]);
+            b[i] = __builtin_fminf(b[i], b[i + w]);
+        }
+    mx = a[0];
+    mn = b[0];
+}
+
 // Symmetric block encoder: returns the fp16 scale bits, fills 32 codes.
 template <int N>
 __device__ __forceinline__ uint32_t encode_block_q0(const float (&x)[32], uint32_t (&u)[32])
 {
-    float mx = x[0], mn = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) {
-        mx = x[i] > mx ? x[i] : mx;
-        mn = x[i] < mn ? x[i] : mn;
-    }
+    float mx, mn;
+    block_max_min(x, mx, mn);
     const float m = (mx >= -mn) ? mx : mn;
     const float qd = m / -(float)(1 << (N - 1));
     const uint32_t d = fp16s_rne(qd);
@@ -136,12 +156,8 @@ __device__ __forceinline__ uint32_t encode_block_q0(const float (&x)[32], uint32
 template <int N>
 __device__ __forceinline__ uint32_t encode_block_q1(const float (&x)[32], uint32_t (&u)[32])
 {
-    float mx = x[0], mn = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) {
-        mx = x[i] > mx ? x[i] : mx;
-        mn = x[i] < mn ? x[i] : mn;
-    }
+    float mx, mn;
+    block_max_min(x, mx, mn);
     const float top = (float)((1 << N) - 1);
     const float dr = mx - mn;
     const float dq = dr / top;
