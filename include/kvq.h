@@ -187,7 +187,8 @@ int64_t kv_prefill_workspace_bytes(const kv_cache* cache, int32_t n_new);
  * out: float32 [n_new][n_q_heads][128].  The step on the other side of append: prefill and
  * decode are measured separately ("Форк beellama и KV-кванты kvarn на длинном контексте",
  * the section on how to compare builds).  Reads the cache only.  Errors: KV_EINVAL
- * (n_new < 1 or n_new > n), KV_EEMPTY (n == 0), KV_ESIZE (workspace). */
+ * (n_new < 1 or n_new > n), KV_EEMPTY (n == 0), KV_ESIZE (workspace), KV_EUNSUPPORTED
+ * (a ring of 8,388,608 slots or more: 2 GiB of 16-bit rows per stream). */
 int kv_prefill_attn(kv_cache* cache, int32_t layer, int32_t seq_id, int32_t n_new, const void* q,
                     int32_t q_dtype, float softmax_scale, float* out, void* workspace,
                     int64_t ws_bytes, void* stream);

@@ -396,6 +396,8 @@ int kv_prefill_attn(kv_cache* c, int32_t layer, int32_t seq_id, int32_t n_new, c
     if (n == 0) return KV_EEMPTY;
     if (n_new < 1 || n_new > n) return KV_EINVAL;
     if (ws_bytes < kv_prefill_workspace_bytes(c, n_new)) return KV_ESIZE;
+    // the ring is read through one buffer resource with 32-bit offsets
+    if (c->ring_slots * 256 >= (int64_t(1) << 31)) return KV_EUNSUPPORTED;
     PrefillArgs a;
     std::memset(&a, 0, sizeof(a));
     a.g = c->geom;

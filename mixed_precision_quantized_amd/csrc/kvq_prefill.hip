@@ -100,11 +100,15 @@ __device__ __forceinline__ void pf_wait_vm0()
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0) only
 }
 
-// Loop-invariant buffer resources of one stream over the split's region (rows past its
-// end read as zero) and the issue of one block's loads into R (every wave: 2 x 64 chunks
-// per stream; chunk c of a block = bytes 16 c of its rows).
+// One stream's bases and the issue of one block's loads into R (every wave: 2 x 64 chunks
+// per stream; chunk c of a block = bytes 16 c of its rows).  Quantized rows: a buffer
+// resource per block, from a 64-bit base (rows past the block's valid ones read as zero),
+// so no offset grows with the context; ring rows: one resource over the ring.
 struct PfStream {
-    pf_rsrc_t rows, scales, chan;
+    pf_rsrc_t ring_rows;    // ring streams
+    const char* codes;      // quantized streams: rows, block scales, channel scales
+    const char* scales;
+    const char* chan;
     int rb, sb;             // code (or BF16) bytes per row, scale bytes per row
     bool ring;
 };
@@ -116,14 +120,11 @@ __device__ __forceinline__ PfStream pf_stream_rsrc(const PrefillArgs& a, const c
     S.ring = !quant;
     S.rb = quant && !exact ? 16 * fbits(fmt) : 256;
     S.sb = kind_affine(fkind(fmt)) ? 16 : 8;
-    if (quant) {
-        S.rows = pf_rsrc(st + Ls.codes, (int)(a.n_q * S.rb));
-        S.scales = pf_rsrc(st + Ls.scales, exact ? 0 : (int)(a.n_q * S.sb));
-        S.chan = pf_rsrc(st + (Ls.cscale >= 0 ? Ls.cscale : 0), kind_paged(fkind(fmt)) ? (int)((a.n_q + kPage - 1) / kPage * 256) : 0);
-    } else {
-        S.rows = pf_rsrc(st + Ls.ring, a.g.ring_slots * 256);
-        S.scales = S.chan = S.rows;
-    }
+    S.codes = st + Ls.codes;
+    S.scales = st + Ls.scales;
+    S.chan = st + (Ls.cscale >= 0 ? Ls.cscale : 0);
+    S.ring_rows = pf_rsrc(st + Ls.ring, quant ? 0 : a.g.ring_slots * 256);
+    (void)exact;
     return S;
 }
 
@@ -137,14 +138,16 @@ __device__ __forceinline__ void pf_dma(PfRawL<BIG>& R, const PrefillArgs& a, con
                       int swave, int cwave) {
         if (!RING) {
             // the block's 2 rb chunks of 16 B (256 for codes of 8 bits or less: one per thread)
-            const int base = (int)tb * S.rb;
+            const pf_rsrc_t rows = pf_rsrc(S.codes + tb * S.rb, nt * S.rb);
 #pragma unroll
             for (int i = 0; i < (BIG ? 2 : 1); ++i) {
                 const int c0 = 64 * (wave + 4 * i);
-                if (c0 + lane < 2 * S.rb) pf_dma16(S.rows, base + 16 * (c0 + lane), dst + 16 * c0);
+                if (c0 + lane < 2 * S.rb) pf_dma16(rows, 16 * (c0 + lane), dst + 16 * c0);
             }
-            if (coded && wave == swave && lane < 32) pf_dma16(S.scales, (int)tb * S.sb + 16 * lane, sdst);
-            if (kvarn && wave == cwave && lane < 16) pf_dma16(S.chan, (int)(tb / kPage) * 256 + 16 * lane, cdst);
+            if (coded && wave == swave && lane < 32)
+                pf_dma16(pf_rsrc(S.scales + tb * S.sb, nt * S.sb), 16 * lane, sdst);
+            if (kvarn && wave == cwave && lane < 16)
+                pf_dma16(pf_rsrc(S.chan + (tb / kPage) * 256, 256), 16 * lane, cdst);
         } else {
             // ring rows: slot (t mod R); rows past nt read past the resource (zero)
             const int R = a.g.ring_slots;
@@ -152,7 +155,7 @@ __device__ __forceinline__ void pf_dma(PfRawL<BIG>& R, const PrefillArgs& a, con
             for (int i = 0; i < 2; ++i) {
                 const int c0 = 64 * (wave + 4 * i), c = c0 + lane, r = c >> 4;
                 const int voff = r < nt ? (int)((tb + r) % R) * 256 + 16 * (c & 15) : R * 256;
-                pf_dma16(S.rows, voff, dst + 16 * c0);
+                pf_dma16(S.ring_rows, voff, dst + 16 * c0);
             }
         }
     };

@@ -11,6 +11,7 @@ device memory and the stream.  There is no CPU fallback: if the library is not b
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -112,6 +113,13 @@ def _ids(xs):
     return arr
 
 
+def _on(stream):
+    """Allocation context for buffers a call on `stream` uses: torch's caching allocator
+    then ties them to that stream, so a buffer freed after the call is reused only by work
+    ordered after the kernels that read or write it."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -186,12 +194,15 @@ class Cache:
         _check(rc, "kv_append")
 
     def decode(self, layer, seq_ids, q, softmax_scale=None, out=None, stream=None):
-        """q: device [n_seqs][n_q_heads][128] bfloat16/float32 -> float32 output."""
+        """q: device [n_seqs][n_q_heads][128] bfloat16/float32 -> float32 output.  The
+        cache's one decode workspace serves every call: calls on different streams must be
+        ordered by the caller (events), as the C ABI requires."""
         assert q.is_contiguous()
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(128)
         if out is None:
-            out = torch.empty((len(seq_ids), self.cfg.n_q_heads, 128), dtype=torch.float32, device=q.device)
+            with _on(stream):
+                out = torch.empty((len(seq_ids), self.cfg.n_q_heads, 128), dtype=torch.float32, device=q.device)
         dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
         rc = lib().kv_decode_attn(self.h, int(layer), len(seq_ids), _ids(seq_ids),
                                   ctypes.c_void_p(q.data_ptr()), dt, float(softmax_scale),
@@ -223,9 +234,11 @@ class Cache:
         if ws is None:
             n_ws = int(lib().kv_prefill_workspace_bytes(self.h, n_new))
             _check(n_ws if n_ws < 0 else 0, "kv_prefill_workspace_bytes")
-            ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
+            with _on(stream):
+                ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
         if out is None:
-            out = torch.empty((n_new, self.cfg.n_q_heads, 128), dtype=torch.float32, device=q.device)
+            with _on(stream):
+                out = torch.empty((n_new, self.cfg.n_q_heads, 128), dtype=torch.float32, device=q.device)
         dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
         rc = lib().kv_prefill_attn(self.h, int(layer), int(seq_id), n_new, ctypes.c_void_p(q.data_ptr()), dt,
                                    float(softmax_scale), ctypes.c_void_p(out.data_ptr()),
@@ -242,8 +255,9 @@ class Cache:
             softmax_scale = 1.0 / math.sqrt(128)
         n_ws = int(lib().kv_attn_kld_workspace_bytes(self.h))
         _check(n_ws if n_ws < 0 else 0, "kv_attn_kld_workspace_bytes")
-        ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
-        out = torch.empty(self.cfg.n_q_heads, dtype=torch.float32, device=q.device)
+        with _on(stream):
+            ws = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=q.device)
+            out = torch.empty(self.cfg.n_q_heads, dtype=torch.float32, device=q.device)
         dt = IN_BF16 if q.dtype == torch.bfloat16 else IN_F32
         rc = lib().kv_attn_kld(self.h, int(layer), int(seq_id), ctypes.c_void_p(q.data_ptr()), dt,
                                float(softmax_scale), ctypes.c_void_p(k_ref.data_ptr()),

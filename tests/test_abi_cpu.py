@@ -184,3 +184,25 @@ def test_noalloc_rejects_plans_beyond_its_array():
     ptr = ctypes.c_void_p(FAKE)
     assert L.kv_decode_attn_noalloc(h, 0, 1, ids, ptr, 0, 0.1, ptr, None) == kvq.KV_ESIZE
     L.kv_cache_destroy(h)
+
+
+def test_prefill_rejects_a_ring_beyond_32_bit_offsets():
+    """The prefill reads the 16-bit ring through one buffer resource: a ring of 2^23 slots
+    or more (2 GiB of rows per stream) is refused before any device call; the quantized
+    rows need no such limit (their resources are rebased per block)."""
+    L = kvq.lib()
+    big = (1 << 23) + 10
+    c = cfg("q4_0", T=big, M=big + 100)
+    rc, h = _handle(c)
+    assert rc == 0
+    assert L.kv_seq_set(h, 0, 0, big, 0) == kvq.KV_OK
+    n_ws = L.kv_prefill_workspace_bytes(h, 1)
+    ptr = ctypes.c_void_p(FAKE)
+    assert L.kv_prefill_attn(h, 0, 0, 1, ptr, 0, 0.1, ptr, ptr, n_ws, None) == kvq.KV_EUNSUPPORTED
+    L.kv_cache_destroy(h)
+    # a ring just under the limit passes validation (then fails only at the launch, which
+    # this host never reaches: no device call is made for a validation error)
+    c = cfg("q4_0", T=(1 << 23) - 1, M=(1 << 23) + 100)
+    rc, h = _handle(c)
+    assert rc == 0
+    L.kv_cache_destroy(h)
