@@ -13,6 +13,8 @@
 //   after a spill with keep tokens n_q = max(n_q, G*floor(max(0, n - keep)/G));
 //   token p with n_q <= p < n lives in ring slot p mod R, R = G*ceil((T+G-1)/G).
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -94,6 +96,26 @@ int64_t nq_after(int64_t nq, int64_t n, int64_t keep, int64_t G)
 }
 
 // Validates a configuration; fills the geometry (without base pointer) and total bytes.
+// KV_LOG (environment): 1 prints each cache's configuration at creation, 2 also every
+// decode call's split plan, to stderr.
+int log_level()
+{
+    static const int level = [] {
+        const char* e = std::getenv("KV_LOG");
+        return e ? std::atoi(e) : 0;
+    }();
+    return level;
+}
+
+const char* format_name(int f)
+{
+    static const char* const names[KV_NUM_FORMATS] = {
+        "bf16", "q2_0", "q2_1", "q3_0", "q3_1", "q4_0", "q4_1", "q5_0", "q5_1", "q6_0", "q6_1",
+        "q8_0", "q8_1", "kvarn2", "kvarn3", "kvarn4", "kvarn5", "kvarn6", "kvarn8", "kvarn2_1",
+        "kvarn3_1", "kvarn4_1", "kvarn5_1", "kvarn6_1", "kvarn8_1"};
+    return f >= 0 && f < KV_NUM_FORMATS ? names[f] : "?";
+}
+
 int plan_config(const kv_config* cfg, CacheGeom* geom, int64_t* total, int64_t* G,
                 int64_t* R, int64_t* tok_pad)
 {
@@ -294,6 +316,13 @@ int kv_cache_init(const kv_config* cfg, void* dev_mem, int64_t bytes, kv_cache**
     size_t cells = (size_t)cfg->n_seqs * cfg->n_layers;
     c->n.assign(cells, 0);
     c->nq.assign(cells, 0);
+    if (log_level() >= 1)
+        std::fprintf(stderr,
+                     "kvq: cache keys %s values %s, tail %d (%s), granule %lld, ring %lld slots, %d layers x "
+                     "%d KV heads x %d q heads, %d sequences x %lld tokens, %lld bytes\n",
+                     format_name(cfg->fmt_k), format_name(cfg->fmt_v), cfg->tail_tokens,
+                     cfg->tail_dtype == KV_TAIL_F16 ? "f16" : "bf16", (long long)G, (long long)R, cfg->n_layers,
+                     cfg->n_kv_heads, cfg->n_q_heads, cfg->n_seqs, (long long)cfg->max_tokens, (long long)total);
     *out = c;
     return KV_OK;
 }
@@ -570,6 +599,12 @@ int decode_launch(kv_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq
         tb += H * a.seqs[i].splits_t;
     }
     a.q_wgs = qb;
+    if (log_level() >= 2)
+        std::fprintf(stderr,
+                     "kvq: decode layer %d, %d sequences: %lld workgroups (%d quantized, %lld ring; %lld waves), "
+                     "%lld pages or %lld ring units per workgroup\n",
+                     layer, n_seqs, (long long)wgs, qb, (long long)(wgs - qb), (long long)waves, (long long)upw,
+                     (long long)upw_t);
     int rc = launch_decode(a, (int)wgs, stream);
     return rc ? KV_EDEVICE : KV_OK;
 }

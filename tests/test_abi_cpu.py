@@ -206,3 +206,25 @@ def test_prefill_rejects_a_ring_beyond_32_bit_offsets():
     rc, h = _handle(c)
     assert rc == 0
     L.kv_cache_destroy(h)
+
+
+def test_kv_log_prints_the_configuration():
+    """KV_LOG=1 prints each cache's formats, tail, granule, ring and size at creation (to
+    stderr); unset, the library prints nothing."""
+    import subprocess
+    import sys
+    code = ("import ctypes; from mixed_precision_quantized_amd import kvq; "
+            "c = kvq.make_config(2, 8, 32, 'kvarn4', 'q4_0', 1024, 3, 5000); h = ctypes.c_void_p(); "
+            "print(kvq.lib().kv_cache_init(ctypes.byref(c), ctypes.c_void_p(%d), kvq.cache_bytes(c), "
+            "ctypes.byref(h)))" % FAKE)
+    env = dict(os.environ, KV_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stderr[-2000:]
+    line = [l for l in r.stderr.splitlines() if l.startswith("kvq: cache")]
+    assert len(line) == 1, r.stderr
+    for part in ("keys kvarn4", "values q4_0", "tail 1024 (bf16)", "granule 128", "2 layers x 8 KV heads x 32 q heads",
+                 "3 sequences x 5000 tokens"):
+        assert part in line[0], line[0]
+    env.pop("KV_LOG")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert "kvq:" not in r.stderr
