@@ -59,6 +59,7 @@ struct alignas(16) PfLds {
     float dk[4][kPfKB];             // key block scales [block][token] (1 for exact rows)
     float mk[4][kPfKB];             // key block minima (affine codes)
     float ck[kD];                   // KVarN key channel scales of the block's page
+    int kscaled[4];                 // per key-unpacking wave: some 16-bit row was range-scaled
 };
 
 __device__ __forceinline__ const char* pf_stream(const CacheGeom& g, int seq, int layer, int head, int isv)
@@ -237,12 +238,15 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             kx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
             kx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
         }
-        // the block's largest |k| (its other half is in the neighbouring lane) to [2^14, 2^15)
+        // a block whose largest |k| (its other half is in the neighbouring lane) lies outside
+        // [2^-10, 2^15) is scaled to [2^14, 2^15): binary16 then holds its large elements
+        // without overflow and its small ones to 2^-25 of the block maximum or better, as
+        // it does unscaled inside that range
         float amax = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(kx[e]));
         amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, false)));
-        if (amax > 0.0f) {
+        if (amax > 0.0f && !(amax >= 0x1p-10f && amax < 32768.0f)) {
             const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
             const int sh = min(126, max(-126, (ex == 0 ? 1 : ex) - 127 - 14));
             const float f = __builtin_ldexpf(1.0f, -sh);
@@ -320,6 +324,11 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
     if (DK && (pp & 1) == 0) {
         L.dk[b][r] = d;
         L.mk[b][r] = m;
+    }
+    if (DK) {
+        // 16-bit rows: whether any row of the block took a scale (else the scores skip dk)
+        const bool any = __builtin_amdgcn_ballot_w64(d != 1.0f) != 0;
+        if ((tid & 63) == 0) L.kscaled[(tid >> 6) & 3] = any ? 1 : 0;
     }
     if (DK && kind_paged(KK) && !RING && tid < kD) L.ck[tid] = fp16_to_f32(R.kch[tid]);
 }
@@ -495,6 +504,21 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Sacc[r] = 0.0f;
         constexpr bool aff_k = !RING && kind_affine(KK);
+        constexpr bool exact_k = RING || KK == KIND_BF16;
+        if (exact_k && !(B.kscaled[0] | B.kscaled[1] | B.kscaled[2] | B.kscaled[3])) {
+            // 16-bit rows, none scaled: one accumulator over the four blocks
+            f32x16 T;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) T[r] = 0.0f;
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx) {
+                const h8 A = *(const h8*)&B.kc[j][16 * idx + 8 * hh];
+                T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qb[idx], T, 0, 0, 0);
+                T = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, ql[idx], T, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Sacc[r] = T[r];
+        } else
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             f32x16 T;
