@@ -60,6 +60,32 @@ def measured_traffic(fmt, ctx, tail, kv_heads):
     return None
 
 
+APPEND_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "append_ragged16_kvarn3.md")
+APPEND_SOURCES = ["kvq_append.hip", "kvq_host.cpp", "kvq_internal.h", "kvq_device.h"]
+
+
+def measured_append_traffic():
+    """HBM bytes of one 16-sequence append step from the committed counter summary, or None
+    when the append sources changed since it was taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in APPEND_SOURCES:
+        with open(os.path.join(ROOT, "mixed_precision_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        lines = open(APPEND_TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        parts = line.split()
+        if parts[:1] != ["append_traffic_per_step"]:
+            continue
+        kv = dict(x.split("=", 1) for x in parts[1:])
+        if kv.get("sources_sha256") == h.hexdigest():
+            return int(kv["bytes"])
+    return None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -211,8 +237,9 @@ def ragged_leg(args):
         "tokens_per_s": round(tps, 1), "unit": "sequence-tokens/s", "ms_per_step": round(a_ms, 4),
         "bytes_per_stream_token": bst, "bytes_per_sequence_token": bst * streams,
         "roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "one 64-layer append call (ring write, spill, page encode)"},
+                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": measured_append_traffic(),
+                     "kernel": "one 64-layer append call (ring write, spill, page encode)",
+                     "bytes_per_step": int(tokens * streams * bst)},
         "alu_roof": {"bound": "alu", "achieved": round(alu / 1e12, 3), "peak": round(ALU_PEAK_LANE_OPS / 1e12, 3),
                      "unit": "T lane-ops/s", "frac": round(alu / ALU_PEAK_LANE_OPS, 4),
                      "ops_per_stream_token": KVARN_OPS_PER_STREAM_TOKEN if ops else 0},
