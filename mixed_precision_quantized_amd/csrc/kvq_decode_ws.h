@@ -22,13 +22,14 @@
 //     block, digit) and whose other operand is the unpacked codes (one byte each, in an
 //     order fixed per code width that the query operand follows), so each lane scores one
 //     head of one token.  The integer dot products are exact; the two 32-bit parts meet
-//     in binary32, the code offset's share (o S sum(q_int)) is subtracted there, and the
-//     per-(token, block) scale applies afterwards.  Codes and scales go to registers,
-//     three steps in flight, through buffer loads that read rows past the end of a page
-//     as zero.
+//     in binary32, the code offset's share (o S sum(q_int)) is subtracted there (for KVarN
+//     keys inside the integer sums), and the per-(token, block) scale applies afterwards.
+//     Codes and scales go to registers, two or three steps in flight, through buffer loads
+//     (non-temporal) that read rows past the end of a page as zero.
 //  V: v_mfma_f32_4x4x4_16b_f16, one 4x4x4 block per (4-token group, 32-dim block): A =
-//     the binary16 weights (2^15 p)(d 2^e) of the four heads (2^e a power of two per lane
-//     quad that keeps every weight between 2^12 and far above the binary16 subnormals),
+//     the binary16 weights (2^15 p)(d 2^e) of the four heads (2^e a power of two uniform
+//     over the wave, lowered when a larger block scale arrives, which keeps every weight
+//     below 2^12 and far above the binary16 subnormals),
 //     B = the centred codes 2^s (u - o) of one
 //     dim per column as exact binary16 integers (v_perm interleaves the bytes of a token
 //     pair; masking a code in place at bit offset s and or-ing 0x6400 gives 1024 + 2^s u,
