@@ -39,7 +39,8 @@
  *
  * Conventions for every call:
  *  - Ownership: the library never allocates or frees device memory.  The cache buffer,
- *    inputs, outputs and the decode workspace are caller-owned device memory.  Host
+ *    inputs, outputs and the decode workspace are caller-owned device memory (the one
+ *    exception, kv_decode_attn_noalloc, uses a fixed array of the library's code object).  Host
  *    arrays (seq_ids, n_new) are read during the call only.
  *  - Asynchrony: device work is enqueued on `stream` (a hipStream_t passed as void*;
  *    NULL = the default stream) and the call returns after enqueueing.  Host metadata
@@ -164,7 +165,8 @@ int kv_decode_attn(kv_cache* cache, int32_t layer, int32_t n_seqs, const int32_t
  * with which it shares its kernels.  The split partials go to a fixed array inside the
  * library: 1024 partials, 4,259,840 bytes per device, held from the first call on that
  * device until the process ends; the split plan is capped at 1024 workgroups (the fast
- * kernel's plans use 256 per 256 compute units).  Errors: as kv_decode_attn, plus KV_ESIZE
+ * kernel's plans use one per compute unit, up to four per compute unit when many
+ * sequences and KV heads are decoded together).  Errors: as kv_decode_attn, plus KV_ESIZE
  * when even the smallest plan (2 workgroups per sequence and KV head) exceeds the array,
  * KV_EDEVICE if the array cannot be located.  Every call on one device uses that same
  * array: calls that overlap on one device (other streams, other threads) race and must be
