@@ -50,6 +50,7 @@ constexpr int kG = 4;
 constexpr float kNeg = -1.0e30f;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct alignas(16) PfLds {
@@ -193,6 +194,59 @@ __device__ __forceinline__ void unpack16_rt(int N, const uint8_t* row, int part,
     }
 }
 
+// Codes of 2, 4 or 8 bits: the 16 codes of part `part` of a row as eight binary16 pairs
+// (dims 2i, 2i + 1) holding u - off exactly.  The byte that holds a pair is copied to both
+// halves of a word (v_perm); a mask keeps one code per half, at bit 0 in the low half and
+// at bit s in the high one, under the exponent bits of 1024 (ulp 1 in [1024, 2048)); one
+// binary16 fma then scales by 2^-s and subtracts 1024 + off.  Every step is exact.
+template <int N>
+__device__ __forceinline__ void codes_h2(const uint8_t* row, int part, float off, h2 (&o)[8])
+{
+    static_assert(N == 2 || N == 4 || N == 8, "2-, 4- or 8-bit codes");
+    const uint32_t* p = (const uint32_t*)(row + 2 * N * part);
+    const _Float16 a0 = (_Float16)(-1024.0f - off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t x;
+        h2 sc, ad;
+        if constexpr (N == 8) {
+            // bytes 2i, 2i + 1 under the exponent byte 0x64
+            const uint32_t b = 2 * (i & 1);
+            x = __builtin_amdgcn_perm(0x64646464u, p[i >> 1], b | (4u << 8) | ((b + 1) << 16) | (4u << 24));
+            sc = (h2){(_Float16)1.0f, (_Float16)1.0f};
+            ad = (h2){a0, a0};
+        } else if constexpr (N == 4) {
+            const uint32_t b = i & 3;
+            x = __builtin_amdgcn_perm(p[i >> 2], p[i >> 2], b * 0x01010101u);
+            x = (x & 0x00F0000Fu) | 0x64006400u;
+            sc = (h2){(_Float16)1.0f, (_Float16)0.0625f};
+            ad = (h2){a0, (_Float16)(-64.0f - off)};
+        } else {
+            const uint32_t b = (i >> 1) & 3;
+            x = __builtin_amdgcn_perm(p[i >> 3], p[i >> 3], b * 0x01010101u);
+            if (i & 1) {
+                x = (x & 0x00C00030u) | 0x64006400u;
+                sc = (h2){(_Float16)0.0625f, (_Float16)0.015625f};
+                ad = (h2){(_Float16)(-64.0f - off), (_Float16)(-16.0f - off)};
+            } else {
+                x = (x & 0x000C0003u) | 0x64006400u;
+                sc = (h2){(_Float16)1.0f, (_Float16)0.25f};
+                ad = (h2){a0, (_Float16)(-256.0f - off)};
+            }
+        }
+        o[i] = __builtin_elementwise_fma(__builtin_bit_cast(h2, x), sc, ad);
+    }
+}
+__device__ __forceinline__ bool codes_h2_rt(int N, const uint8_t* row, int part, float off, h2 (&o)[8])
+{
+    switch (N) {
+    case 2: codes_h2<2>(row, part, off, o); return true;
+    case 4: codes_h2<4>(row, part, off, o); return true;
+    case 8: codes_h2<8>(row, part, off, o); return true;
+    default: return false;
+    }
+}
+
 // Unpack a raw block into the operand buffers.  Thread tid (0..255): token r, dims 16 pp ..
 // of the keys (PART 1), the values (PART 2) or both (PART 0); r = tid >> 3, pp = tid & 7,
 // except for values alone (r = tid & 31, pp = tid >> 5).
@@ -208,7 +262,48 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
     const bool valid = r < nt;
     float kx[16], vx[16];
     float d = 1.0f, m = 0.0f;
-    if (!DK) {
+    bool kdone = false;     // keys already stored (2-, 4- and 8-bit codes in binary16 pairs)
+    if (DK && quant && KK != KIND_BF16) {
+        if (kind_affine(KK)) {
+            const uint32_t dm = *(const uint32_t*)(R.ks + r * 16 + 4 * b);
+            d = fp16_to_f32(dm & 0xFFFFu);
+            m = fp16_to_f32(dm >> 16);
+        } else {
+            d = fp16_to_f32(*(const uint16_t*)(R.ks + r * 8 + 2 * b));
+        }
+        const int N = fbits(g.fmt_k);
+        h2 uo[8];
+        // (not for kvarnN_1 streams: their kernel is the one short of registers, and the
+        // binary32 route spills less there)
+        if (KK != KIND_KVARN1 && codes_h2_rt(N, R.k + r * 16 * N, pp, kind_affine(KK) ? 0.0f : (float)(1 << (N - 1)), uo)) {
+            kdone = true;
+            uint32_t w[8], wl[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (kind_paged(KK) && !RING) {
+                    // c (u - o) rounded to binary16, and its exact remainder: the same two
+                    // terms as the binary32 route below (the product is exact there)
+                    const h2 c2 = ((const h2*)R.kch)[8 * pp + i];
+                    const h2 hi = uo[i] * c2;
+                    const h2 lo = __builtin_elementwise_fma(uo[i], c2, -hi);
+                    w[i] = valid ? __builtin_bit_cast(uint32_t, hi) : 0u;
+                    wl[i] = valid ? __builtin_bit_cast(uint32_t, lo) : 0u;
+                } else {
+                    w[i] = valid ? __builtin_bit_cast(uint32_t, uo[i]) : 0u;
+                    wl[i] = 0u;
+                }
+            }
+            uint4* dst = (uint4*)&L.kc[r][16 * pp];
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            if (kind_paged(KK) && !RING) {
+                uint4* dl = (uint4*)&L.kl[r][16 * pp];
+                dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+                dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+            }
+        }
+    }
+    if (!DK || kdone) {
     } else if (quant && KK != KIND_BF16) {
         const int N = fbits(g.fmt_k);
         uint32_t u[16];
@@ -221,13 +316,6 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             // (11 + N significant bits) and splits into two exact binary16 terms
 #pragma unroll
             for (int e = 0; e < 16; ++e) kx[e] *= fp16_to_f32(R.kch[16 * pp + e]);
-        }
-        if (kind_affine(KK)) {
-            const uint32_t dm = *(const uint32_t*)(R.ks + r * 16 + 4 * b);
-            d = fp16_to_f32(dm & 0xFFFFu);
-            m = fp16_to_f32(dm >> 16);
-        } else {
-            d = fp16_to_f32(*(const uint16_t*)(R.ks + r * 8 + 2 * b));
         }
     } else {
         const uint4* q = (const uint4*)(R.k + r * 256 + 32 * pp);
@@ -255,22 +343,36 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
             d = __builtin_ldexpf(1.0f, sh);
         }
     }
+    // values: the power of two vmul enters with the block scale and minimum (exact: the
+    // results are those of scaling afterwards, nothing here leaves the binary32 range)
     if (!DV) {
     } else if (quant && KV != KIND_BF16) {
         const int N = fbits(g.fmt_v);
-        uint32_t u[16];
-        unpack16_rt(N, R.v + r * 16 * N, pp, u);
+        const float off = kind_affine(KV) ? 0.0f : (float)(1 << (N - 1));
+        float dv, mv = 0.0f;
         if (kind_affine(KV)) {
             const uint32_t dm = *(const uint32_t*)(R.vs + r * 16 + 4 * b);
-            const float dv = fp16_to_f32(dm & 0xFFFFu), mv = fp16_to_f32(dm >> 16);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) vx[e] = fmaf(dv, (float)u[e], mv);
+            dv = fp16_to_f32(dm & 0xFFFFu) * vmul;
+            mv = fp16_to_f32(dm >> 16) * vmul;
         } else {
-            const float dv = fp16_to_f32(*(const uint16_t*)(R.vs + r * 8 + 2 * b));
-            const float off = (float)(1 << (N - 1));
-#pragma unroll
-            for (int e = 0; e < 16; ++e) vx[e] = ((float)u[e] - off) * dv;
+            dv = fp16_to_f32(*(const uint16_t*)(R.vs + r * 8 + 2 * b)) * vmul;
         }
+        h2 uo[8];
+        if (KV != KIND_KVARN1 && codes_h2_rt(N, R.v + r * 16 * N, pp, off, uo)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                vx[2 * i] = (float)uo[i].x;
+                vx[2 * i + 1] = (float)uo[i].y;
+            }
+        } else {
+            uint32_t u[16];
+            unpack16_rt(N, R.v + r * 16 * N, pp, u);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) vx[e] = (float)u[e] - off;
+        }
+        // affine: d u + m in one rounding; symmetric: (u - o) d, exact
+#pragma unroll
+        for (int e = 0; e < 16; ++e) vx[e] = kind_affine(KV) ? fmaf(dv, vx[e], mv) : vx[e] * dv;
         if (kind_paged(KV)) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) vx[e] *= fp16_to_f32(R.vch[16 * pp + e]);
@@ -281,20 +383,15 @@ __device__ __forceinline__ void pf_unpack(PfLds& L, const PfRawL<BIG>& R, const 
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            vx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16);
-            vx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16);
+            vx[2 * i] = canon_to_f32(w[i] & 0xFFFFu, !quant && g.tail_f16) * vmul;
+            vx[2 * i + 1] = canon_to_f32(w[i] >> 16, !quant && g.tail_f16) * vmul;
         }
-    }
-    if (DV) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) vx[e] *= vmul;
     }
     if (!valid) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) { kx[e] = 0.0f; vx[e] = 0.0f; }
     }
-    if (DK) {
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    if (DK && !kdone) {
         uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -550,32 +647,40 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Sacc[r] *= qmul;
-        // mask: rows past the block's end, and keys later than the query (only blocks that
-        // reach the tile's first query or end early need it; unused query slots are never
-        // read back)
+        // The scores are Sacc qmul (qmul a power of two, so the product is exact and the
+        // maximum may be taken before it).  Masked blocks: rows past the block's end, and keys
+        // later than the query (only blocks that reach the tile's first query or end early;
+        // unused query slots are never read back).
+        float mx = kNeg, mn;
+        float ps = 0.0f;
+        float p[16];
         if (nt < kPfKB || tb + kPfKB - 1 > pos_min) {
             const int lim = (int)min<int64_t>(nt - 1, pos - tb);      // last visible row
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (i > lim) Sacc[r] = kNeg;
+                Sacc[r] = i > lim ? kNeg : Sacc[r] * qmul;
+                mx = fmaxf(mx, Sacc[r]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mn = fmaxf(mrun, mx);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = Sacc[r] > 0.5f * kNeg ? __builtin_amdgcn_exp2f(Sacc[r] - mn) : 0.0f;
+                ps += p[r];
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sacc[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * qmul;
+            mn = fmaxf(mrun, mx);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(Sacc[r], qmul, -mn));
+                ps += p[r];
             }
         }
-        float mx = kNeg;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sacc[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(mrun, mx);
         const float al = __builtin_amdgcn_exp2f(mrun - mn);
-        float ps = 0.0f;
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = Sacc[r] > 0.5f * kNeg ? __builtin_amdgcn_exp2f(Sacc[r] - mn) : 0.0f;
-            ps += p[r];
-        }
         ps += __shfl_xor(ps, 32);
         lrun = fmaf(lrun, al, ps);
         mrun = mn;
