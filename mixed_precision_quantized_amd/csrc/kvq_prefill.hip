@@ -63,6 +63,20 @@ struct alignas(16) PfLds {
     int kscaled[4];                 // per key-unpacking wave: some 16-bit row was range-scaled
 };
 
+// The two halves of the wave exchanged by v_permlane32_swap (no LDS round trip): with both
+// operands x, one result holds x of lanes 0-31 in both halves and the other x of lanes
+// 32-63, so their maximum or sum is that of x with the lane l ^ 32 in every lane.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ const char* pf_stream(const CacheGeom& g, int seq, int layer, int head, int isv)
 {
     const int64_t unit = ((int64_t)seq * g.n_layers + layer) * g.n_kv_heads + head;
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
                 Sacc[r] = i > lim ? kNeg : Sacc[r] * qmul;
                 mx = fmaxf(mx, Sacc[r]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_xor32(mx);
             mn = fmaxf(mrun, mx);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -672,7 +686,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sacc[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * qmul;
+            mx = max_xor32(mx) * qmul;
             mn = fmaxf(mrun, mx);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -681,7 +695,7 @@ __global__ __launch_bounds__(256 * NT, 1) void k_prefill(PrefillArgs a)
             }
         }
         const float al = __builtin_amdgcn_exp2f(mrun - mn);
-        ps += __shfl_xor(ps, 32);
+        ps = sum_xor32(ps);
         lrun = fmaf(lrun, al, ps);
         mrun = mn;
         if (__builtin_amdgcn_ballot_w64(al != 1.0f)) {
