@@ -58,6 +58,29 @@ int main()
         c = config(1, 1, 99, 5, 16, 1, 100, 0); EXPECT(kv_cache_bytes(&c) < 0);
         EXPECT(kv_cache_bytes(nullptr) < 0);
     }
+    // large appends: every layer at once, then one layer at a time (over a million
+    // token-heads per call), bf16 and f32 input
+    for (int fk : {14, 5}) {
+        const int L = 8, H = 8, S = 32, T = 1024;
+        kv_config c = config(L, H, fk, fk, T, S, 20000, 0);
+        const int64_t b = kv_cache_bytes(&c);
+        EXPECT(b > 0);
+        std::vector<char> mem(4096);
+        char* p = (char*)(((uintptr_t)mem.data() + 255) & ~(uintptr_t)255);
+        kv_cache* h = nullptr;
+        EXPECT(kv_cache_init(&c, p, b, &h) == KV_OK);
+        std::vector<int32_t> ids(S), nn(S, 4096);
+        for (int s = 0; s < S; ++s) ids[s] = s;
+        EXPECT(kv_append(h, -1, S, ids.data(), nn.data(), (void*)16, (void*)16, KV_IN_BF16, nullptr) == KV_OK);
+        for (int l = 0; l < L; ++l)
+            EXPECT(kv_append(h, l, S, ids.data(), nn.data(), (void*)16, (void*)16, KV_IN_F32, nullptr) == KV_OK);
+        for (int s = 0; s < S; ++s) {
+            int64_t n = -1, nq = -1;
+            EXPECT(kv_seq_get(h, s, L - 1, &n, &nq) == KV_OK);
+            EXPECT(n == 8192 && n - nq <= T + 128 && n - nq >= T);
+        }
+        kv_cache_destroy(h);
+    }
     // a cache of 32 sequences: appends, spills, decode plans
     const int fmts[][2] = {{15, 15}, {5, 5}, {14, 14}, {0, 0}, {11, 5}, {21, 21}};
     for (auto& fp : fmts) {
