@@ -37,8 +37,9 @@ DECODE_SOURCES = ["kvq_decode_ws.h", "kvq_decode_ws_key.hip", "kvq_decode_ws.hip
 
 
 def measured_traffic(fmt, ctx, tail, kv_heads):
-    """HBM bytes of one decode call from the committed counter summary, or None when it
-    does not cover this workload or the decode sources changed since it was taken."""
+    """HBM bytes of one launch of the split-K decode kernel from the committed counter
+    summary, or None when it does not cover this workload or the decode sources changed
+    since it was taken."""
     import hashlib
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
@@ -52,7 +53,7 @@ def measured_traffic(fmt, ctx, tail, kv_heads):
             "sources_sha256": h.hexdigest()}
     for line in lines:
         parts = line.split()
-        if parts[:1] != ["traffic_per_call"]:
+        if parts[:1] != ["traffic_per_launch"]:
             continue
         kv = dict(x.split("=", 1) for x in parts[1:])
         if all(kv.get(k) == v for k, v in want.items()):
@@ -640,17 +641,24 @@ def main():
     dec_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     value = dec_bytes / steps / (dec_ms * 1e-3) / 1e9
 
-    # per-launch duration of the decode kernel (events around each launch)
+    # per-launch duration of the split-K decode kernel alone: the library records a pair of
+    # events on the call's stream right before and right after that kernel (ahead of the
+    # merge), one pair per layer; also the whole call (events around it)
     n, n_q = cache.seq_get(0, 0)
-    per = []
+    per, calls = [], []
     for l in range(L):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        kvq.debug_decode_events(a, b)
+        c0.record(stream)
         cache.decode(l, [0], qs[l], out=out)
-        b.record(stream)
+        c1.record(stream)
+        kvq.debug_decode_events(None, None)
         per.append((a, b))
+        calls.append((c0, c1))
     torch.cuda.synchronize()
     launch_ms = sum(a.elapsed_time(b) for a, b in per) / L
+    call_ms = sum(a.elapsed_time(b) for a, b in calls) / L
     launch_bytes = decode_bytes_layer(args.fmt, n, n_q, H)
     achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
 
@@ -693,8 +701,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.fmt, args.ctx, args.tail, H),
-                     "kernel": "one decode call: split-K decode kernel + merge kernel (%s)" % args.fmt,
-                     "bytes_per_launch": int(launch_bytes), "launch_us": round(launch_ms * 1e3, 2)},
+                     "kernel": "split-K decode kernel (%s), timed alone by events the library records around it"
+                               % args.fmt,
+                     "bytes_per_launch": int(launch_bytes), "launch_us": round(launch_ms * 1e3, 2),
+                     "call_us": round(call_ms * 1e3, 2),
+                     "call_frac": round(launch_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }

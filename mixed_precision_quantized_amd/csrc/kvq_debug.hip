@@ -31,3 +31,8 @@ extern "C" int kv_debug_convert(const float* in, int64_t n, uint16_t* bf16_out, 
                        bf16_out, fp16_out, recip_out, sqrt_out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
+
+extern "C" int kv_debug_decode_events(void* before, void* after)
+{
+    return kvq::set_decode_events(before, after);
+}

@@ -23,6 +23,8 @@
 // accumulator is rotated back once at the end; ring tokens stay in the original domain.
 #include <float.h>
 
+#include <atomic>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -373,10 +375,26 @@ int occ_fmt(bool mixed)
 
 }  // namespace
 
+// Caller events that bracket the split kernel (kv_debug_decode_events), or null.
+static std::atomic<hipEvent_t> g_ev_before{nullptr}, g_ev_after{nullptr};
+
+int set_decode_events(void* before, void* after)
+{
+    if ((before == nullptr) != (after == nullptr)) return -1;
+    g_ev_before.store((hipEvent_t)before, std::memory_order_release);
+    g_ev_after.store((hipEvent_t)after, std::memory_order_release);
+    return 0;
+}
+
 int launch_decode(const DecodeArgs& a, int n_wgs, void* stream)
 {
+    const hipEvent_t eb = g_ev_before.load(std::memory_order_acquire);
+    const hipEvent_t ea = g_ev_after.load(std::memory_order_acquire);
+    if (eb && hipEventRecord(eb, (hipStream_t)stream) != hipSuccess) return (int)hipErrorLaunchFailure;
     int rc = launch_decode_split(a, n_wgs, stream);
-    return rc ? rc : launch_merge(a, stream);
+    if (rc) return rc;
+    if (ea && hipEventRecord(ea, (hipStream_t)stream) != hipSuccess) return (int)hipErrorLaunchFailure;
+    return launch_merge(a, stream);
 }
 
 int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream)

@@ -458,32 +458,53 @@ __device__ __forceinline__ void build_qmat(QMat& Q, const float (&q)[8], const u
     // inv * amax <= 127 * 2^24 up to the rounding of the reciprocal: the bound is met with a
     // margin of 2^-7 (the top digit then stays within [-128, 127])
     const float inv = amax > 0.0f ? (kQLim * 0.9921875f) * __builtin_amdgcn_rcpf(amax) : 0.0f;
-    // N = 4, 8: the lane's 8 elements fill 8 consecutive bytes per digit ((even | odd)
-    // elements for N = 4, in order for N = 8), packed as they are made; other widths spread
-    // the positions over the half-block, one byte store per digit
-    uint32_t w[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
-    int slo = 0, shi = 0;               // sums of the low and high 16-bit parts
+    // The four digits of q_int at once: y = q_int + 0x808080 carries every balanced digit's
+    // +128 (bytes 0..2 of y are d0 + 128, d1 + 128, d2 + 128, and y >> 24 = d3), so
+    // z = y ^ 0x808080 holds d0..d3 as its four two's-complement bytes, and the high part
+    // d2 + 2^8 d3 = (y >> 16) - 128.  N = 4, 8: the lane's 8 elements fill 8 consecutive
+    // bytes per digit ((even | odd) elements for N = 4, in order for N = 8): a 4 x 4 byte
+    // transpose of four z's by v_perm per dword; other widths spread the positions over the
+    // half-block, one byte store per digit.
+    uint32_t z[8];
+    uint32_t sx = 0u;                   // sum of q_int (mod 2^32)
+    int shi = -8 * 128;                 // sum of the high parts
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int x = (int)__builtin_rintf(v[e] * inv);
-        const int x1 = (x + 128) >> 8, x2 = (x1 + 128) >> 8, x3 = (x2 + 128) >> 8;
-        const int dig[4] = {x, x1, x2, x3};
-        slo += x - (x2 << 16);
-        shi += x2;
+        const int y = x + 0x808080;
+        z[e] = (uint32_t)y ^ 0x808080u;
+        sx += (uint32_t)x;
+        shi += y >> 16;
+        if constexpr (N != 4 && N != 8) {
+            uint8_t* const bk = (uint8_t*)&Q.qa[0][h][16 * (g8 >> 1) + ((g8 & 1) ? kpos<N>(8 + e) : kpos<N>(e))];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if constexpr (N == 4 || N == 8) {
-                const int wi = N == 4 ? (e & 1) : (e >> 2), bi = N == 4 ? (e >> 1) : (e & 3);
-                w[k][wi] |= ((uint32_t)dig[k] & 0xFFu) << (8 * bi);
-            } else {
-                uint8_t* bk = (uint8_t*)&Q.qa[k][h][16 * (g8 >> 1)];
-                bk[(g8 & 1) ? kpos<N>(8 + e) : kpos<N>(e)] = (uint8_t)dig[k];
-            }
+            for (int k = 0; k < 4; ++k) bk[k * kG * kD] = (uint8_t)(z[e] >> (8 * k));
         }
     }
+    // the sum of the low parts, d0 + 2^8 d1 = q_int - 2^16 (d2 + 2^8 d3), exact in 32 bits
+    int slo = (int)(sx - ((uint32_t)shi << 16));
     if constexpr (N == 4 || N == 8) {
+        // elements (a, b, c, d) -> dwords (digit 0 of a..d, digit 1, digit 2, digit 3)
+        auto tr4 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&o)[4]) {
+            const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);   // a2 b2 a3 b3
+            const uint32_t u0 = __builtin_amdgcn_perm(d, c, 0x05010400u);   // c0 d0 c1 d1
+            const uint32_t u1 = __builtin_amdgcn_perm(d, c, 0x07030602u);   // c2 d2 c3 d3
+            o[0] = __builtin_amdgcn_perm(u0, t0, 0x05040100u);
+            o[1] = __builtin_amdgcn_perm(u0, t0, 0x07060302u);
+            o[2] = __builtin_amdgcn_perm(u1, t1, 0x05040100u);
+            o[3] = __builtin_amdgcn_perm(u1, t1, 0x07060302u);
+        };
+        uint32_t w0[4], w1[4];
+        if constexpr (N == 4) {
+            tr4(z[0], z[2], z[4], z[6], w0);
+            tr4(z[1], z[3], z[5], z[7], w1);
+        } else {
+            tr4(z[0], z[1], z[2], z[3], w0);
+            tr4(z[4], z[5], z[6], z[7], w1);
+        }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *(uint2*)&Q.qa[k][h][8 * g8] = make_uint2(w[k][0], w[k][1]);
+        for (int k = 0; k < 4; ++k) *(uint2*)&Q.qa[k][h][8 * g8] = make_uint2(w0[k], w1[k]);
     }
     slo += __builtin_amdgcn_mov_dpp(slo, QP_XOR1, 0xF, 0xF, false);
     slo += __builtin_amdgcn_mov_dpp(slo, QP_XOR2, 0xF, 0xF, false);
@@ -1042,6 +1063,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             asm volatile("" ::: "memory");
             const Stage<NV>& B = ring[slot];
             const PBuf& P = S.pb[pr][slot];
+            // the step's block scales (two token pairs per half), gathered by 16-bit LDS loads
+            const _Float16* sc16 = (const _Float16*)B.scales;
+            constexpr int SW = SB_V / 2;                       // binary16 words per scale row
+            const int so = (AFF_V ? 2 : 1) * vblk;
+            auto dpair = [&](int hf, int i) __attribute__((always_inline)) -> half2_t {
+                const int sx = 8 * hf + tg + 4 * i;
+                return (half2_t){sc16[SW * (2 * sx) + so], sc16[SW * (2 * sx + 1) + so]};
+            };
+            // the scales of the range check below are read together with the rescale factor,
+            // so that one LDS wait covers both
+            const half2_t dq0 = dpair(0, 0), dq1 = dpair(0, 1), dq2 = dpair(1, 0), dq3 = dpair(1, 1);
+            // KVarN: this page's value channel scales of the lane's dims, read with them
+            const uint4 cpg = KVARN_V && page_start ? *(const uint4*)(B.chan + 32 * vblk + 8 * vj)
+                                                    : make_uint4(0u, 0u, 0u, 0u);
             const f32x4 al = *(const f32x4*)P.alpha;
             if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
 #pragma unroll
@@ -1067,8 +1102,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             if (KVARN_V && page_start) {
                 // this page's value channel scales: move the accumulator to them (it is zero
                 // before the first page, so the first move is inert)
-                const uint4 c = *(const uint4*)(B.chan + 32 * vblk + 8 * vj);
-                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+                const uint32_t cw[4] = {cpg.x, cpg.y, cpg.z, cpg.w};
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const float cn = fp16_to_f32((cw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
@@ -1076,21 +1110,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     cvr[r] = cn;
                 }
             }
-            // the step's block scales (two token pairs per half), gathered by 16-bit LDS loads
-            const _Float16* sc16 = (const _Float16*)B.scales;
-            constexpr int SW = SB_V / 2;                       // binary16 words per scale row
-            const int so = (AFF_V ? 2 : 1) * vblk;
-            auto dpair = [&](int hf, int i) __attribute__((always_inline)) -> half2_t {
-                const int sx = 8 * hf + tg + 4 * i;
-                return (half2_t){sc16[SW * (2 * sx) + so], sc16[SW * (2 * sx + 1) + so]};
-            };
             {
                 // a scale of the step at or above 2^(-3 - ve): lower ve for the whole wave
                 const u16x2 m = {0x7FFF, 0x7FFF};
-                u16x2 r = __builtin_bit_cast(u16x2, dpair(0, 0)) & m;
-                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(0, 1)) & m);
-                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(1, 0)) & m);
-                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dpair(1, 1)) & m);
+                u16x2 r = __builtin_bit_cast(u16x2, dq0) & m;
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dq1) & m);
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dq2) & m);
+                r = __builtin_elementwise_max(r, __builtin_bit_cast(u16x2, dq3) & m);
                 const uint32_t dm = r.x > r.y ? r.x : r.y;  // binary16 bits of the largest |d|
                 const uint32_t lim = (uint32_t)max(0, 12 - ve) << 10;     // 2^(-3 - ve)
                 if (__builtin_amdgcn_ballot_w64(dm >= lim)) {
@@ -1107,7 +1133,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                     ve = nve;
                 }
             }
-            asm volatile("" ::: "memory");                   // reload the scales below (registers)
+            // affine values reload the scales below (registers); the others keep the four read
+            // above, and their operand reads below may move up past the checks
+            if constexpr (AFF_V) asm volatile("" ::: "memory");
             const uint32_t vh = ve >= -14 ? (uint32_t)(ve + 15) << 10 : 1u << (ve + 24);
             const half2_t vsc = __builtin_bit_cast(half2_t, vh | (vh << 16));   // {2^ve, 2^ve}
 #pragma unroll
@@ -1119,8 +1147,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
                 // scales, two tokens per packed multiply
                 const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
                 const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
-                const uint32_t a01 = __builtin_bit_cast(uint32_t, p01 * (dpair(hf, 0) * vsc));
-                const uint32_t a23 = __builtin_bit_cast(uint32_t, p23 * (dpair(hf, 1) * vsc));
+                uint32_t a01, a23;
+                if constexpr (AFF_V) {
+                    a01 = __builtin_bit_cast(uint32_t, p01 * (dpair(hf, 0) * vsc));
+                    a23 = __builtin_bit_cast(uint32_t, p23 * (dpair(hf, 1) * vsc));
+                } else {
+                    a01 = __builtin_bit_cast(uint32_t, p01 * ((hf ? dq2 : dq0) * vsc));
+                    a23 = __builtin_bit_cast(uint32_t, p23 * ((hf ? dq3 : dq1) * vsc));
+                }
                 if (AFF_V) {
                     const half2_t d01 = dpair(hf, 0), d23 = dpair(hf, 1);
                     const half2_t m01 = {sc16[SW * (2 * s0) + so + 1], sc16[SW * (2 * s0 + 1) + so + 1]};

@@ -160,6 +160,7 @@ int launch_append_ring(const AppendArgs& a, void* stream);     // BF16 ring writ
 int launch_decode(const DecodeArgs& a, int n_wgs, void* stream);        // split kernel + merge
 int launch_decode_split(const DecodeArgs& a, int n_wgs, void* stream);  // partials only
 int launch_merge(const DecodeArgs& a, void* stream);                    // kvq_merge.hip
+int set_decode_events(void* before, void* after);                         // timing hook of launch_decode
 int decode_wgs_per_cu(int fmt_k, int fmt_v, int group);        // occupancy of the decode kernel
 // 4-bit fast path (kvq_decode_ws.hip), used by launch_decode when it applies.
 bool decode_fast_supported(int fmt_k, int fmt_v);

@@ -99,6 +99,8 @@ def lib():
         L.kv_format_info.restype = ctypes.c_int
         L.kv_debug_convert.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp]
         L.kv_debug_convert.restype = ctypes.c_int
+        L.kv_debug_decode_events.argtypes = [_vp, _vp]
+        L.kv_debug_decode_events.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -300,6 +302,21 @@ class Cache:
         cs = b[occ: occ + (n_q // 128) * 256].view(torch.int16).view(n_q // 128, 128) if occ >= 0 else None
         ring = b[orr: orr + R * 256].view(torch.int16).view(R, 128) if R else None
         return codes, scales, cs, ring
+
+
+def debug_decode_events(before, after):
+    """Bracket the split-K decode kernel of every following decode call with two
+    torch.cuda.Event objects (recorded by the library on the call's stream, before the
+    kernel and after it, ahead of the merge); debug_decode_events(None, None) clears it.
+    The events are recorded once here first, so that their HIP handles exist."""
+    if before is None and after is None:
+        _check(lib().kv_debug_decode_events(None, None), "kv_debug_decode_events")
+        return
+    for e in (before, after):
+        if not e.cuda_event:
+            e.record()
+    _check(lib().kv_debug_decode_events(ctypes.c_void_p(before.cuda_event), ctypes.c_void_p(after.cuda_event)),
+           "kv_debug_decode_events")
 
 
 def debug_convert(x: torch.Tensor):
