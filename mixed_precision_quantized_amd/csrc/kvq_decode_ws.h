@@ -98,33 +98,53 @@ __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// x with the value of lane l ^ 16 (or l ^ 32) combined in every lane, by v_permlane16_swap
+// (v_permlane32_swap) with x as both operands: the two results then hold, in every lane, x
+// of that lane and of its partner, with no LDS round trip (a shuffle is a ds_bpermute)
+__device__ __forceinline__ float sum_x16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // reduction over lanes with equal (lane & 3)
 __device__ __forceinline__ float wave_max16(float x)
 {
     x = fmaxf(x, dpp<ROW_ROR4>(x));
     x = fmaxf(x, dpp<ROW_ROR8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    return max_x32(max_x16(x));
 }
 __device__ __forceinline__ float wave_sum16(float x)
 {
     x += dpp<ROW_ROR4>(x);
     x += dpp<ROW_ROR8>(x);
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    return sum_x32(sum_x16(x));
 }
 // reduction over lanes with equal (lane & 7)
 __device__ __forceinline__ float wave_max8(float x)
 {
     x = fmaxf(x, dpp<ROW_ROR8>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    return max_x32(max_x16(x));
 }
 __device__ __forceinline__ float wave_sum8(float x)
 {
     x += dpp<ROW_ROR8>(x);
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    return sum_x32(sum_x16(x));
 }
 
 // Direct global -> LDS loads: lane l writes its 16 (or 4) bytes at lds + 16 l (4 l).
@@ -1077,6 +1097,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
             // KVarN: this page's value channel scales of the lane's dims, read with them
             const uint4 cpg = KVARN_V && page_start ? *(const uint4*)(B.chan + 32 * vblk + 8 * vj)
                                                     : make_uint4(0u, 0u, 0u, 0u);
+            // the MFMA operands of both halves of the step (codes of the lane's runs, binary16
+            // 2^15 p): for symmetric block values (qN_0) of up to 4 bits they are read here
+            // too, so the whole step waits on one batch of LDS reads (q4_0, q2_0: +5-6 %);
+            // other formats read them per half (measured 0.7 % slower early for kvarn4, whose
+            // page-start rescale keeps more registers live)
+            constexpr bool kOpsEarly = !AFF_V && !KVARN_V && NV <= 4;
+            struct VOps { VRun x[4]; half2_t p01, p23; };
+            auto read_ops = [&](int hf) __attribute__((always_inline)) -> VOps {
+                const int s0 = 8 * hf + tg, s1 = s0 + 4;
+                VOps o;
+                o.x[0] = vrun(B.codes, s0);
+                o.x[1] = vrun(B.codes, 16 + s0);
+                o.x[2] = vrun(B.codes, s1);
+                o.x[3] = vrun(B.codes, 16 + s1);
+                o.p01 = *(const half2_t*)&P.ph[vj][2 * s0];
+                o.p23 = *(const half2_t*)&P.ph[vj][2 * s1];
+                return o;
+            };
+            VOps early[2];
+            if constexpr (kOpsEarly) {
+                early[0] = read_ops(0);
+                early[1] = read_ops(1);
+            }
             const f32x4 al = *(const f32x4*)P.alpha;
             if (al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f) {
 #pragma unroll
@@ -1141,12 +1184,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int s0 = 8 * hf + tg, s1 = s0 + 4;
-                const VRun x0 = vrun(B.codes, s0), x1 = vrun(B.codes, 16 + s0);
-                const VRun x2 = vrun(B.codes, s1), x3 = vrun(B.codes, 16 + s1);
+                const VOps ops = kOpsEarly ? early[hf] : read_ops(hf);
+                const VRun &x0 = ops.x[0], &x1 = ops.x[1], &x2 = ops.x[2], &x3 = ops.x[3];
                 // A: binary16 2^15 p (written by the K wave) times the scaled binary16 block
                 // scales, two tokens per packed multiply
-                const half2_t p01 = *(const half2_t*)&P.ph[vj][2 * s0];
-                const half2_t p23 = *(const half2_t*)&P.ph[vj][2 * s1];
+                const half2_t p01 = ops.p01, p23 = ops.p23;
                 uint32_t a01, a23;
                 if constexpr (AFF_V) {
                     a01 = __builtin_bit_cast(uint32_t, p01 * (dpair(hf, 0) * vsc));
@@ -1196,14 +1238,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_decode_ws(DecodeArgs a)
         for (int r = 0; r < 8; ++r)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                float x = D[r][c] * unscale;
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                D[r][c] = x;
+                D[r][c] = sum_x32(sum_x16(D[r][c] * unscale));
             }
         ms = fmaf((float)(1 << (NV - 1)), msd, ms) * (1.0f / kPScale);    // sum of p (m + o d)
-        ms += __shfl_xor(ms, 16);
-        ms += __shfl_xor(ms, 32);
+        ms = sum_x32(sum_x16(ms));
         const f32x4 mh4 = {quad_bcast(ms, 0), quad_bcast(ms, 1), quad_bcast(ms, 2), quad_bcast(ms, 3)};
         wait_vmcnt<0>();                          // stages past the end, before reusing the ring
         asm volatile("" ::: "memory");
