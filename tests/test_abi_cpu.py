@@ -228,3 +228,12 @@ def test_kv_log_prints_the_configuration():
     env.pop("KV_LOG")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
     assert "kvq:" not in r.stderr
+
+
+def test_decode_events_hook_validation():
+    # the measurement hook stores two caller event handles; it touches no device, so its
+    # argument checks run here: exactly one null is refused, two nulls clear it
+    L = kvq.lib()
+    assert L.kv_debug_decode_events(ctypes.c_void_p(FAKE), None) == kvq.KV_EINVAL
+    assert L.kv_debug_decode_events(None, ctypes.c_void_p(FAKE)) == kvq.KV_EINVAL
+    assert L.kv_debug_decode_events(None, None) == kvq.KV_OK
