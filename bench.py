@@ -547,6 +547,8 @@ def sweep(args):
                 us, gbs = _decode_rate(cache, wl, fmt, L, H, QH)
                 out.append({"fmt": fmt, "tail": tail, "replicas": L, "decode_us": round(us, 2),
                             "decode_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)})
+                print("  sweep %s %s tail %d: %s GB/s" % (wl, fmt, tail, out[-1]["decode_gbs"]), file=sys.stderr,
+                      flush=True)
                 del cache
                 torch.cuda.empty_cache()
         print("  sweep %s done" % wl, file=sys.stderr, flush=True)
